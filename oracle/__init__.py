@@ -1,0 +1,258 @@
+"""Scalar CPU oracle for the K-quant x int8 GEMM (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never does.  The arithmetic lives in ``dq_oracle.c``
+(plain C, built with gcc, no fast-math); this module only marshals numpy
+arrays, splits the weight rows over threads and, for ``qgemm_rows``, gathers
+canvas rows by index before quantizing.
+
+Sources (each routine in ``dq_oracle.c`` cites its own):
+  * mojo-dllm "Architecture" page, "Source map": scalar K-quant decoders are
+    the test oracle; int8 activations with one scale per 256 values; a
+    row-major reference GEMM.
+  * same page, "A forward pass", steps 2-4: quantize once and reuse; the
+    output projection runs on the requested rows only.
+  * heatdrop.ai card, "Key highlights": GEMM checked against dequantization.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+Q4_K = 12
+Q6_K = 14
+QK = 256
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+SUBBLOCKS = {Q4_K: 8, Q6_K: 16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dq_oracle.c")
+_LIB = os.path.join(_HERE, "libdq_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = False) -> str:
+    """Compile dq_oracle.c with gcc into oracle/libdq_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            i64, vp = ctypes.c_int64, ctypes.c_void_p
+            lib.dqo_fp16_to_f32.restype = ctypes.c_float
+            lib.dqo_fp16_to_f32.argtypes = [ctypes.c_uint16]
+            lib.dqo_decode_q4k.argtypes = [vp] * 6
+            lib.dqo_decode_q6k.argtypes = [vp] * 4
+            lib.dqo_dequant_row.argtypes = [ctypes.c_int, vp, i64, vp]
+            lib.dqo_quantize_act.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+            lib.dqo_subdots.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, i64, i64, vp]
+            lib.dqo_superblock_sums.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp,
+                                                i64, i64, vp, vp]
+            lib.dqo_qgemm_ref.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, i64, i64,
+                                          vp, vp]
+            lib.dqo_qgemm_ref_points.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp,
+                                                 vp, vp]
+            lib.dqo_qgemm_f32.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, i64,
+                                          i64, vp, i64]
+            for name in ("dqo_dequant_row", "dqo_quantize_act", "dqo_subdots",
+                         "dqo_superblock_sums", "dqo_qgemm_ref", "dqo_qgemm_ref_points",
+                         "dqo_qgemm_f32"):
+                getattr(lib, name).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+
+
+def _rows(W: np.ndarray, type_: int, K: int) -> np.ndarray:
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    nb = K // QK
+    return W.reshape(-1, nb * BLOCK_BYTES[type_])
+
+
+def _threads(n: int, threads: int | None):
+    t = threads or os.cpu_count() or 1
+    t = max(1, min(t, n))
+    bounds = [n * i // t for i in range(t + 1)]
+    return [(bounds[i], bounds[i + 1]) for i in range(t) if bounds[i + 1] > bounds[i]]
+
+
+def _run_threaded(fn, ranges):
+    if len(ranges) == 1:
+        fn(*ranges[0])
+        return
+    ts = [threading.Thread(target=fn, args=r) for r in ranges]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+
+
+# --------------------------------------------------------------------------- #
+# Element-level routines                                                      #
+# --------------------------------------------------------------------------- #
+def fp16_to_f32(bits: np.ndarray) -> np.ndarray:
+    lib = _load()
+    bits = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.dqo_fp16_to_f32(int(b)) for b in bits], dtype=np.float32)
+
+
+def decode_q4k(block: np.ndarray):
+    """One 144-byte Q4_K block -> (d, dmin, sc[8], mn[8], q[256])."""
+    lib = _load()
+    blk = np.ascontiguousarray(block, dtype=np.uint8)
+    assert blk.size == 144
+    d, dm = ctypes.c_float(), ctypes.c_float()
+    sc, mn, q = (np.zeros(8, np.uint8), np.zeros(8, np.uint8), np.zeros(256, np.uint8))
+    lib.dqo_decode_q4k(_p(blk), ctypes.byref(d), ctypes.byref(dm), _p(sc), _p(mn), _p(q))
+    return np.float32(d.value), np.float32(dm.value), sc, mn, q
+
+
+def decode_q6k(block: np.ndarray):
+    """One 210-byte Q6_K block -> (d, sc[16] int8, q[256] in [0, 63])."""
+    lib = _load()
+    blk = np.ascontiguousarray(block, dtype=np.uint8)
+    assert blk.size == 210
+    d = ctypes.c_float()
+    sc, q = np.zeros(16, np.int8), np.zeros(256, np.uint8)
+    lib.dqo_decode_q6k(_p(blk), ctypes.byref(d), _p(sc), _p(q))
+    return np.float32(d.value), sc, q
+
+
+def dequant(type_: int, W: np.ndarray, K: int) -> np.ndarray:
+    """Fully dequantized N x K weights in float64."""
+    lib = _load()
+    rows = _rows(W, type_, K)
+    out = np.zeros((rows.shape[0], K), np.float64)
+    for n in range(rows.shape[0]):
+        r = np.ascontiguousarray(rows[n])
+        o = out[n]
+        _check(lib.dqo_dequant_row(type_, _p(r), K, o.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def quantize_act(x: np.ndarray):
+    """f32 M x K -> (q int8 M x K, d f32 M x K/256, bsum int32 M x K/32)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    q = np.zeros((M, K), np.int8)
+    d = np.zeros((M, K // QK), np.float32)
+    bs = np.zeros((M, K // 32), np.int32)
+    _check(lib.dqo_quantize_act(M, K, _p(x), K, _p(q), _p(d), _p(bs)))
+    return q, d, bs
+
+
+def subdots(type_: int, q: np.ndarray, W: np.ndarray, N: int, threads=None) -> np.ndarray:
+    """Integer dot per (m, n, super-block, sub-block): int32 [M, N, K/256, J]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    M, K = q.shape
+    Wr = _rows(W, type_, K)
+    J = SUBBLOCKS[type_]
+    out = np.zeros((M, N, K // QK, J), np.int32)
+    _run_threaded(lambda a, b: _check(lib.dqo_subdots(type_, M, N, K, _p(q), _p(Wr), a, b,
+                                                        _p(out))), _threads(N, threads))
+    return out
+
+
+def superblock_sums(type_: int, q, bsum, W, N: int, threads=None):
+    """(S, Mn) int32 [M, N, K/256]: sum_j sc_j*dot_j and sum_j mn_j*bsum_j."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    bsum = np.ascontiguousarray(bsum, dtype=np.int32)
+    M, K = q.shape
+    Wr = _rows(W, type_, K)
+    S = np.zeros((M, N, K // QK), np.int32)
+    Mn = np.zeros((M, N, K // QK), np.int32)
+    _run_threaded(lambda a, b: _check(lib.dqo_superblock_sums(
+        type_, M, N, K, _p(q), _p(bsum), _p(Wr), a, b, _p(S), _p(Mn))), _threads(N, threads))
+    return S, Mn
+
+
+def qgemm_ref(type_: int, q, d, W, N: int, threads=None):
+    """Plain definition in f64: (y, T), both M x N, T = sum_k |w^ x^|."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    M, K = q.shape
+    Wr = _rows(W, type_, K)
+    y = np.zeros((M, N), np.float64)
+    T = np.zeros((M, N), np.float64)
+    _run_threaded(lambda a, b: _check(lib.dqo_qgemm_ref(type_, M, N, K, _p(q), _p(d), _p(Wr),
+                                                        a, b, _p(y), _p(T))),
+                  _threads(N, threads))
+    return y, T
+
+
+def qgemm_ref_points(type_: int, q, d, W, m_idx, n_idx, threads=None):
+    """Plain-definition (y, T) at the listed (m, n) output points only."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    M, K = q.shape
+    Wr = _rows(W, type_, K)
+    mi = np.ascontiguousarray(m_idx, dtype=np.int64)
+    ni = np.ascontiguousarray(n_idx, dtype=np.int64)
+    P = mi.size
+    y = np.zeros(P, np.float64)
+    T = np.zeros(P, np.float64)
+
+    def run(a, b):
+        _check(lib.dqo_qgemm_ref_points(
+            type_, K, b - a, mi[a:].ctypes.data_as(ctypes.c_void_p),
+            ni[a:].ctypes.data_as(ctypes.c_void_p), _p(q), _p(d), _p(Wr),
+            y[a:].ctypes.data_as(ctypes.c_void_p), T[a:].ctypes.data_as(ctypes.c_void_p)))
+
+    _run_threaded(run, _threads(P, threads))
+    return y, T
+
+
+def qgemm_f32(type_: int, q, d, bsum, W, N: int, threads=None):
+    """Integer decomposition folded in f32 (the oracle's own f32 output)."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    bsum = np.ascontiguousarray(bsum, dtype=np.int32)
+    M, K = q.shape
+    Wr = _rows(W, type_, K)
+    y = np.zeros((M, N), np.float32)
+    _run_threaded(lambda a, b: _check(lib.dqo_qgemm_f32(type_, M, N, K, _p(q), _p(d), _p(bsum),
+                                                        _p(Wr), a, b, _p(y), N)),
+                  _threads(N, threads))
+    return y
+
+
+def qgemm_rows_inputs(canvas: np.ndarray, idx: np.ndarray):
+    """Gathered-row projection, activation side: quantize rows canvas[idx].
+
+    Architecture page, "A forward pass", steps 3-4: only the requested
+    positions reach the output projection.  Returns (q, d, bsum) of the
+    gathered rows in idx order (duplicates allowed).
+    """
+    rows = np.ascontiguousarray(np.asarray(canvas, np.float32)[np.asarray(idx, np.int64)])
+    return quantize_act(rows)

@@ -1,0 +1,398 @@
+/*
+ * dq_oracle.c -- plain, slow, scalar CPU oracle for the K-quant x int8 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header or table with the HIP
+ * library: every rule below is written out again from its definition.
+ *
+ * What it computes (sources named per function):
+ *   - mojo-dllm "Architecture" page, "Source map": the scalar K-quant decoders
+ *     are the test oracle; activations are quantized to int8 with one scale
+ *     per 256 values; a row-major reference GEMM sits beside the packed one.
+ *   - same page, "A forward pass", step 2: one quantization of the activations
+ *     feeds several projections.
+ *   - heatdrop.ai "vladimirrott/mojo-dllm" card, "Key highlights": the decoder
+ *     and GEMM are checked against a dequantize-then-multiply reference.
+ *   - The pages name the GGUF Q4_K and Q6_K block types but do not spell out
+ *     their bytes.  The layouts below follow the public GGUF/ggml K-quant
+ *     block definitions (super-block of 256 weights; Q4_K = 144 bytes with
+ *     6-bit scales/mins, Q6_K = 210 bytes with int8 scales).
+ *
+ * Precision rules: decoding and the integer sub-block dots are exact.  The
+ * activation quantizer uses IEEE binary32 for every step (one correctly
+ * rounded division 127/amax, one multiply, round-half-to-even, clamp), so the
+ * integer codes it produces are the ones any binary32 implementation of the
+ * same steps produces.  The reference GEMM output is formed in binary64 from
+ * fully dequantized weights and activations (the plain definition); a second
+ * routine forms the same output in binary32 through the integer decomposition.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QK 256 /* weights per super-block */
+#define Q4K_BYTES 144
+#define Q6K_BYTES 210
+#define TYPE_Q4K 12 /* GGUF tensor type id of Q4_K */
+#define TYPE_Q6K 14 /* GGUF tensor type id of Q6_K */
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 -> binary32 (exact: every half value is a float value). */
+/* sign | 5-bit exponent (bias 15) | 10-bit fraction; exponent 0 is the      */
+/* subnormal range f * 2^-24, exponent 31 is Inf/NaN.                        */
+/* ------------------------------------------------------------------------ */
+float dqo_fp16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return (float)(sign ? -v : v);
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ------------------------------------------------------------------------ */
+/* Q4_K super-block (144 bytes): d (fp16), dmin (fp16), scales[12], qs[128]. */
+/* Eight sub-blocks of 32 weights; sub-block j has a 6-bit scale sc[j] and a */
+/* 6-bit min mn[j].  j < 4: sc = low 6 bits of scales[j], mn = low 6 bits of */
+/* scales[j+4].  j >= 4: low 4 bits from scales[j+4] (sc: low nibble, mn:    */
+/* high nibble), high 2 bits from the top 2 bits of scales[j-4] (sc) and of  */
+/* scales[j] (mn).  qs byte 32c+l holds weight 64c+l in its low nibble and   */
+/* weight 64c+32+l in its high nibble (c = 0..3, l = 0..31).                 */
+/* Dequantized weight i (sub-block j = i/32): d*sc[j]*q[i] - dmin*mn[j].     */
+/* ------------------------------------------------------------------------ */
+void dqo_decode_q4k(const uint8_t *blk, float *d, float *dmin, uint8_t sc[8],
+                    uint8_t mn[8], uint8_t q[256]) {
+  const uint8_t *s = blk + 4;
+  const uint8_t *qs = blk + 16;
+  *d = dqo_fp16_to_f32(rd16(blk));
+  *dmin = dqo_fp16_to_f32(rd16(blk + 2));
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = s[j] & 63;
+    mn[j] = s[j + 4] & 63;
+  }
+  for (int j = 4; j < 8; ++j) {
+    sc[j] = (uint8_t)((s[j + 4] & 15) | ((s[j - 4] >> 6) << 4));
+    mn[j] = (uint8_t)((s[j + 4] >> 4) | ((s[j] >> 6) << 4));
+  }
+  for (int c = 0; c < 4; ++c)
+    for (int l = 0; l < 32; ++l) {
+      q[64 * c + l] = qs[32 * c + l] & 15;
+      q[64 * c + 32 + l] = qs[32 * c + l] >> 4;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q6_K super-block (210 bytes): ql[128], qh[64], scales[16] (int8), d fp16. */
+/* Sixteen sub-blocks of 16 weights; weight i uses scales[i/16].  For half   */
+/* h = 0,1 and l = 0..31 the 6-bit codes are                                 */
+/*   i = 128h+l    : low  nibble of ql[64h+l]    | bits 0-1 of qh[32h+l] <<4 */
+/*   i = 128h+32+l : low  nibble of ql[64h+32+l] | bits 2-3 of qh[32h+l] <<4 */
+/*   i = 128h+64+l : high nibble of ql[64h+l]    | bits 4-5 of qh[32h+l] <<4 */
+/*   i = 128h+96+l : high nibble of ql[64h+32+l] | bits 6-7 of qh[32h+l] <<4 */
+/* Dequantized weight: d * scales[i/16] * (q[i] - 32).                       */
+/* ------------------------------------------------------------------------ */
+void dqo_decode_q6k(const uint8_t *blk, float *d, int8_t sc[16], uint8_t q[256]) {
+  const uint8_t *ql = blk;
+  const uint8_t *qh = blk + 128;
+  for (int j = 0; j < 16; ++j) sc[j] = (int8_t)blk[192 + j];
+  *d = dqo_fp16_to_f32(rd16(blk + 208));
+  for (int h = 0; h < 2; ++h)
+    for (int l = 0; l < 32; ++l) {
+      uint8_t hb = qh[32 * h + l];
+      q[128 * h + l] = (uint8_t)((ql[64 * h + l] & 15) | (((hb >> 0) & 3) << 4));
+      q[128 * h + 32 + l] = (uint8_t)((ql[64 * h + 32 + l] & 15) | (((hb >> 2) & 3) << 4));
+      q[128 * h + 64 + l] = (uint8_t)((ql[64 * h + l] >> 4) | (((hb >> 4) & 3) << 4));
+      q[128 * h + 96 + l] = (uint8_t)((ql[64 * h + 32 + l] >> 4) | (((hb >> 6) & 3) << 4));
+    }
+}
+
+static int block_bytes(int type) {
+  return type == TYPE_Q4K ? Q4K_BYTES : (type == TYPE_Q6K ? Q6K_BYTES : 0);
+}
+
+/* Dequantize one weight row of K values (K/256 consecutive blocks) to f64.  */
+/* Every value is exact in binary64 (at most 21 significant bits).           */
+int dqo_dequant_row(int type, const uint8_t *row, int64_t K, double *w) {
+  int bb = block_bytes(type);
+  if (!bb || K % QK) return -1;
+  for (int64_t b = 0; b < K / QK; ++b) {
+    const uint8_t *blk = row + b * bb;
+    double *o = w + b * QK;
+    if (type == TYPE_Q4K) {
+      float d, dmin;
+      uint8_t sc[8], mn[8], q[256];
+      dqo_decode_q4k(blk, &d, &dmin, sc, mn, q);
+      for (int i = 0; i < QK; ++i)
+        o[i] = (double)d * sc[i / 32] * q[i] - (double)dmin * mn[i / 32];
+    } else {
+      float d;
+      int8_t sc[16];
+      uint8_t q[256];
+      dqo_decode_q6k(blk, &d, sc, q);
+      for (int i = 0; i < QK; ++i) o[i] = (double)d * sc[i / 16] * ((int)q[i] - 32);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation quantization: int8, one scale per 256 values of a row.         */
+/* (Architecture page, "Source map", kernels/qgemm.mojo.)  Symmetric absmax: */
+/*   amax = max |x| over the 256-block;                                      */
+/*   amax == 0  ->  d = 0, q = 0;                                            */
+/*   else inv = 127 / amax (binary32, correctly rounded),                    */
+/*        q = clamp(rint(x * inv), -127, 127) (binary32 multiply, ties even),*/
+/*        d = amax / 127 (binary32).                                         */
+/* bsum[m][k/32] = sum of the 32 codes of that group (int32).                */
+/* x is M rows with leading dimension ldx (floats); q is M x K (ld K);       */
+/* d is M x K/256; bsum is M x K/32.                                         */
+/* ------------------------------------------------------------------------ */
+int dqo_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *q,
+                     float *d, int32_t *bsum) {
+  if (K % QK || ldx < K) return -1;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t b = 0; b < K / QK; ++b) {
+      const float *xb = x + m * ldx + b * QK;
+      int8_t *qb = q + m * K + b * QK;
+      float amax = 0.0f;
+      for (int i = 0; i < QK; ++i) {
+        float a = fabsf(xb[i]);
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) {
+        d[m * (K / QK) + b] = 0.0f;
+        for (int i = 0; i < QK; ++i) qb[i] = 0;
+      } else {
+        float inv = 127.0f / amax;
+        for (int i = 0; i < QK; ++i) {
+          float v = rintf(xb[i] * inv);
+          if (v > 127.0f) v = 127.0f;
+          if (v < -127.0f) v = -127.0f;
+          qb[i] = (int8_t)v;
+        }
+        d[m * (K / QK) + b] = amax / 127.0f;
+      }
+      for (int g = 0; g < QK / 32; ++g) {
+        int32_t s = 0;
+        for (int i = 0; i < 32; ++i) s += qb[32 * g + i];
+        bsum[m * (K / 32) + b * 8 + g] = s;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-sub-block integer dots.  For activation row m, weight row n,          */
+/* super-block b and sub-block j:                                            */
+/*   Q4_K (J = 8, width 32):  dot = sum q_w * q_x        (q_w in [0,15])     */
+/*   Q6_K (J = 16, width 16): dot = sum (q_w - 32) * q_x (q_w in [0,63])     */
+/* out[((m*N + n)*(K/256) + b)*J + j], rows n in [n0, n1) only.              */
+/* ------------------------------------------------------------------------ */
+int dqo_subdots(int type, int64_t M, int64_t N, int64_t K, const int8_t *qx,
+                const uint8_t *W, int64_t n0, int64_t n1, int32_t *out) {
+  int bb = block_bytes(type);
+  if (!bb || K % QK) return -1;
+  int64_t nb = K / QK;
+  int J = type == TYPE_Q4K ? 8 : 16, wid = QK / J;
+  uint8_t q[256];
+  for (int64_t n = n0; n < n1; ++n)
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t *blk = W + (n * nb + b) * bb;
+      int off = 0;
+      if (type == TYPE_Q4K) {
+        float d, dm;
+        uint8_t sc[8], mn[8];
+        dqo_decode_q4k(blk, &d, &dm, sc, mn, q);
+      } else {
+        float d;
+        int8_t sc[16];
+        dqo_decode_q6k(blk, &d, sc, q);
+        off = 32;
+      }
+      for (int64_t m = 0; m < M; ++m) {
+        const int8_t *xb = qx + m * K + b * QK;
+        for (int j = 0; j < J; ++j) {
+          int32_t s = 0;
+          for (int i = j * wid; i < (j + 1) * wid; ++i) s += ((int)q[i] - off) * xb[i];
+          out[((m * N + n) * nb + b) * J + j] = s;
+        }
+      }
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-super-block integer sums (the combine of the integer decomposition):  */
+/*   S[m,n,b]  = sum_j sc_j * dot_j                                          */
+/*   Mn[m,n,b] = sum_j mn_j * bsum_j   (Q4_K; 0 for Q6_K)                    */
+/* so that the output is y[m,n] = sum_b dx[m,b]*(d[n,b]*S - dmin[n,b]*Mn).   */
+/* Layout [m][n][b]; rows n in [n0, n1).                                     */
+/* ------------------------------------------------------------------------ */
+int dqo_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const int8_t *qx,
+                        const int32_t *bsum, const uint8_t *W, int64_t n0, int64_t n1,
+                        int32_t *S, int32_t *Mn) {
+  int bb = block_bytes(type);
+  if (!bb || K % QK) return -1;
+  int64_t nb = K / QK;
+  int J = type == TYPE_Q4K ? 8 : 16;
+  int32_t *dots = (int32_t *)malloc(sizeof(int32_t) * J);
+  uint8_t q[256];
+  for (int64_t n = n0; n < n1; ++n)
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t *blk = W + (n * nb + b) * bb;
+      uint8_t sc4[8], mn4[8];
+      int8_t sc6[16];
+      float d, dm;
+      if (type == TYPE_Q4K)
+        dqo_decode_q4k(blk, &d, &dm, sc4, mn4, q);
+      else
+        dqo_decode_q6k(blk, &d, sc6, q);
+      for (int64_t m = 0; m < M; ++m) {
+        const int8_t *xb = qx + m * K + b * QK;
+        int wid = QK / J, off = type == TYPE_Q4K ? 0 : 32;
+        for (int j = 0; j < J; ++j) {
+          int32_t s = 0;
+          for (int i = j * wid; i < (j + 1) * wid; ++i) s += ((int)q[i] - off) * xb[i];
+          dots[j] = s;
+        }
+        int32_t s_acc = 0, m_acc = 0;
+        for (int j = 0; j < J; ++j) {
+          if (type == TYPE_Q4K) {
+            s_acc += (int32_t)sc4[j] * dots[j];
+            m_acc += (int32_t)mn4[j] * bsum[m * (K / 32) + b * 8 + j];
+          } else {
+            s_acc += (int32_t)sc6[j] * dots[j];
+          }
+        }
+        S[(m * N + n) * nb + b] = s_acc;
+        Mn[(m * N + n) * nb + b] = m_acc;
+      }
+    }
+  free(dots);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reference GEMM, plain definition in binary64:                             */
+/*   y[m,n] = sum_k w^[n,k] * x^[m,k],  x^[m,k] = dx[m,k/256] * qx[m,k],     */
+/*   T[m,n] = sum_k |w^[n,k] * x^[m,k]|  (the tolerance scale).              */
+/* W is N rows of K/256 raw GGUF blocks.  Rows n in [n0, n1); y, T are M x N */
+/* row-major (ld N).                                                         */
+/* ------------------------------------------------------------------------ */
+int dqo_qgemm_ref(int type, int64_t M, int64_t N, int64_t K, const int8_t *qx,
+                  const float *dx, const uint8_t *W, int64_t n0, int64_t n1, double *y,
+                  double *T) {
+  int bb = block_bytes(type);
+  if (!bb || K % QK) return -1;
+  double *w = (double *)malloc(sizeof(double) * K);
+  for (int64_t n = n0; n < n1; ++n) {
+    dqo_dequant_row(type, W + n * (K / QK) * bb, K, w);
+    for (int64_t m = 0; m < M; ++m) {
+      double acc = 0.0, tol = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double xh = (double)dx[m * (K / QK) + k / QK] * qx[m * K + k];
+        double p = w[k] * xh;
+        acc += p;
+        tol += fabs(p);
+      }
+      y[m * N + n] = acc;
+      T[m * N + n] = tol;
+    }
+  }
+  free(w);
+  return 0;
+}
+
+/* Same as dqo_qgemm_ref for a list of P (m, n) output points.               */
+int dqo_qgemm_ref_points(int type, int64_t K, int64_t P, const int64_t *mi, const int64_t *ni,
+                         const int8_t *qx, const float *dx, const uint8_t *W, double *y,
+                         double *T) {
+  int bb = block_bytes(type);
+  if (!bb || K % QK) return -1;
+  double *w = (double *)malloc(sizeof(double) * K);
+  for (int64_t p = 0; p < P; ++p) {
+    int64_t m = mi[p], n = ni[p];
+    dqo_dequant_row(type, W + n * (K / QK) * bb, K, w);
+    double acc = 0.0, tol = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double xh = (double)dx[m * (K / QK) + k / QK] * qx[m * K + k];
+      double pr = w[k] * xh;
+      acc += pr;
+      tol += fabs(pr);
+    }
+    y[p] = acc;
+    T[p] = tol;
+  }
+  free(w);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The same output through the integer decomposition, in binary32:           */
+/*   for b in order: y += dx[m,b] * (d[n,b]*S[m,n,b] - dmin[n,b]*Mn[m,n,b])  */
+/* with S, Mn the exact integers above (Mn = 0 for Q6_K).                    */
+/* Rows n in [n0, n1); y is M x N row-major with leading dimension ldy.      */
+/* ------------------------------------------------------------------------ */
+int dqo_qgemm_f32(int type, int64_t M, int64_t N, int64_t K, const int8_t *qx,
+                  const float *dx, const int32_t *bsum, const uint8_t *W, int64_t n0,
+                  int64_t n1, float *y, int64_t ldy) {
+  int bb = block_bytes(type);
+  if (!bb || K % QK) return -1;
+  int64_t nb = K / QK;
+  int J = type == TYPE_Q4K ? 8 : 16, wid = QK / J, off = type == TYPE_Q4K ? 0 : 32;
+  uint8_t *q = (uint8_t *)malloc((size_t)nb * QK);
+  uint8_t *sc4 = (uint8_t *)malloc((size_t)nb * 8), *mn4 = (uint8_t *)malloc((size_t)nb * 8);
+  int8_t *sc6 = (int8_t *)malloc((size_t)nb * 16);
+  float *dd = (float *)malloc(sizeof(float) * nb), *dm = (float *)malloc(sizeof(float) * nb);
+  for (int64_t n = n0; n < n1; ++n) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t *blk = W + (n * nb + b) * bb;
+      if (type == TYPE_Q4K)
+        dqo_decode_q4k(blk, &dd[b], &dm[b], sc4 + 8 * b, mn4 + 8 * b, q + QK * b);
+      else {
+        dqo_decode_q6k(blk, &dd[b], sc6 + 16 * b, q + QK * b);
+        dm[b] = 0.0f;
+      }
+    }
+    for (int64_t m = 0; m < M; ++m) {
+      float acc = 0.0f;
+      for (int64_t b = 0; b < nb; ++b) {
+        const int8_t *xb = qx + m * K + b * QK;
+        const uint8_t *qb = q + QK * b;
+        int32_t s_acc = 0, m_acc = 0;
+        for (int j = 0; j < J; ++j) {
+          int32_t s = 0;
+          for (int i = j * wid; i < (j + 1) * wid; ++i) s += ((int)qb[i] - off) * xb[i];
+          if (type == TYPE_Q4K) {
+            s_acc += (int32_t)sc4[8 * b + j] * s;
+            m_acc += (int32_t)mn4[8 * b + j] * bsum[m * (K / 32) + b * 8 + j];
+          } else {
+            s_acc += (int32_t)sc6[16 * b + j] * s;
+          }
+        }
+        float t = dd[b] * (float)s_acc - dm[b] * (float)m_acc;
+        acc += dx[m * nb + b] * t;
+      }
+      y[m * ldy + n] = acc;
+    }
+  }
+  free(q);
+  free(sc4);
+  free(mn4);
+  free(sc6);
+  free(dd);
+  free(dm);
+  return 0;
+}

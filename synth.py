@@ -1,0 +1,108 @@
+"""Seeded synthetic inputs for the K-quant x int8 GEMM (shared by tests and bench).
+
+This module draws random numbers and places them at the byte offsets of the
+GGUF K-quant super-blocks; it holds none of the method's arithmetic (no
+decoding, quantization or products).  Both the CPU oracle and the HIP path
+consume what it produces.
+
+Draws (numpy ``default_rng(seed)``, PCG64), in this order per matrix:
+  * Q4_K block (144 bytes): d then dmin as fp16(|N(0,1)| * 2e-3) at bytes 0-1
+    and 2-3; the 12 scale bytes uniform on [0, 255] (the 6-bit scale/min
+    packing is a bijection between these 96 bits and sixteen 6-bit values, so
+    every scale and min is uniform on [0, 63]); the 128 nibble bytes uniform
+    (every 4-bit code uniform on [0, 15]).
+  * Q6_K block (210 bytes): d as fp16(|N(0,1)| * 2e-3) at bytes 208-209; the
+    16 int8 scales at bytes 192-207 uniform on [-32, 31]; the 128 low-nibble
+    bytes and 64 high-bit bytes uniform (every 6-bit code uniform on [0, 63]).
+  * Activations: N(0, 1) float32, then round(0.01 * K) columns drawn without
+    replacement and multiplied by 20 in every row.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q4_K = 12
+Q6_K = 14
+QK = 256
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+
+
+def _fp16_bytes(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+    v = (np.abs(rng.standard_normal(shape)) * scale).astype(np.float16)
+    return v.view(np.uint8).reshape(tuple(shape) + (2,))
+
+
+def _bytes(rng: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape)
+
+
+def q4k_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-3) -> np.ndarray:
+    """N x K weights as raw Q4_K blocks, uint8 [N, K/256, 144]."""
+    nb = K // QK
+    out = np.empty((N, nb, 144), np.uint8)
+    out[..., 0:2] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 2:4] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 4:16] = _bytes(rng, (N, nb, 12))
+    out[..., 16:144] = _bytes(rng, (N, nb, 128))
+    return out
+
+
+def q6k_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-3,
+                sc_lo: int = -32, sc_hi: int = 31) -> np.ndarray:
+    """N x K weights as raw Q6_K blocks, uint8 [N, K/256, 210]."""
+    nb = K // QK
+    out = np.empty((N, nb, 210), np.uint8)
+    out[..., 208:210] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 192:208] = rng.integers(sc_lo, sc_hi + 1, size=(N, nb, 16)).astype(np.int8).view(
+        np.uint8)
+    out[..., 0:192] = _bytes(rng, (N, nb, 192))
+    return out
+
+
+def weights(rng: np.random.Generator, type_: int, N: int, K: int) -> np.ndarray:
+    return q4k_weights(rng, N, K) if type_ == Q4_K else q6k_weights(rng, N, K)
+
+
+def activations(rng: np.random.Generator, M: int, K: int, outlier_frac: float = 0.01,
+                outlier_mul: float = 20.0) -> np.ndarray:
+    """M x K float32 ~ N(0,1) with round(outlier_frac*K) columns scaled by outlier_mul."""
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        cols = rng.choice(K, size=n_out, replace=False)
+        x[:, cols] *= np.float32(outlier_mul)
+    return x
+
+
+def row_index(rng: np.random.Generator, L: int, M: int) -> np.ndarray:
+    """M distinct canvas rows of [0, L), sorted ascending, int32."""
+    return np.sort(rng.choice(L, size=M, replace=False)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------- #
+# Workloads (shapes of the five configurations; seeds 1000*config+10*layer+p)  #
+# --------------------------------------------------------------------------- #
+LLADA = dict(L=160, K=4096, ffn=12288, vocab=126464, layers=32)
+DREAM = dict(L=512, K=3584, ffn=18944, kv=512, vocab=152064)
+
+
+def llada_layer(layer: int):
+    """(name, type, N, K) of one LLaDA-8B layer's projections.
+
+    Down is Q6_K on odd layers and Q4_K on even layers.
+    """
+    K, F = LLADA["K"], LLADA["ffn"]
+    down_t = Q6_K if layer % 2 else Q4_K
+    return [("q", Q4_K, K, K), ("k", Q4_K, K, K), ("v", Q4_K, K, K), ("o", Q4_K, K, K),
+            ("gate", Q4_K, F, K), ("up", Q4_K, F, K), ("down", down_t, K, F)]
+
+
+def dream_layer():
+    K, F, KV = DREAM["K"], DREAM["ffn"], DREAM["kv"]
+    return [("q", Q4_K, K, K), ("k", Q4_K, KV, K), ("v", Q4_K, KV, K), ("o", Q4_K, K, K),
+            ("gate", Q4_K, F, K), ("up", Q4_K, F, K), ("down", Q6_K, K, F)]
+
+
+def seed(config: int, layer: int, proj: int) -> int:
+    return 1000 * config + 10 * layer + proj

@@ -1,0 +1,326 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+* fp16 decode: exhaustive against numpy's float16 (an independent library).
+* Q4_K / Q6_K decode: hand-built golden blocks (tests/golden), every 6-bit
+  scale/min value in every slot, and a round trip against the field-level
+  encoder in kq_fields.py (written per weight position, the inverse map).
+* Activation quantization: closed forms (amax -> +-127, integer identity,
+  half-way ties to even, the rounding-error bound, zero blocks, sign and
+  power-of-two scaling symmetry, bsum as a plain integer sum).
+* Sub-block dots and per-super-block sums: numpy int64 brute force straight
+  from the fields; with unit scales the sums reduce to numpy.matmul.
+* Reference GEMM: numpy float64 brute force from the fields; the oracle's own
+  f32 output through the integer decomposition lies within 1e-6 * T.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from kq_fields import (dequant_q4k_fields, dequant_q6k_fields, enc_q4k, enc_q6k,
+                       encode_q4k_matrix, encode_q6k_matrix, random_q4k_fields,
+                       random_q6k_fields)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.split()
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# fp16                                                                        #
+# --------------------------------------------------------------------------- #
+def test_fp16_exhaustive_against_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.fp16_to_f32(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# --------------------------------------------------------------------------- #
+# Q4_K                                                                        #
+# --------------------------------------------------------------------------- #
+def test_q4k_handbuilt_golden():
+    g = _read_golden("q4k_handbuilt.txt")
+    blk = np.array([int(b, 16) for b in g["bytes"]], np.uint8)
+    assert blk.size == 144
+    d, dmin, sc, mn, q = oracle.decode_q4k(blk)
+    assert d == np.float32(g["d"][0]) and dmin == np.float32(g["dmin"][0])
+    assert list(sc) == [int(v) for v in g["sc"]]
+    assert list(mn) == [int(v) for v in g["mn"]]
+    exp_q = np.zeros(256, np.int64)
+    for c in range(4):
+        for l in range(32):
+            exp_q[64 * c + l] = l % 16
+            exp_q[64 * c + 32 + l] = 2 * c + l // 16
+    assert np.array_equal(q.astype(np.int64), exp_q)
+    w = oracle.dequant(oracle.Q4_K, blk, 256)[0]
+    sc_i = np.repeat(np.array(g["sc"], np.float64), 32)
+    mn_i = np.repeat(np.array(g["mn"], np.float64), 32)
+    assert np.array_equal(w, 1.0 * sc_i * exp_q - 0.5 * mn_i)
+
+
+@pytest.mark.parametrize("slot", range(8))
+def test_q4k_every_scale_and_min_value_in_every_slot(slot):
+    rng = np.random.default_rng(100 + slot)
+    for v in range(64):
+        sc = rng.integers(0, 64, 8)
+        mn = rng.integers(0, 64, 8)
+        sc[slot] = v
+        mn[slot] = 63 - v
+        blk = enc_q4k(1.0, 1.0, sc, mn, np.zeros(256, np.int64))
+        _, _, dsc, dmn, _ = oracle.decode_q4k(blk)
+        assert list(dsc) == list(sc) and list(dmn) == list(mn), (slot, v)
+
+
+def test_q4k_random_round_trip():
+    rng = np.random.default_rng(7)
+    f = random_q4k_fields(rng, 6, 3)
+    W = encode_q4k_matrix(f)
+    for n in range(6):
+        for b in range(3):
+            d, dmin, sc, mn, q = oracle.decode_q4k(W[n, b])
+            assert d == np.float32(f["d"][n, b]) and dmin == np.float32(f["dmin"][n, b])
+            assert np.array_equal(sc, f["sc"][n, b]) and np.array_equal(mn, f["mn"][n, b])
+            assert np.array_equal(q, f["q"][n, b])
+    assert np.array_equal(oracle.dequant(oracle.Q4_K, W, 768), dequant_q4k_fields(f))
+
+
+def test_q4k_negative_and_subnormal_superblock_scales():
+    q = np.arange(256) % 16
+    sc = np.arange(8) + 1
+    mn = np.arange(8) * 3
+    sub = np.float16(2.0 ** -20)  # fp16 subnormal
+    blk = enc_q4k(-2.0, sub, sc, mn, q)
+    d, dmin, *_ = oracle.decode_q4k(blk)
+    assert d == -2.0 and dmin == np.float32(2.0 ** -20)
+    w = oracle.dequant(oracle.Q4_K, blk, 256)[0]
+    exp = -2.0 * np.repeat(sc, 32) * q - 2.0 ** -20 * np.repeat(mn, 32)
+    assert np.array_equal(w, exp)
+
+
+# --------------------------------------------------------------------------- #
+# Q6_K                                                                        #
+# --------------------------------------------------------------------------- #
+def test_q6k_handbuilt_golden():
+    g = _read_golden("q6k_handbuilt.txt")
+    blk = np.zeros(210, np.uint8)
+    for item in g["set"]:
+        pos, val = item.split("=")
+        blk[int(pos)] = int(val, 16)
+    d, sc, q = oracle.decode_q6k(blk)
+    assert d == np.float32(g["d"][0])
+    assert list(sc) == [int(v) for v in g["sc"]]
+    exp_q = np.zeros(256, np.int64)
+    for item in g["q"]:
+        i, v = item.split("=")
+        exp_q[int(i)] = int(v)
+    assert np.array_equal(q.astype(np.int64), exp_q)
+    w = oracle.dequant(oracle.Q6_K, blk, 256)[0]
+    sc_i = np.repeat(np.array(g["sc"], np.float64), 16)
+    assert np.array_equal(w, 0.25 * sc_i * (exp_q - 32))
+
+
+def test_q6k_random_round_trip_full_scale_range():
+    rng = np.random.default_rng(8)
+    f = random_q6k_fields(rng, 6, 3)  # scales over the whole int8 range
+    W = encode_q6k_matrix(f)
+    for n in range(6):
+        for b in range(3):
+            d, sc, q = oracle.decode_q6k(W[n, b])
+            assert d == np.float32(f["d"][n, b])
+            assert np.array_equal(sc, f["sc"][n, b]) and np.array_equal(q, f["q"][n, b])
+    assert np.array_equal(oracle.dequant(oracle.Q6_K, W, 768), dequant_q6k_fields(f))
+
+
+def test_q6k_every_code_at_every_quarter():
+    # each 6-bit code value at each of the 8 (half, quarter) positions
+    for h in range(2):
+        for quarter in range(4):
+            for l in (0, 17, 31):
+                for v in range(64):
+                    q = np.zeros(256, np.int64)
+                    q[128 * h + 32 * quarter + l] = v
+                    _, _, dq = oracle.decode_q6k(enc_q6k(1.0, np.ones(16, np.int64), q))
+                    assert np.array_equal(dq, q), (h, quarter, l, v)
+
+
+# --------------------------------------------------------------------------- #
+# Activation quantization                                                     #
+# --------------------------------------------------------------------------- #
+def test_quant_amax_maps_to_127_and_scale():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 512)).astype(np.float32)
+    q, d, bs = oracle.quantize_act(x)
+    for m in range(5):
+        for b in range(2):
+            blk = x[m, 256 * b:256 * (b + 1)]
+            i = np.argmax(np.abs(blk))
+            assert q[m, 256 * b + i] == (127 if blk[i] > 0 else -127)
+            assert d[m, b] == np.float32(np.abs(blk[i])) / np.float32(127)
+
+
+def test_quant_integer_identity():
+    rng = np.random.default_rng(2)
+    x = rng.integers(-127, 128, (3, 768)).astype(np.float32)
+    x[:, ::256] = 127.0  # amax = 127 in every block
+    q, d, bs = oracle.quantize_act(x)
+    assert np.array_equal(q.astype(np.float32), x)
+    assert np.all(d == 1.0)
+
+
+def test_quant_ties_to_even():
+    # amax = 254 -> inv = 0.5 exactly; x = 2k+1 lands on k + 0.5
+    x = np.zeros((1, 256), np.float32)
+    x[0, 0] = 254.0
+    odd = np.arange(1, 254, 2, dtype=np.float32)[:120]
+    x[0, 1:121] = odd
+    x[0, 121:241] = -odd
+    q, d, _ = oracle.quantize_act(x)
+    half = odd / 2.0  # k + 0.5
+    exp = np.where(np.floor(half) % 2 == 0, np.floor(half), np.ceil(half))
+    assert np.array_equal(q[0, 1:121], exp.astype(np.int8))
+    assert np.array_equal(q[0, 121:241], (-exp).astype(np.int8))
+    assert d[0, 0] == np.float32(2.0)
+
+
+def test_quant_error_bound_sign_and_scaling():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 1024)).astype(np.float32) * 3
+    q, d, bs = oracle.quantize_act(x)
+    xhat = q.astype(np.float64) * np.repeat(d, 256, axis=1)
+    bound = np.repeat(d, 256, axis=1) * 0.5 * (1 + 2.0 ** -21)
+    assert np.all(np.abs(x - xhat) <= bound)
+    qn, dn, bn = oracle.quantize_act(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d) and np.array_equal(bn, -bs)
+    for k in (-7, 5):
+        qs, ds, _ = oracle.quantize_act(x * np.float32(2.0 ** k))
+        assert np.array_equal(qs, q) and np.array_equal(ds, d * np.float32(2.0 ** k))
+
+
+def test_quant_zero_block_and_bsum():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 768)).astype(np.float32)
+    x[1, 256:512] = 0.0
+    q, d, bs = oracle.quantize_act(x)
+    assert np.all(q[1, 256:512] == 0) and d[1, 1] == 0.0 and np.all(bs[1, 8:16] == 0)
+    assert np.array_equal(bs, q.astype(np.int64).reshape(3, 24, 32).sum(-1))
+
+
+# --------------------------------------------------------------------------- #
+# Sub-block dots, per-super-block sums, GEMM                                  #
+# --------------------------------------------------------------------------- #
+def _q4k_case(seed, M, N, nb):
+    rng = np.random.default_rng(seed)
+    f = random_q4k_fields(rng, N, nb)
+    W = encode_q4k_matrix(f)
+    x = rng.standard_normal((M, nb * 256)).astype(np.float32)
+    return f, W, x
+
+
+def _q6k_case(seed, M, N, nb, sc_lo=-128, sc_hi=127):
+    rng = np.random.default_rng(seed)
+    f = random_q6k_fields(rng, N, nb, sc_lo, sc_hi)
+    W = encode_q6k_matrix(f)
+    x = rng.standard_normal((M, nb * 256)).astype(np.float32)
+    return f, W, x
+
+
+def test_q4k_subdots_and_sums_brute_force():
+    M, N, nb = 3, 5, 2
+    f, W, x = _q4k_case(11, M, N, nb)
+    q, d, bs = oracle.quantize_act(x)
+    dots = oracle.subdots(oracle.Q4_K, q, W, N)
+    qx = q.astype(np.int64).reshape(M, nb, 8, 32)
+    qw = f["q"].astype(np.int64).reshape(N, nb, 8, 32)
+    exp = np.einsum("mbjk,nbjk->mnbj", qx, qw)
+    assert np.array_equal(dots, exp)
+    S, Mn = oracle.superblock_sums(oracle.Q4_K, q, bs, W, N)
+    assert np.array_equal(S, np.einsum("mnbj,nbj->mnb", exp, f["sc"]))
+    bsx = qx.sum(-1)  # [M, nb, 8]
+    assert np.array_equal(Mn, np.einsum("mbj,nbj->mnb", bsx, f["mn"]))
+
+
+def test_q6k_subdots_and_sums_brute_force():
+    M, N, nb = 3, 5, 2
+    f, W, x = _q6k_case(12, M, N, nb)
+    q, d, bs = oracle.quantize_act(x)
+    dots = oracle.subdots(oracle.Q6_K, q, W, N)
+    qx = q.astype(np.int64).reshape(M, nb, 16, 16)
+    qw = (f["q"].astype(np.int64) - 32).reshape(N, nb, 16, 16)
+    exp = np.einsum("mbjk,nbjk->mnbj", qx, qw)
+    assert np.array_equal(dots, exp)
+    S, Mn = oracle.superblock_sums(oracle.Q6_K, q, bs, W, N)
+    assert np.array_equal(S, np.einsum("mnbj,nbj->mnb", exp, f["sc"]))
+    assert np.all(Mn == 0)
+
+
+def test_unit_scales_reduce_to_integer_matmul():
+    # d = 1, dmin = 0, sc = 1, mn = 0: sum over the row of S is q_x . q_w
+    rng = np.random.default_rng(13)
+    M, N, nb = 4, 6, 3
+    qw = rng.integers(0, 16, (N, nb, 256))
+    W = np.stack([np.stack([enc_q4k(1.0, 0.0, np.ones(8, int), np.zeros(8, int), qw[n, b])
+                            for b in range(nb)]) for n in range(N)])
+    x = rng.integers(-127, 128, (M, nb * 256)).astype(np.float32)
+    x[:, ::256] = 127.0
+    q, d, bs = oracle.quantize_act(x)
+    S, _ = oracle.superblock_sums(oracle.Q4_K, q, bs, W, N)
+    ref = np.matmul(q.astype(np.int64), qw.reshape(N, -1).T)
+    assert np.array_equal(S.sum(-1), ref)
+    y, T = oracle.qgemm_ref(oracle.Q4_K, q, d, W, N)
+    assert np.array_equal(y, ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_gemm_reference_brute_force_and_decomposition(kind):
+    M, N, nb = 5, 7, 3
+    if kind == "q4k":
+        f, W, x = _q4k_case(21, M, N, nb)
+        t, wf = oracle.Q4_K, dequant_q4k_fields(f)
+    else:
+        f, W, x = _q6k_case(22, M, N, nb)
+        t, wf = oracle.Q6_K, dequant_q6k_fields(f)
+    q, d, bs = oracle.quantize_act(x)
+    xh = q.astype(np.float64) * np.repeat(d, 256, axis=1).astype(np.float64)
+    y_bf = xh @ wf.T
+    T_bf = np.abs(xh) @ np.abs(wf).T
+    y, T = oracle.qgemm_ref(t, q, d, W, N)
+    assert np.all(np.abs(y - y_bf) <= 1e-12 * T_bf)
+    assert np.allclose(T, T_bf, rtol=1e-12, atol=0)
+    # the integer decomposition in f64 equals the plain definition
+    S, Mn = oracle.superblock_sums(t, q, bs, W, N)
+    if kind == "q4k":
+        dd, dm = f["d"].astype(np.float64), f["dmin"].astype(np.float64)
+    else:
+        dd, dm = f["d"].astype(np.float64), np.zeros_like(f["d"], np.float64)
+    y_dec = np.einsum("mb,mnb->mn", d.astype(np.float64),
+                      dd[None] * S - dm[None] * Mn.astype(np.float64))
+    assert np.all(np.abs(y_dec - y) <= 1e-12 * T)
+    # the oracle's own binary32 output
+    y32 = oracle.qgemm_f32(t, q, d, bs, W, N)
+    assert np.all(np.abs(y32.astype(np.float64) - y) <= 1e-6 * T)
+    # sampled points agree with the dense routine
+    mi = np.array([0, 4, 2]); ni = np.array([6, 0, 3])
+    yp, Tp = oracle.qgemm_ref_points(t, q, d, W, mi, ni)
+    assert np.array_equal(yp, y[mi, ni]) and np.array_equal(Tp, T[mi, ni])
+
+
+def test_rows_inputs_gather_then_quantize():
+    rng = np.random.default_rng(31)
+    canvas = rng.standard_normal((20, 512)).astype(np.float32)
+    idx = np.array([7, 3, 3, 19, 0], np.int32)
+    q, d, bs = oracle.qgemm_rows_inputs(canvas, idx)
+    qa, da, ba = oracle.quantize_act(canvas)
+    assert np.array_equal(q, qa[idx]) and np.array_equal(d, da[idx]) and np.array_equal(bs, ba[idx])
