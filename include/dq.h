@@ -1,0 +1,185 @@
+/*
+ * dq.h -- C ABI of libdq: GGUF K-quant weight x int8 activation GEMM on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The workload: a diffusion LLM (LLaDA, Dream) run from GGUF files reruns
+ * every Q/K/V/O, gate/up and down projection over the whole canvas of L
+ * tokens on each denoising step, and runs the output projection only on the
+ * canvas rows the sampler may commit (heatdrop.ai "vladimirrott/mojo-dllm"
+ * card, "What it does" and "The interesting bit"; mojo-dllm "Architecture"
+ * page, "A forward pass").  This library is that GEMM and nothing else.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     allocates nothing, keeps no state besides a per-device property cache,
+ *     and is safe to call from several host threads.
+ *   - Every call only validates its arguments on the host and enqueues work on
+ *     `stream`; it returns before the work runs.  Results are visible after
+ *     the caller synchronizes the stream.
+ *   - Shapes: K is the reduction length and must be a positive multiple of
+ *     256 (one K-quant super-block).  M (activation rows) and N (weight rows)
+ *     may be any value >= 0; M == 0 or N == 0 is a valid no-op.
+ *   - Return value: DQ_OK or one of the DQ_E* codes below.  On any error no
+ *     work is enqueued.  dq_last_error() gives a message for the last error
+ *     raised on the calling host thread.
+ *   - Types: weights are GGUF tensors of type DQ_Q4_K or DQ_Q6_K (the GGUF
+ *     type ids).  A 2-D GGUF weight of shape N x K is N rows, each of K/256
+ *     consecutive super-blocks (144 bytes for Q4_K, 210 bytes for Q6_K).
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF tensor type ids of the supported weight blocks. */
+enum { DQ_Q4_K = 12, DQ_Q6_K = 14 };
+
+/* Status codes. */
+enum {
+  DQ_OK = 0,
+  DQ_EINVAL = 1,       /* bad shape, leading dimension, alignment or NULL pointer */
+  DQ_EUNSUPPORTED = 2, /* unknown weight type */
+  DQ_EWORKSPACE = 3,   /* workspace pointer NULL or smaller than required */
+  DQ_EHIP = 4          /* the HIP runtime refused a launch */
+};
+
+/* Human-readable name of a status code (static string). */
+const char *dq_status_string(int status);
+
+/* Message describing the last error returned on this host thread ("" if none). */
+const char *dq_last_error(void);
+
+/* --------------------------------------------------------------------------
+ * dq_packed_size -- bytes of the repacked matrix (host-only, no GPU work).
+ *
+ * The repacked layout holds the same bits as the GGUF blocks (4.5 bits per
+ * Q4_K weight, 6.5625 bits per Q6_K weight), permuted into tiles of 32 weight
+ * rows x one super-block; N is rounded up to a multiple of 32 with zero rows.
+ * bytes = ceil(N/32) * 32 * (K/256) * block_bytes.
+ * Errors: DQ_EUNSUPPORTED (type), DQ_EINVAL (K, N < 0, bytes NULL).
+ * ------------------------------------------------------------------------ */
+int dq_packed_size(int type, int64_t N, int64_t K, size_t *bytes);
+
+/* --------------------------------------------------------------------------
+ * dq_repack_weights -- load-time permutation of GGUF K-quant blocks into the
+ * gfx950 tile layout used by dq_qgemm / dq_qgemm_rows.
+ *
+ * Source: the pages' load-time repack (heatdrop.ai card, "The interesting
+ * bit"; Architecture page, "Memory": every projection matrix is repacked once
+ * at load and stays resident; Q4_K stays 4-bit).  Here it is a lossless
+ * permutation at the same bit-width (Q6_K is not expanded).
+ *
+ *   gguf   : device, N*(K/256) blocks, row-major as in the GGUF file; read only.
+ *   packed : device, dq_packed_size() bytes, 16-byte aligned; written fully
+ *            (padding rows are zero).  Must not overlap gguf.
+ * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (shape, NULL, alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_repack_weights(int type, int64_t N, int64_t K, const void *gguf, void *packed,
+                      hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_quantize_act -- f32 activations -> int8 codes, one f32 scale per 256.
+ *
+ * Source: Architecture page, "Source map" (kernels/qgemm.mojo): activation
+ * quantization, int8 with one scale per 256 values; "A forward pass", step 2:
+ * one quantization feeds several projections (Q, K, V; gate and up).
+ * Rule, per row m and 256-block b, all in IEEE binary32:
+ *   amax = max |x|; if amax == 0: d = 0 and every code is 0;
+ *   else inv = 127/amax (correctly rounded), q = clamp(rint(x*inv), -127, 127)
+ *   with ties to even, d = amax/127.
+ *   bsum[m][k/32] = sum of the 32 codes of each group (int32).
+ * The codes, scales and sums are bit-identical to any binary32 implementation
+ * of these steps.  Inputs must be finite; amax below 127/FLT_MAX is out of
+ * domain.
+ *
+ *   x    : device f32, M rows, row stride ldx >= K floats; read only.
+ *   q    : device int8 [M][K] (row stride K), 16-byte aligned.
+ *   d    : device f32 [M][K/256].
+ *   bsum : device int32 [M][K/32], 16-byte aligned.
+ * Errors: DQ_EINVAL (shape, ldx < K, NULL, alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *q, float *d,
+                    int32_t *bsum, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_qgemm -- y[m][n] = sum_k w^[n][k] * x^[m][k] for int8 activations and a
+ * repacked K-quant weight matrix.
+ *
+ * Source: Architecture page, "Source map" (kernels/packed.mojo: the GEMM used
+ * for every projection; gpu/kernels.mojo: an int8 matrix-core GEMM over Q4_K /
+ * Q6_K blocks).  x^ = d[m][k/256] * q[m][k];  w^ = d*sc_j*q - dmin*m_j (Q4_K,
+ * 32-wide sub-blocks) or d*sc_j*(q-32) (Q6_K, 16-wide sub-blocks).  The kernel
+ * forms, for every (m, n, super-block b), the exact integer
+ *   S = sum_j sc_j * dot_j  (dot_j = int32 dot of the codes of sub-block j)
+ *   Mn = sum_j m_j * bsum_j (Q4_K only)
+ * on int8 matrix cores and folds y += d_x*(d*S - dmin*Mn) in binary32.
+ * |y - y_exact| stays far below 1e-4 * sum_k |w^ x^|.
+ *
+ *   q, d, bsum : the outputs of dq_quantize_act for these M rows (bsum may be
+ *                NULL for Q6_K).
+ *   packed     : output of dq_repack_weights for (type, N, K).
+ *   y          : device f32, M rows, row stride ldy >= N; columns [0, N) of
+ *                each row are written, nothing else.
+ * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (shape, ldy < N, NULL, alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *d,
+             const int32_t *bsum, const void *packed, float *y, int64_t ldy, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_qgemm_rows_workspace -- workspace bytes dq_qgemm_rows needs for M
+ * gathered rows of length K (host-only).
+ * ------------------------------------------------------------------------ */
+int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes);
+
+/* --------------------------------------------------------------------------
+ * dq_qgemm_rows -- output projection on the requested canvas rows only.
+ *
+ * Source: Architecture page, "A forward pass": the caller gives a canvas of L
+ * tokens and the list of positions whose logits it needs; the final
+ * projection runs on those rows only (heatdrop.ai card, "The interesting
+ * bit": logits only for positions the sampler can commit).
+ * Output row i is canvas row idx[i] quantized by the dq_quantize_act rule and
+ * multiplied by the weights exactly as dq_qgemm does.
+ *
+ *   canvas : device f32, L rows, row stride ldc >= K floats; read only.
+ *   idx    : device int32 [M], values in [0, L); any order; duplicates allowed.
+ *            An index outside [0, L) is never dereferenced: its row is taken
+ *            as zeros and int32 word i of the workspace's flag array (the
+ *            first 4*M bytes of ws) is set to 1 (0 for valid rows).
+ *   packed : output of dq_repack_weights for (type, N, K).
+ *   y      : device f32, M rows, row stride ldy >= N.
+ *   ws     : device workspace of at least dq_qgemm_rows_workspace(M, K) bytes,
+ *            256-byte aligned; its contents are overwritten.
+ * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (shape, NULL, alignment),
+ *         DQ_EWORKSPACE (ws NULL or ws_bytes too small), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
+                  int64_t ldc, const int32_t *idx, const void *packed, float *y, int64_t ldy,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_debug_superblock_sums -- test hook.  Runs the dq_qgemm kernel with its
+ * fold replaced by stores of the exact per-super-block integers, so that the
+ * integer part of the production code path can be compared bit for bit:
+ *   S[(m*N + n)*(K/256) + b]  = sum_j sc_j * dot_j
+ *   Mn[(m*N + n)*(K/256) + b] = sum_j m_j * bsum_j   (Q4_K; 0 for Q6_K)
+ * With every scale but sub-block j's set to 0 (and that one to 1) S equals
+ * the sub-block dot dot_j, which is how per-sub-block dots are checked.
+ * S and Mn are device int32 arrays of M*N*(K/256) entries.
+ * ------------------------------------------------------------------------ */
+int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                             const int32_t *bsum, const void *packed, int32_t *S, int32_t *Mn,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQ_H */

@@ -1,0 +1,225 @@
+"""Python binding of libdq (include/dq.h): the GGUF K-quant x int8 GEMM on MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of libdq.so,
+which must have been built in-tree (``__graft_entry__.build()`` or
+``python quantized_gemm_diffusion_amd/_build.py``).  There is no fallback: if
+the library is missing, every call raises.  torch supplies device memory and
+the current stream; tensors must live on a GPU.
+
+Names follow the C ABI:
+  packed_size, repack_weights, quantize_act, qgemm, qgemm_rows_workspace,
+  qgemm_rows, debug_superblock_sums.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+Q4_K = 12
+Q6_K = 14
+QK = 256
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+
+DQ_OK, DQ_EINVAL, DQ_EUNSUPPORTED, DQ_EWORKSPACE, DQ_EHIP = 0, 1, 2, 3, 4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdq.so")
+
+EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_weights",
+           "dq_quantize_act", "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows",
+           "dq_debug_superblock_sums")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class DQError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdq.so and declare the C signatures.  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        i32, i64, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        psz = ctypes.POINTER(ctypes.c_size_t)
+        lib.dq_status_string.restype = ctypes.c_char_p
+        lib.dq_status_string.argtypes = [i32]
+        lib.dq_last_error.restype = ctypes.c_char_p
+        lib.dq_last_error.argtypes = []
+        sigs = {
+            "dq_packed_size": [i32, i64, i64, psz],
+            "dq_repack_weights": [i32, i64, i64, vp, vp, vp],
+            "dq_quantize_act": [i64, i64, vp, i64, vp, vp, vp, vp],
+            "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp],
+            "dq_qgemm_rows_workspace": [i64, i64, psz],
+            "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
+            "dq_debug_superblock_sums": [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp],
+        }
+        for name, args in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype = i32
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _check(status: int, where: str):
+    if status != DQ_OK:
+        lib = load_library()
+        raise DQError(status, where, lib.dq_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise ValueError("libdq works on GPU tensors only")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def packed_size(type_: int, N: int, K: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_packed_size(type_, N, K, ctypes.byref(out)), "dq_packed_size")
+    return out.value
+
+
+def repack_weights(type_: int, N: int, K: int, gguf: torch.Tensor,
+                   packed: torch.Tensor | None = None) -> torch.Tensor:
+    """GGUF blocks (uint8, N*(K/256)*block bytes, on the GPU) -> packed tiles."""
+    lib = load_library()
+    _need(gguf, torch.uint8, "gguf")
+    if not gguf.is_contiguous() or gguf.numel() != N * (K // QK) * BLOCK_BYTES.get(type_, 0):
+        raise ValueError("gguf must be contiguous with N*(K/256) blocks of the given type")
+    if packed is None:
+        packed = torch.empty(packed_size(type_, N, K), dtype=torch.uint8, device=gguf.device)
+    _need(packed, torch.uint8, "packed")
+    _check(lib.dq_repack_weights(type_, N, K, _ptr(gguf), _ptr(packed), _stream(gguf)),
+           "dq_repack_weights")
+    return packed
+
+
+def quantize_act(x: torch.Tensor, q=None, d=None, bsum=None):
+    """f32 [M, K] (row stride >= K, unit column stride) -> (q int8, d f32, bsum int32)."""
+    lib = load_library()
+    _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    dev = x.device
+    q = torch.empty((M, K), dtype=torch.int8, device=dev) if q is None else q
+    d = torch.empty((M, K // QK), dtype=torch.float32, device=dev) if d is None else d
+    bsum = torch.empty((M, K // 32), dtype=torch.int32, device=dev) if bsum is None else bsum
+    _need(q, torch.int8, "q"), _need(d, torch.float32, "d"), _need(bsum, torch.int32, "bsum")
+    for t, shape, name in ((q, (M, K), "q"), (d, (M, K // QK), "d"), (bsum, (M, K // 32), "bsum")):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with shape {shape}")
+    _check(lib.dq_quantize_act(M, K, _ptr(x), x.stride(0) if M > 1 else K, _ptr(q), _ptr(d),
+                               _ptr(bsum), _stream(x)), "dq_quantize_act")
+    return q, d, bsum
+
+
+def _check_operands(type_, q, d, bsum, packed, N):
+    """Shape/size checks that keep every kernel access inside the tensors."""
+    _need(q, torch.int8, "q")
+    if q.dim() != 2 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [M, K] int8 tensor")
+    M, K = q.shape
+    if d is not None:
+        _need(d, torch.float32, "d")
+        if tuple(d.shape) != (M, K // QK) or not d.is_contiguous():
+            raise ValueError(f"d must be contiguous [{M}, {K // QK}]")
+    if bsum is not None:
+        _need(bsum, torch.int32, "bsum")
+        if tuple(bsum.shape) != (M, K // 32) or not bsum.is_contiguous():
+            raise ValueError(f"bsum must be contiguous [{M}, {K // 32}]")
+    _need(packed, torch.uint8, "packed")
+    if packed.numel() < packed_size(type_, N, K) or not packed.is_contiguous():
+        raise ValueError("packed is smaller than packed_size(type, N, K)")
+    return M, K
+
+
+def qgemm(type_: int, q: torch.Tensor, d: torch.Tensor, bsum: torch.Tensor | None,
+          packed: torch.Tensor, N: int, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] f32 = dequant(q, d) @ dequant(packed)^T."""
+    lib = load_library()
+    M, K = _check_operands(type_, q, d, bsum, packed, N)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    _need(y, torch.float32, "y")
+    if y.dim() != 2 or y.shape[0] != M or y.shape[1] < N or y.stride(1) != 1:
+        raise ValueError("y must be [M, >=N] with unit column stride")
+    _check(lib.dq_qgemm(type_, M, N, K, _ptr(q), _ptr(d), _ptr(bsum), _ptr(packed), _ptr(y),
+                        y.stride(0) if M > 1 else N, _stream(q)), "dq_qgemm")
+    return y
+
+
+def qgemm_rows_workspace(M: int, K: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_qgemm_rows_workspace(M, K, ctypes.byref(out)), "dq_qgemm_rows_workspace")
+    return out.value
+
+
+def qgemm_rows(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packed: torch.Tensor,
+               N: int, y: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Logits for canvas rows idx only: y [M, N] f32."""
+    lib = load_library()
+    _need(canvas, torch.float32, "canvas")
+    _need(idx, torch.int32, "idx")
+    if canvas.dim() != 2 or canvas.stride(1) != 1:
+        raise ValueError("canvas must be 2-D with unit column stride")
+    L, K = canvas.shape
+    M = idx.numel()
+    if not idx.is_contiguous():
+        raise ValueError("idx must be contiguous")
+    _need(packed, torch.uint8, "packed")
+    if packed.numel() < packed_size(type_, N, K) or not packed.is_contiguous():
+        raise ValueError("packed is smaller than packed_size(type, N, K)")
+    dev = canvas.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(qgemm_rows_workspace(M, K), dtype=torch.uint8, device=dev)
+    _need(y, torch.float32, "y")
+    if y.dim() != 2 or y.shape[0] != M or y.shape[1] < N or y.stride(1) != 1:
+        raise ValueError("y must be [M, >=N] with unit column stride")
+    _need(ws, torch.uint8, "ws")
+    _check(lib.dq_qgemm_rows(type_, L, M, N, K, _ptr(canvas), canvas.stride(0) if L > 1 else K,
+                             _ptr(idx), _ptr(packed), _ptr(y),
+                             y.stride(0) if M > 1 else N, _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(canvas)), "dq_qgemm_rows")
+    return y, ws
+
+
+def debug_superblock_sums(type_: int, q: torch.Tensor, bsum: torch.Tensor | None,
+                          packed: torch.Tensor, N: int):
+    """Exact per-(m, n, super-block) integers (S, Mn) from the GEMM kernel's own path."""
+    lib = load_library()
+    M, K = _check_operands(type_, q, None, bsum, packed, N)
+    nb = K // QK
+    S = torch.empty((M, N, nb), dtype=torch.int32, device=q.device)
+    Mn = torch.empty((M, N, nb), dtype=torch.int32, device=q.device)
+    _check(lib.dq_debug_superblock_sums(type_, M, N, K, _ptr(q), _ptr(bsum), _ptr(packed),
+                                        _ptr(S), _ptr(Mn), _stream(q)),
+           "dq_debug_superblock_sums")
+    return S, Mn

@@ -1,0 +1,210 @@
+// dq_api.hip -- the C ABI of libdq (declared in include/dq.h): argument
+// checks on the host, then one or two kernel launches on the caller's stream.
+// Nothing here allocates device memory or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dq.h"
+#include "dq_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return DQ_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int block_bytes(int type) { return type == DQ_Q4_K ? dq::Q4K_BLOCK : dq::Q6K_BLOCK; }
+
+int check_type(int type) {
+  if (type != DQ_Q4_K && type != DQ_Q6_K)
+    return fail(DQ_EUNSUPPORTED, "unsupported weight type %d (Q4_K = 12, Q6_K = 14)", type);
+  return DQ_OK;
+}
+
+int check_k(int64_t K) {
+  if (K <= 0 || K % dq::QK)
+    return fail(DQ_EINVAL, "K = %lld must be a positive multiple of 256", (long long)K);
+  if (K > (int64_t)1 << 24) return fail(DQ_EINVAL, "K = %lld too large", (long long)K);
+  return DQ_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+  if (e != hipSuccess)
+    return fail(DQ_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" {
+
+const char *dq_status_string(int status) {
+  switch (status) {
+    case DQ_OK: return "DQ_OK";
+    case DQ_EINVAL: return "DQ_EINVAL";
+    case DQ_EUNSUPPORTED: return "DQ_EUNSUPPORTED";
+    case DQ_EWORKSPACE: return "DQ_EWORKSPACE";
+    case DQ_EHIP: return "DQ_EHIP";
+    default: return "DQ_UNKNOWN";
+  }
+}
+
+const char *dq_last_error(void) { return g_err; }
+
+int dq_packed_size(int type, int64_t N, int64_t K, size_t *bytes) {
+  if (int s = check_type(type)) return s;
+  if (int s = check_k(K)) return s;
+  if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
+  const int64_t ntiles = (N + dq::TILE_N - 1) / dq::TILE_N;
+  *bytes = (size_t)ntiles * dq::TILE_N * (size_t)(K / dq::QK) * (size_t)block_bytes(type);
+  return ok();
+}
+
+int dq_repack_weights(int type, int64_t N, int64_t K, const void *gguf, void *packed,
+                      hipStream_t stream) {
+  size_t bytes = 0;
+  if (int s = dq_packed_size(type, N, K, &bytes)) return s;
+  if (N == 0) return ok();
+  if (!gguf || !packed) return fail(DQ_EINVAL, "gguf or packed is NULL");
+  if (!aligned(packed, 16)) return fail(DQ_EINVAL, "packed must be 16-byte aligned");
+  const uint8_t *s = static_cast<const uint8_t *>(gguf);
+  const uint8_t *p = static_cast<const uint8_t *>(packed);
+  const size_t src_bytes = (size_t)N * (size_t)(K / dq::QK) * (size_t)block_bytes(type);
+  if (s < p + bytes && p < s + src_bytes) return fail(DQ_EINVAL, "gguf and packed overlap");
+  if (K / dq::QK > 65535) return fail(DQ_EINVAL, "K too large for the repack grid");
+  return launched(dq::launch_repack(type, N, K, s, static_cast<uint8_t *>(packed), stream),
+                  "dq_repack_weights");
+}
+
+int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *q, float *d,
+                    int32_t *bsum, hipStream_t stream) {
+  if (int s = check_k(K)) return s;
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (ldx < K) return fail(DQ_EINVAL, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (M == 0) return ok();
+  if (!x || !q || !d || !bsum) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(q, 16) || !aligned(bsum, 16) || !aligned(d, 4) || !aligned(x, 4))
+    return fail(DQ_EINVAL, "q and bsum must be 16-byte aligned, x and d 4-byte aligned");
+  return launched(dq::launch_quantize(M, K, x, ldx, nullptr, 0, q, d, bsum, nullptr, stream),
+                  "dq_quantize_act");
+}
+
+static int check_gemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                      const float *d, const int32_t *bsum, const void *packed, bool need_d) {
+  if (int s = check_type(type)) return s;
+  if (int s = check_k(K)) return s;
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if ((M + 31) / 32 > 2147483647LL || (N + 31) / 32 > 65535)
+    return fail(DQ_EINVAL, "M or N too large for the GEMM grid");
+  if (M == 0 || N == 0) return DQ_OK;
+  if (!q || !packed || (need_d && !d)) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (type == DQ_Q4_K && !bsum) return fail(DQ_EINVAL, "bsum is required for Q4_K");
+  if (!aligned(q, 16) || !aligned(packed, 16) || (bsum && !aligned(bsum, 16)) ||
+      (d && !aligned(d, 4)))
+    return fail(DQ_EINVAL, "q, bsum and packed must be 16-byte aligned, d 4-byte aligned");
+  return DQ_OK;
+}
+
+int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *d,
+             const int32_t *bsum, const void *packed, float *y, int64_t ldy, hipStream_t stream) {
+  if (int s = check_gemm(type, M, N, K, q, d, bsum, packed, true)) return s;
+  if (ldy < N) return fail(DQ_EINVAL, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  if (!y || !aligned(y, 4)) return fail(DQ_EINVAL, "y is NULL or not 4-byte aligned");
+  return launched(dq::launch_qgemm(type, M, N, K, q, d, bsum,
+                                   static_cast<const uint8_t *>(packed), y, ldy, nullptr,
+                                   nullptr, stream),
+                  "dq_qgemm");
+}
+
+// Workspace: [flags int32 x M | pad to 256] [q int8 M x K] [d f32 M x K/256 | pad]
+//            [bsum int32 M x K/32]
+static size_t rows_ws_layout(int64_t M, int64_t K, size_t *off_q, size_t *off_d,
+                             size_t *off_b) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  size_t o = up((size_t)M * 4);
+  *off_q = o;
+  o = up(o + (size_t)M * (size_t)K);
+  *off_d = o;
+  o = up(o + (size_t)M * (size_t)(K / dq::QK) * 4);
+  *off_b = o;
+  o = up(o + (size_t)M * (size_t)(K / 32) * 4);
+  return o;
+}
+
+int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes) {
+  if (int s = check_k(K)) return s;
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
+  size_t a, b, c;
+  *bytes = rows_ws_layout(M, K, &a, &b, &c);
+  return ok();
+}
+
+int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
+                  int64_t ldc, const int32_t *idx, const void *packed, float *y, int64_t ldy,
+                  void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (int s = check_type(type)) return s;
+  if (int s = check_k(K)) return s;
+  if (L < 0 || L > kMaxRows) return fail(DQ_EINVAL, "L = %lld out of range", (long long)L);
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if (ldc < K) return fail(DQ_EINVAL, "ldc = %lld < K = %lld", (long long)ldc, (long long)K);
+  if (ldy < N) return fail(DQ_EINVAL, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  if (!canvas || !idx || !packed || !y) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(canvas, 4) || !aligned(idx, 4) || !aligned(y, 4) || !aligned(packed, 16))
+    return fail(DQ_EINVAL, "canvas, idx, y must be 4-byte aligned, packed 16-byte aligned");
+  size_t off_q, off_d, off_b;
+  const size_t need = rows_ws_layout(M, K, &off_q, &off_d, &off_b);
+  if (!ws || ws_bytes < need)
+    return fail(DQ_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned(ws, 256)) return fail(DQ_EINVAL, "workspace must be 256-byte aligned");
+  if (int s = check_gemm(type, M, N, K, (const int8_t *)ws, (const float *)ws,
+                         (const int32_t *)ws, packed, true))
+    return s;
+  uint8_t *w = static_cast<uint8_t *>(ws);
+  int32_t *flags = reinterpret_cast<int32_t *>(w);
+  int8_t *q = reinterpret_cast<int8_t *>(w + off_q);
+  float *d = reinterpret_cast<float *>(w + off_d);
+  int32_t *bs = reinterpret_cast<int32_t *>(w + off_b);
+  hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, q, d, bs, flags, stream);
+  if (e != hipSuccess) return launched(e, "dq_qgemm_rows (gather-quantize)");
+  return launched(dq::launch_qgemm(type, M, N, K, q, d, bs, static_cast<const uint8_t *>(packed),
+                                   y, ldy, nullptr, nullptr, stream),
+                  "dq_qgemm_rows (gemm)");
+}
+
+int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                             const int32_t *bsum, const void *packed, int32_t *S, int32_t *Mn,
+                             hipStream_t stream) {
+  if (int s = check_gemm(type, M, N, K, q, nullptr, bsum, packed, false)) return s;
+  if (M == 0 || N == 0) return ok();
+  if (!S || !Mn || !aligned(S, 4) || !aligned(Mn, 4))
+    return fail(DQ_EINVAL, "S and Mn must be non-NULL and 4-byte aligned");
+  return launched(dq::launch_qgemm(type, M, N, K, q, nullptr, bsum,
+                                   static_cast<const uint8_t *>(packed), nullptr, N, S, Mn,
+                                   stream),
+                  "dq_debug_superblock_sums");
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// dq_internal.h -- private to libdq: tile layout, vector types and launchers.
+//
+// Packed weight layout (written by dq_repack_weights, read by the GEMMs).
+// Weights are cut into tiles of 32 weight rows (n) x one 256-wide super-block
+// (b); tiles are stored n-tile-major, so the tiles one n-tile needs over the
+// whole reduction are contiguous:  tile(nt, b) at ((nt * nb) + b) * TILE_BYTES.
+//
+// Inside a tile every plane is laid out for the 32x32x32 int8 MFMA: lane l of
+// a wave owns weight row n = l % 32 of the tile and the k-half g = l / 32 of
+// each 32-wide k chunk c (c = 0..7), i.e. codes at k = 32c + 16g + p,
+// p = 0..15.  A 16-byte per-lane record holds the 4-bit parts of two chunks:
+// dword t (t = 0..3) covers chunk 2i + t/2 (record i), half h = t % 2, and its
+// byte e (e = 0..3) carries code p = 8h + e in the low nibble and code
+// p = 8h + 4 + e in the high nibble.  Records are [i][lane][16 B].
+//
+//   Q4_K tile (4608 B = 32 x 144):
+//     [0, 512)     heads: per row n, the 16 GGUF header bytes d, dmin, scales[12]
+//     [512, 4608)  codes: 4 records x 64 lanes x 16 B (the layout above)
+//   Q6_K tile (6720 B = 32 x 210):
+//     [0, 4096)    low 4 bits of the codes: 4 records x 64 lanes x 16 B
+//     [4096, 6144) high 2 bits: 2 records x 64 lanes x 16 B; dword t of record
+//                  i covers chunk 4i + t; its byte e holds the 2-bit parts of
+//                  codes p = e, 4+e, 8+e, 12+e at bits 0, 2, 4, 6
+//     [6144, 6656) scales: [g][n][8 B], byte c = scale of sub-block 2c + g
+//     [6656, 6720) d: [n] fp16
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dq {
+
+constexpr int QK = 256;
+constexpr int TILE_N = 32;
+constexpr int Q4K_BLOCK = 144;
+constexpr int Q6K_BLOCK = 210;
+constexpr int Q4K_TILE = TILE_N * Q4K_BLOCK;  // 4608
+constexpr int Q6K_TILE = TILE_N * Q6K_BLOCK;  // 6720
+constexpr int Q4K_CODES_OFF = 512;
+constexpr int Q6K_QH_OFF = 4096;
+constexpr int Q6K_SC_OFF = 6144;
+constexpr int Q6K_D_OFF = 6656;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, const int32_t *idx,
+                           int64_t L, int8_t *q, float *d, int32_t *bsum, int32_t *err,
+                           hipStream_t stream);
+hipError_t launch_repack(int type, int64_t N, int64_t K, const uint8_t *src, uint8_t *dst,
+                         hipStream_t stream);
+hipError_t launch_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
+                        const float *d, const int32_t *bsum, const uint8_t *packed, float *y,
+                        int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream);
+
+}  // namespace dq

@@ -1,0 +1,91 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/dq.h
+declares, and its host-side checks return the documented status codes (none of
+these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dq.h")
+
+dq = pytest.importorskip("quantized_gemm_diffusion_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dq.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return dq.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dq_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    assert sorted(dq.EXPORTS) == syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(lib):
+    assert lib.dq_status_string(dq.DQ_OK) == b"DQ_OK"
+    assert lib.dq_status_string(dq.DQ_EWORKSPACE) == b"DQ_EWORKSPACE"
+    assert lib.dq_status_string(99) == b"DQ_UNKNOWN"
+
+
+@pytest.mark.parametrize("type_,N,K,exp", [
+    (dq.Q4_K, 4096, 4096, 4096 * 16 * 144),
+    (dq.Q6_K, 126464, 4096, 126464 * 16 * 210),
+    (dq.Q4_K, 33, 512, 64 * 2 * 144),      # rounded up to 32-row tiles
+    (dq.Q6_K, 1, 256, 32 * 210),
+    (dq.Q4_K, 0, 256, 0),
+])
+def test_packed_size(lib, type_, N, K, exp):
+    assert dq.packed_size(type_, N, K) == exp
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_host_checks_return_codes(lib):
+    out = ctypes.c_size_t()
+    assert lib.dq_packed_size(13, 32, 256, ctypes.byref(out)) == dq.DQ_EUNSUPPORTED
+    assert lib.dq_packed_size(dq.Q4_K, 32, 300, ctypes.byref(out)) == dq.DQ_EINVAL
+    assert b"multiple of 256" in lib.dq_last_error()
+    assert lib.dq_packed_size(dq.Q4_K, -1, 256, ctypes.byref(out)) == dq.DQ_EINVAL
+    assert lib.dq_packed_size(dq.Q4_K, 32, 256, None) == dq.DQ_EINVAL
+    # NULL device pointers are refused before any launch
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 256, None, None, None, None, None, 32, None) == dq.DQ_EINVAL
+    assert lib.dq_qgemm(15, 4, 32, 256, None, None, None, None, None, 32, None) == dq.DQ_EUNSUPPORTED
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 16, 16, 16, 16, 16, 31, None) == dq.DQ_EINVAL  # ldy < N
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 16, 16, None, 16, 16, 32, None) == dq.DQ_EINVAL  # Q4_K needs bsum
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 8, 16, 16, 16, 16, 32, None) == dq.DQ_EINVAL  # q misaligned
+    assert lib.dq_quantize_act(4, 512, 16, 500, 16, 16, 16, None) == dq.DQ_EINVAL  # ldx < K
+    assert lib.dq_quantize_act(4, 100, 16, 100, 16, 16, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_repack_weights(dq.Q6_K, 32, 256, None, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_repack_weights(dq.Q6_K, 32, 256, 16, 8, None) == dq.DQ_EINVAL  # packed misaligned
+    # empty shapes are valid no-ops
+    assert lib.dq_qgemm(dq.Q4_K, 0, 32, 256, None, None, None, None, None, 32, None) == dq.DQ_OK
+    assert lib.dq_quantize_act(0, 256, None, 256, None, None, None, None) == dq.DQ_OK
+
+
+def test_rows_workspace(lib):
+    need = dq.qgemm_rows_workspace(32, 4096)
+    assert need >= 32 * 4 + 32 * 4096 + 32 * 16 * 4 + 32 * 128 * 4
+    assert need % 256 == 0
+    # short workspace -> DQ_EWORKSPACE, before anything is launched
+    st = lib.dq_qgemm_rows(dq.Q6_K, 160, 32, 126464, 4096, 256, 4096, 256, 256, 256, 126464,
+                           256, need - 1, None)
+    assert st == dq.DQ_EWORKSPACE
+    st = lib.dq_qgemm_rows(dq.Q6_K, 160, 32, 126464, 4096, 256, 4096, 256, 256, 256, 126464,
+                           None, need, None)
+    assert st == dq.DQ_EWORKSPACE
+    assert lib.dq_qgemm_rows_workspace(4, 100, None) == dq.DQ_EINVAL

@@ -1,0 +1,100 @@
+"""Parity at the workloads' full sizes, on sampled outputs.
+
+Every GEMM of the LLaDA-8B (L = 160) and Dream-7B (L = 512) projection sets,
+and the gathered-row output projections (LLaDA vocab 126,464 at M = 1, 8, 32 of
+160 rows; Dream vocab 152,064 at M = 64 of 512 rows), run through the C ABI in
+the launch configuration the benchmark uses.  The quantizer is compared bit
+for bit on the whole activation; 1,024 sampled outputs per GEMM are compared
+with the oracle's f64 plain definition (|err| <= 1e-4 * T); every output must
+be finite.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-4
+SAMPLES = 1024
+
+
+@pytest.fixture(scope="module")
+def dq():
+    import quantized_gemm_diffusion_amd as m
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load_library()
+    return m
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _sampled_check(type_, xq, xd, W, y, seed, what):
+    M, N = y.shape
+    rng = np.random.default_rng(seed)
+    mi = rng.integers(0, M, SAMPLES)
+    ni = rng.integers(0, N, SAMPLES)
+    mi[:4] = [0, M - 1, 0, M - 1]
+    ni[:4] = [0, N - 1, N - 1, 0]
+    yr, T = oracle.qgemm_ref_points(type_, xq, xd, W, mi, ni)
+    err = np.abs(y[mi, ni].astype(np.float64) - yr)
+    assert np.all(np.isfinite(y)), what
+    assert np.all(err <= TOL * T), f"{what}: worst err/T {np.max(err / T):.3g}"
+
+
+def _run_set(dq, layers, M, K_act, seed0):
+    x = synth.activations(np.random.default_rng(seed0), M, K_act)
+    xq, xd, xb = oracle.quantize_act(x)
+    q, d, b = dq.quantize_act(_t(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), xq) and np.array_equal(b.cpu().numpy(), xb)
+    assert np.array_equal(d.cpu().numpy(), xd)
+    return x, (xq, xd, xb), (q, d, b)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def test_llada_projection_full_size(dq, name):
+    proj = {p[0]: p for p in synth.llada_layer(1)}[name]  # layer 1: down is Q6_K
+    _, type_, N, K = proj
+    M = synth.LLADA["L"]
+    W = synth.weights(np.random.default_rng(synth.seed(1, 1, ["q", "k", "v", "o", "gate", "up",
+                                                              "down"].index(name))), type_, N, K)
+    _, (xq, xd, xb), (q, d, b) = _run_set(dq, None, M, K, 1000 + K)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(type_, q, d, b, packed, N).cpu().numpy()
+    _sampled_check(type_, xq, xd, W, y, 7, f"LLaDA {name}")
+
+
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def test_dream_projection_full_size(dq, name):
+    proj = {p[0]: p for p in synth.dream_layer()}[name]
+    _, type_, N, K = proj
+    M = synth.DREAM["L"]
+    W = synth.weights(np.random.default_rng(synth.seed(4, 0, ["q", "k", "v", "o", "gate", "up",
+                                                              "down"].index(name))), type_, N, K)
+    _, (xq, xd, xb), (q, d, b) = _run_set(dq, None, M, K, 4000 + K)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(type_, q, d, b, packed, N).cpu().numpy()
+    _sampled_check(type_, xq, xd, W, y, 8, f"Dream {name}")
+
+
+@pytest.mark.parametrize("model,Ms", [("llada", (1, 8, 32)), ("dream", (64,))])
+def test_logits_rows_full_size(dq, model, Ms):
+    cfg = synth.LLADA if model == "llada" else synth.DREAM
+    L, K, V = cfg["L"], cfg["K"], cfg["vocab"]
+    rng = np.random.default_rng(3 if model == "llada" else 5)
+    canvas = synth.activations(rng, L, K)
+    W = synth.q6k_weights(np.random.default_rng(synth.seed(3, 0, 7)), V, K)
+    packed = dq.repack_weights(oracle.Q6_K, V, K, _t(W.reshape(-1)))
+    ct = _t(canvas)
+    for M in Ms:
+        idx = synth.row_index(np.random.default_rng(100 + M), L, M)
+        y, ws = dq.qgemm_rows(oracle.Q6_K, ct, _t(idx), packed, V)
+        yn = y.cpu().numpy()
+        gq, gd, _ = oracle.qgemm_rows_inputs(canvas, idx)
+        _sampled_check(oracle.Q6_K, gq, gd, W, yn, 9 + M, f"{model} logits M={M}")

@@ -1,0 +1,279 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Bit-exact: int8 codes, scales and code sums of the quantizer; the repacked
+layout; the per-super-block integers S and Mn of the GEMM's own code path; the
+per-sub-block dots (unit-scale probes).  Floating point: every output within
+1e-4 * T[m, n], T = sum_k |w^[n,k] * x^[m,k]| in f64 (the tolerance of the
+method's statement), against the oracle's plain f64 definition.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from kq_fields import (encode_q4k_matrix, encode_q6k_matrix, random_q4k_fields,
+                       random_q6k_fields)
+from packed_layout import read_tile
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dq():
+    import quantized_gemm_diffusion_amd as m
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    m.load_library()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _weights(type_, N, K, seed, full_scales=False):
+    rng = np.random.default_rng(seed)
+    if type_ == oracle.Q4_K:
+        return synth.q4k_weights(rng, N, K)
+    if full_scales:
+        return synth.q6k_weights(rng, N, K, sc_lo=-128, sc_hi=127)
+    return synth.q6k_weights(rng, N, K)
+
+
+def _check_tol(y, yr, T, what):
+    err = np.abs(np.asarray(y, np.float64) - yr)
+    bad = err > TOL * T
+    assert not bad.any(), f"{what}: {bad.sum()} outputs out of tolerance, worst err/T " \
+                          f"{np.max(err / np.maximum(T, 1e-300)):.3g}"
+
+
+# --------------------------------------------------------------------------- #
+# Activation quantization: bit-exact                                          #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("M,K,seed", [(1, 256, 0), (17, 512, 1), (160, 4096, 2), (5, 18944, 3)])
+def test_quantize_bit_exact(dq, M, K, seed):
+    x = synth.activations(np.random.default_rng(seed), M, K)
+    x[0, :256] = 0.0  # a zero block
+    if M > 1:
+        x[1, 256 % K:256 % K + 3] = [254.0, 3.0, -5.0]  # halfway ties
+    q, d, b = dq.quantize_act(_t(x))
+    _sync()
+    xq, xd, xb = oracle.quantize_act(x)
+    assert np.array_equal(q.cpu().numpy(), xq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), xd.view(np.uint32))
+    assert np.array_equal(b.cpu().numpy(), xb)
+
+
+def test_quantize_strided_and_unaligned_rows(dq):
+    rng = np.random.default_rng(5)
+    big = synth.activations(rng, 9, 1024 + 65)
+    xq, xd, xb = oracle.quantize_act(np.ascontiguousarray(big[:, 1:1025]))
+    xt = _t(big)
+    q, d, b = dq.quantize_act(xt[:, 1:1025])  # row stride 1089, start off 16-byte alignment
+    _sync()
+    assert np.array_equal(q.cpu().numpy(), xq) and np.array_equal(b.cpu().numpy(), xb)
+    assert np.array_equal(d.cpu().numpy(), xd)
+
+
+# --------------------------------------------------------------------------- #
+# Repack: every bit lands where the layout says                              #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("type_", [oracle.Q4_K, oracle.Q6_K])
+def test_repack_layout(dq, type_):
+    N, K = 70, 768  # three tiles, the last one ragged
+    nb = K // 256
+    W = _weights(type_, N, K, 40, full_scales=True)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1))).cpu().numpy()
+    assert packed.size == dq.packed_size(type_, N, K)
+    tb = 4608 if type_ == oracle.Q4_K else 6720
+    tiles = packed.reshape(-1, nb, tb)
+    for nt in range(tiles.shape[0]):
+        for b in range(nb):
+            got = read_tile(type_, tiles[nt, b])
+            for r in range(32):
+                n = 32 * nt + r
+                if type_ == oracle.Q4_K:
+                    heads, q = got
+                    if n >= N:
+                        assert not heads[r].any() and not q[r].any()
+                        continue
+                    _, _, _, _, oq = oracle.decode_q4k(W[n, b])
+                    assert np.array_equal(heads[r], W[n, b, :16])
+                    assert np.array_equal(q[r], oq)
+                else:
+                    d_bits, sc, q = got
+                    if n >= N:
+                        assert d_bits[r] == 0 and not sc[r].any() and not q[r].any()
+                        continue
+                    _, osc, oq = oracle.decode_q6k(W[n, b])
+                    assert int(d_bits[r]) == int(W[n, b, 208]) | (int(W[n, b, 209]) << 8)
+                    assert np.array_equal(sc[r], osc) and np.array_equal(q[r], oq)
+
+
+# --------------------------------------------------------------------------- #
+# Integer part of the GEMM: bit-exact                                         #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("type_,M,N,K", [(oracle.Q4_K, 37, 70, 768), (oracle.Q6_K, 37, 70, 768),
+                                         (oracle.Q4_K, 64, 32, 256), (oracle.Q6_K, 1, 33, 512)])
+def test_superblock_sums_bit_exact(dq, type_, M, N, K):
+    W = _weights(type_, N, K, 50 + M, full_scales=True)
+    x = synth.activations(np.random.default_rng(60 + M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    S, Mn = dq.debug_superblock_sums(type_, _t(xq), _t(xb), packed, N)
+    _sync()
+    oS, oMn = oracle.superblock_sums(type_, xq, xb, W, N)
+    assert np.array_equal(S.cpu().numpy(), oS)
+    assert np.array_equal(Mn.cpu().numpy(), oMn)
+
+
+@pytest.mark.parametrize("type_", [oracle.Q4_K, oracle.Q6_K])
+def test_subblock_dots_bit_exact(dq, type_):
+    # all scales 0 except sub-block j's, set to 1: S of super-block b is dot_j
+    M, N, nb = 33, 40, 2
+    K = 256 * nb
+    rng = np.random.default_rng(70)
+    x = synth.activations(rng, M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    J = 8 if type_ == oracle.Q4_K else 16
+    f = random_q4k_fields(rng, N, nb) if type_ == oracle.Q4_K else random_q6k_fields(rng, N, nb)
+    W0 = encode_q4k_matrix(f) if type_ == oracle.Q4_K else encode_q6k_matrix(f)
+    dots = oracle.subdots(type_, xq, W0, N)  # [M, N, nb, J]
+    for j in range(J):
+        fj = dict(f)
+        fj["sc"] = np.zeros_like(f["sc"])
+        fj["sc"][..., j] = 1
+        Wj = encode_q4k_matrix(fj) if type_ == oracle.Q4_K else encode_q6k_matrix(fj)
+        packed = dq.repack_weights(type_, N, K, _t(Wj.reshape(-1)))
+        S, _ = dq.debug_superblock_sums(type_, _t(xq), _t(xb), packed, N)
+        _sync()
+        assert np.array_equal(S.cpu().numpy(), dots[..., j]), f"sub-block {j}"
+
+
+# --------------------------------------------------------------------------- #
+# GEMM outputs within tolerance, tails and degenerate shapes                  #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("type_", [oracle.Q4_K, oracle.Q6_K])
+@pytest.mark.parametrize("M,N,K", [(1, 32, 256), (8, 100, 1024), (17, 33, 512), (160, 96, 768),
+                                   (511, 40, 512), (16, 256, 512)])
+def test_qgemm_within_tolerance(dq, type_, M, N, K):
+    W = _weights(type_, N, K, 80 + M + N)
+    x = synth.activations(np.random.default_rng(90 + M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(type_, _t(xq), _t(xd), _t(xb), packed, N)
+    _sync()
+    yr, T = oracle.qgemm_ref(type_, xq, xd, W, N)
+    _check_tol(y.cpu().numpy(), yr, T, f"type {type_} {M}x{N}x{K}")
+
+
+def test_qgemm_strided_output_untouched_padding(dq):
+    M, N, K = 40, 70, 512
+    W = _weights(oracle.Q4_K, N, K, 3)
+    xq, xd, xb = oracle.quantize_act(synth.activations(np.random.default_rng(4), M, K))
+    packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
+    ybig = torch.full((M, N + 9), -7.0, device=DEV)
+    dq.qgemm(oracle.Q4_K, _t(xq), _t(xd), _t(xb), packed, N, y=ybig)
+    _sync()
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, N:] == -7.0)
+    yr, T = oracle.qgemm_ref(oracle.Q4_K, xq, xd, W, N)
+    _check_tol(yb[:, :N], yr, T, "strided y")
+
+
+def test_qgemm_deterministic_and_power_of_two_scaling(dq):
+    M, N, K = 160, 64, 1024
+    W = _weights(oracle.Q6_K, N, K, 5)
+    x = synth.activations(np.random.default_rng(6), M, K)
+    packed = dq.repack_weights(oracle.Q6_K, N, K, _t(W.reshape(-1)))
+    q, d, b = dq.quantize_act(_t(x))
+    y1 = dq.qgemm(oracle.Q6_K, q, d, b, packed, N).cpu().numpy()
+    y2 = dq.qgemm(oracle.Q6_K, q, d, b, packed, N).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    q3, d3, b3 = dq.quantize_act(_t(x * np.float32(2.0 ** -5)))
+    y3 = dq.qgemm(oracle.Q6_K, q3, d3, b3, packed, N).cpu().numpy()
+    assert np.array_equal(y3, y1 * np.float32(2.0 ** -5))
+
+
+def test_zero_activations_give_zero(dq):
+    M, N, K = 20, 64, 512
+    W = _weights(oracle.Q4_K, N, K, 8)
+    packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
+    q, d, b = dq.quantize_act(torch.zeros((M, K), device=DEV))
+    y = dq.qgemm(oracle.Q4_K, q, d, b, packed, N).cpu().numpy()
+    assert np.all(y == 0.0)
+
+
+# --------------------------------------------------------------------------- #
+# Gathered-row projection                                                     #
+# --------------------------------------------------------------------------- #
+def test_rows_gather_matches_quantized_gemm(dq):
+    L, K, N = 160, 1024, 200
+    W = _weights(oracle.Q6_K, N, K, 9)
+    canvas = synth.activations(np.random.default_rng(10), L, K)
+    packed = dq.repack_weights(oracle.Q6_K, N, K, _t(W.reshape(-1)))
+    idx = np.array([159, 0, 7, 7, 42, 3], np.int32)  # unsorted, with a duplicate
+    y, ws = dq.qgemm_rows(oracle.Q6_K, _t(canvas), _t(idx), packed, N)
+    _sync()
+    gq, gd, gb = oracle.qgemm_rows_inputs(canvas, idx)
+    yr, T = oracle.qgemm_ref(oracle.Q6_K, gq, gd, W, N)
+    yn = y.cpu().numpy()
+    _check_tol(yn, yr, T, "rows")
+    assert np.array_equal(yn[2], yn[3])  # duplicate index, identical row
+    assert not ws[: 4 * len(idx)].view(torch.int32).cpu().numpy().any()
+    # gather-then-quantize equals quantize-then-gather, bit for bit
+    q, d, b = dq.quantize_act(_t(canvas))
+    yall = dq.qgemm(oracle.Q6_K, q, d, b, packed, N).cpu().numpy()
+    assert np.array_equal(yn.view(np.uint32), yall[idx].view(np.uint32))
+    # permuting idx permutes the rows
+    perm = np.array([3, 5, 0, 1, 2, 4])
+    yp, _ = dq.qgemm_rows(oracle.Q6_K, _t(canvas), _t(idx[perm]), packed, N)
+    assert np.array_equal(yp.cpu().numpy(), yn[perm])
+
+
+def test_rows_out_of_range_index_is_flagged_not_read(dq):
+    L, K, N = 10, 512, 64
+    W = _weights(oracle.Q4_K, N, K, 11)
+    canvas = synth.activations(np.random.default_rng(12), L, K)
+    packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
+    idx = np.array([2, 10, -1, 9], np.int32)
+    y, ws = dq.qgemm_rows(oracle.Q4_K, _t(canvas), _t(idx), packed, N)
+    _sync()
+    flags = ws[:16].view(torch.int32).cpu().numpy()
+    assert list(flags) == [0, 1, 1, 0]
+    yn = y.cpu().numpy()
+    assert np.all(yn[1] == 0) and np.all(yn[2] == 0)
+    gq, gd, _ = oracle.qgemm_rows_inputs(canvas, idx[[0, 3]])
+    yr, T = oracle.qgemm_ref(oracle.Q4_K, gq, gd, W, N)
+    _check_tol(yn[[0, 3]], yr, T, "valid rows")
+
+
+# --------------------------------------------------------------------------- #
+# ABI errors through the binding on the GPU                                   #
+# --------------------------------------------------------------------------- #
+def test_abi_errors_on_gpu(dq):
+    q = torch.zeros((4, 512), dtype=torch.int8, device=DEV)
+    d = torch.zeros((4, 2), dtype=torch.float32, device=DEV)
+    b = torch.zeros((4, 16), dtype=torch.int32, device=DEV)
+    packed = torch.zeros(dq.packed_size(dq.Q4_K, 32, 512), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        dq.qgemm(dq.Q4_K, q, d, b, packed[:-1], 32)  # packed too small
+    with pytest.raises(dq.DQError) as e:
+        dq.qgemm(dq.Q4_K, q, d, None, packed, 32)
+    assert e.value.status == dq.DQ_EINVAL
+    canvas = torch.zeros((8, 512), device=DEV)
+    idx = torch.zeros(4, dtype=torch.int32, device=DEV)
+    with pytest.raises(dq.DQError) as e:
+        dq.qgemm_rows(dq.Q4_K, canvas, idx, packed, 32,
+                      ws=torch.zeros(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == dq.DQ_EWORKSPACE
