@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Throughput of the K-quant x int8 GEMM hot path on one MI355X.
+
+One timed step is one LLaDA-8B denoising step's GEMM work at canvas L = 160
+(heatdrop.ai card, "What it does": each step reruns the whole model over the
+canvas, so the runtime is a stream of GEMMs; Architecture page, "A forward
+pass"): for each of 32 layers, 4 activation quantizations (Q/K/V share one,
+O, gate/up share one, down) and the 7 projections Q, K, V, O (4096 x 4096
+Q4_K), gate, up (12288 x 4096 Q4_K) and down (4096 x 12288; Q6_K on odd
+layers, Q4_K on even), then the output projection on 32 gathered canvas rows
+(126,464 x 4096 Q6_K).  Every layer has its own seeded weights (4.6 GB in
+all, far above the 256 MB last-level cache), resident in HBM before timing.
+
+Prints one JSON line: whole-step TOPS (value), HBM GB/s, the roofline of the
+dominant kernel measured with HIP events around its launches inside the timed
+region, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "K-quant×int8 GEMM TOPS + HBM GB/s (% roofline) at LLaDA-8B step shapes"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
+L, K, F, V, LAYERS, ROWS = 160, 4096, 12288, 126464, 32, 32
+Q4_K, Q6_K = 12, 14
+BLOCK = {Q4_K: 144, Q6_K: 210}
+KERNEL_SOURCES = ["quantized_gemm_diffusion_amd/csrc/qgemm.hip",
+                  "quantized_gemm_diffusion_amd/csrc/dq_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-layers", type=int, default=6,
+                   help="layers of the step the CPU oracle baseline runs on")
+    p.add_argument("--cpu-threads", type=int, default=min(os.cpu_count() or 1, 16))
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle timing (for profiler runs)")
+    return p.parse_args()
+
+
+def gemm_bytes(type_, M, N, K_):
+    w = N * (K_ // 256) * BLOCK[type_]
+    act = M * K_ + M * (K_ // 256) * 4 + (M * (K_ // 32) * 4 if type_ == Q4_K else 0)
+    return w + act + M * N * 4
+
+
+def quant_bytes(M, K_):
+    return M * K_ * 4 + M * K_ + M * (K_ // 256) * 4 + M * (K_ // 32) * 4
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log("bench.py measures one GPU: this build runs the hot path on a single MI355X; "
+            "multi-GPU sharding is a design note only, so --gpus must be 1.")
+        sys.exit(2)
+
+    import torch
+    import quantized_gemm_diffusion_amd as dq
+
+    lib = dq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.perf_counter()
+    act_rng = np.random.default_rng(synth.seed(2, 0, 9))
+    acts = {"qkv": up(synth.activations(act_rng, L, K)), "o": up(synth.activations(act_rng, L, K)),
+            "ffn": up(synth.activations(act_rng, L, K)),
+            "down": up(synth.activations(act_rng, L, F))}
+    qb = {kk: (torch.empty((L, kk), dtype=torch.int8, device=dev),
+               torch.empty((L, kk // 256), dtype=torch.float32, device=dev),
+               torch.empty((L, kk // 32), dtype=torch.int32, device=dev)) for kk in (K, F)}
+    outs = {name: torch.empty((L, N), dtype=torch.float32, device=dev)
+            for name, _, N, _ in synth.llada_layer(1)}
+    host_keep = {}
+    packed = []
+    for layer in range(LAYERS):
+        lp = {}
+        for p, (name, t, N, KK) in enumerate(synth.llada_layer(layer)):
+            W = synth.weights(np.random.default_rng(synth.seed(2, layer, p)), t, N, KK)
+            if layer < args.cpu_layers:
+                host_keep[(layer, name)] = W
+            g = up(W.reshape(-1))
+            lp[name] = (t, N, KK, dq.repack_weights(t, N, KK, g))
+            del g
+        packed.append(lp)
+    Wout = synth.q6k_weights(np.random.default_rng(synth.seed(3, 0, 0)), V, K)
+    out_packed = dq.repack_weights(Q6_K, V, K, up(Wout.reshape(-1)))
+    canvas_np = synth.activations(np.random.default_rng(synth.seed(3, 0, 1)), L, K)
+    idx_np = synth.row_index(np.random.default_rng(synth.seed(3, 0, 2)), L, ROWS)
+    canvas, idx = up(canvas_np), up(idx_np)
+    logits = torch.empty((ROWS, V), dtype=torch.float32, device=dev)
+    ws = torch.empty(dq.qgemm_rows_workspace(ROWS, K), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM after {time.perf_counter() - t0:.1f} s")
+
+    # ------------------------------------------------------- the step's calls
+    calls = []  # (C function, args, kind, ops, algorithmic bytes)
+
+    def quant(name):
+        x = acts[name]
+        kk = x.shape[1]
+        q, d, b = qb[kk]
+        calls.append((lib.dq_quantize_act,
+                      (L, kk, x.data_ptr(), kk, q.data_ptr(), d.data_ptr(), b.data_ptr(), sp),
+                      "quantize", 0, quant_bytes(L, kk)))
+        return q, d, b
+
+    def gemm(lp, name, qdb):
+        t, N, kk, pk = lp[name]
+        q, d, b = qdb
+        y = outs[name]
+        calls.append((lib.dq_qgemm, (t, L, N, kk, q.data_ptr(), d.data_ptr(), b.data_ptr(),
+                                     pk.data_ptr(), y.data_ptr(), N, sp),
+                      f"qgemm_{'q4k' if t == Q4_K else 'q6k'}", 2 * L * N * kk,
+                      gemm_bytes(t, L, N, kk)))
+
+    for lp in packed:
+        a = quant("qkv")
+        for n in ("q", "k", "v"):
+            gemm(lp, n, a)
+        gemm(lp, "o", quant("o"))
+        a = quant("ffn")
+        for n in ("gate", "up"):
+            gemm(lp, n, a)
+        gemm(lp, "down", quant("down"))
+    # gathered f32 rows and the index list stand in for pre-quantized activations
+    rows_bytes = V * (K // 256) * BLOCK[Q6_K] + ROWS * K * 4 + ROWS * 4 + ROWS * V * 4
+    calls.append((lib.dq_qgemm_rows,
+                  (Q6_K, L, ROWS, V, K, canvas.data_ptr(), K, idx.data_ptr(),
+                   out_packed.data_ptr(), logits.data_ptr(), V, ws.data_ptr(), ws.numel(), sp),
+                  "rows", 2 * ROWS * V * K, rows_bytes))
+    step_ops = sum(c[3] for c in calls)
+    step_bytes = sum(c[4] for c in calls)
+
+    def run_calls(brackets=None, kind=None):
+        """Launch one step; optionally record events around each launch of `kind`."""
+        for fn, a, k, _, _ in calls:
+            if brackets is not None and k == kind:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = fn(*a)
+                e1.record(stream)
+                brackets.append((e0, e1))
+            else:
+                rc = fn(*a)
+            if rc:
+                raise RuntimeError(f"{fn.__name__}: {lib.dq_last_error().decode()}")
+
+    # ------------------------------------------------------ warmup, calibrate
+    for _ in range(args.warmup):
+        run_calls()
+    torch.cuda.synchronize()
+    per_kind = {}
+    evs = []
+    for fn, a, k, ops, nbytes in calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        evs.append((k, e0, e1, ops, nbytes))
+    torch.cuda.synchronize()
+    for k, e0, e1, ops, nbytes in evs:
+        d = per_kind.setdefault(k, [0, 0.0, 0, 0])
+        d[0] += 1
+        d[1] += e0.elapsed_time(e1)
+        d[2] += ops
+        d[3] += nbytes
+    dominant = max((k for k in per_kind if k.startswith("qgemm")), key=lambda k: per_kind[k][1])
+    kernels = {k: {"calls_per_step": v[0], "avg_us": round(1e3 * v[1] / v[0], 3),
+                   "TOPS": round(v[2] / (v[1] * 1e-3) / 1e12, 2) if v[2] else None,
+                   "GB_s": round(v[3] / (v[1] * 1e-3) / 1e9, 1)}
+               for k, v in per_kind.items()}
+    log("per-kind (isolated launches):", json.dumps(kernels))
+
+    # ------------------------------------------------------------- timed run
+    brackets = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        run_calls(brackets, dominant)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = 1e3 * elapsed / args.steps
+    dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in brackets)
+    dom_launches = per_kind[dominant][0] * args.steps
+    dom_bytes = per_kind[dominant][3] / per_kind[dominant][0]  # per launch (average)
+    dom_ops = per_kind[dominant][2] / per_kind[dominant][0]
+    dom_avg_s = dom_ms * 1e-3 / dom_launches
+    bound = "hbm" if dom_ops / dom_bytes < (INT8_PEAK_TOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = dom_bytes / dom_avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = dom_ops / dom_avg_s / 1e12, INT8_PEAK_TOPS, "TOPS"
+    traffic = stored_traffic(dominant)
+
+    step_s = ms_per_step * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": round(step_ops / step_s / 1e12, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "LLaDA-8B denoising step at canvas L=160: 32 layers x (4 int8 "
+                               "activation quantizations + Q/K/V/O 4096x4096, gate/up "
+                               "12288x4096, down 4096x12288 K-quant GEMMs; down Q6_K on odd "
+                               "layers, Q4_K on even) + output projection on 32 of 160 "
+                               "gathered rows, 126464x4096 Q6_K",
+                   "L": L, "K": K, "ffn": F, "vocab": V, "layers": LAYERS, "rows": ROWS,
+                   "step_GOP": round(step_ops / 1e9, 2),
+                   "step_algorithmic_MB": round(step_bytes / 1e6, 1)},
+        "hbm_GBs": round(step_bytes / step_s / 1e9, 1),
+        "hbm_frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(step_ops / step_s / 1e12 / INT8_PEAK_TOPS, 4),
+        "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "avg_launch_us": round(dom_avg_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": int(dom_bytes),
+                     "ops_per_launch": int(dom_ops), "launches": dom_launches},
+        "kernels_isolated": kernels,
+        "device": torch.cuda.get_device_properties(dev).name,
+    }
+
+    # ------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
+    """The oracle, as it stands, on the first layers of the step plus 1/4 of the vocab rows."""
+    import oracle
+
+    th = args.cpu_threads
+    xs = {k: v.cpu().numpy() for k, v in acts.items()}
+    ops = 0
+    t0 = time.perf_counter()
+    for layer in range(args.cpu_layers):
+        quantized = {}
+        for p, (name, t, N, KK) in enumerate(synth.llada_layer(layer)):
+            src = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "ffn", "up": "ffn",
+                   "down": "down"}[name]
+            if src not in quantized:
+                quantized[src] = oracle.quantize_act(xs[src])
+            q, d, b = quantized[src]
+            oracle.qgemm_f32(t, q, d, b, host_keep[(layer, name)], N, threads=th)
+            ops += 2 * L * N * KK
+    nv = V // 4
+    gq, gd, gb = oracle.qgemm_rows_inputs(canvas_np, idx_np)
+    oracle.qgemm_f32(Q6_K, gq, gd, gb, Wout.reshape(V, -1)[:nv], nv, threads=th)
+    ops += 2 * ROWS * nv * K
+    dt = time.perf_counter() - t0
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": th, "kind": "oracle",
+            "sample": f"oracle quantize + integer-decomposition GEMM on {args.cpu_layers} of 32 "
+                      f"layers (all 7 projections, L=160) and 1/4 of the 126464 vocab rows at "
+                      f"M=32: {ops / 1e9:.1f} GOP in {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,9 @@ FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-ffp-contract=off", "-Wall", "-Wno-unused-command-line-argument",
+    # MFMA results in VGPRs: the fold reads every accumulator element once per super-block
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-Wall", "-Wno-unused-command-line-argument",
 ]
 
 

@@ -130,7 +130,7 @@ int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q, const f
   if (ldy < N) return fail(DQ_EINVAL, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
   if (M == 0 || N == 0) return ok();
   if (!y || !aligned(y, 4)) return fail(DQ_EINVAL, "y is NULL or not 4-byte aligned");
-  return launched(dq::launch_qgemm(type, M, N, K, q, d, bsum,
+  return launched(dq::launch_qgemm(type, 0, M, N, K, q, d, bsum,
                                    static_cast<const uint8_t *>(packed), y, ldy, nullptr,
                                    nullptr, stream),
                   "dq_qgemm");
@@ -189,7 +189,7 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
   int32_t *bs = reinterpret_cast<int32_t *>(w + off_b);
   hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, q, d, bs, flags, stream);
   if (e != hipSuccess) return launched(e, "dq_qgemm_rows (gather-quantize)");
-  return launched(dq::launch_qgemm(type, M, N, K, q, d, bs, static_cast<const uint8_t *>(packed),
+  return launched(dq::launch_qgemm(type, 1, M, N, K, q, d, bs, static_cast<const uint8_t *>(packed),
                                    y, ldy, nullptr, nullptr, stream),
                   "dq_qgemm_rows (gemm)");
 }
@@ -201,7 +201,7 @@ int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const in
   if (M == 0 || N == 0) return ok();
   if (!S || !Mn || !aligned(S, 4) || !aligned(Mn, 4))
     return fail(DQ_EINVAL, "S and Mn must be non-NULL and 4-byte aligned");
-  return launched(dq::launch_qgemm(type, M, N, K, q, nullptr, bsum,
+  return launched(dq::launch_qgemm(type, 2, M, N, K, q, nullptr, bsum,
                                    static_cast<const uint8_t *>(packed), nullptr, N, S, Mn,
                                    stream),
                   "dq_debug_superblock_sums");

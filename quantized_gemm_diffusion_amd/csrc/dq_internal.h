@@ -6,9 +6,11 @@
 // whole reduction are contiguous:  tile(nt, b) at ((nt * nb) + b) * TILE_BYTES.
 //
 // Inside a tile every plane is laid out for the 32x32x32 int8 MFMA: lane l of
-// a wave owns weight row n = l % 32 of the tile and the k-half g = l / 32 of
-// each 32-wide k chunk c (c = 0..7), i.e. codes at k = 32c + 16g + p,
-// p = 0..15.  A 16-byte per-lane record holds the 4-bit parts of two chunks:
+// a wave owns weight row n = l % 32 of the tile and, for each of the 8 MFMA
+// k-chunks c, the 16 codes at k = 128g + 16c + p (g = l / 32, p = 0..15).  So
+// lane half g covers k in [128g, 128g + 128): the matching activation bytes
+// of one row are a single 128-byte line.  A 16-byte per-lane record holds the
+// 4-bit parts of two chunks:
 // dword t (t = 0..3) covers chunk 2i + t/2 (record i), half h = t % 2, and its
 // byte e (e = 0..3) carries code p = 8h + e in the low nibble and code
 // p = 8h + 4 + e in the high nibble.  Records are [i][lane][16 B].
@@ -21,7 +23,7 @@
 //     [4096, 6144) high 2 bits: 2 records x 64 lanes x 16 B; dword t of record
 //                  i covers chunk 4i + t; its byte e holds the 2-bit parts of
 //                  codes p = e, 4+e, 8+e, 12+e at bits 0, 2, 4, 6
-//     [6144, 6656) scales: [g][n][8 B], byte c = scale of sub-block 2c + g
+//     [6144, 6656) scales: [g][n][8 B], byte c = scale of sub-block 8g + c
 //     [6656, 6720) d: [n] fp16
 #pragma once
 
@@ -56,7 +58,8 @@ hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, co
                            hipStream_t stream);
 hipError_t launch_repack(int type, int64_t N, int64_t K, const uint8_t *src, uint8_t *dst,
                          hipStream_t stream);
-hipError_t launch_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
+// mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers.
+hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const int8_t *q,
                         const float *d, const int32_t *bsum, const uint8_t *packed, float *y,
                         int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream);
 

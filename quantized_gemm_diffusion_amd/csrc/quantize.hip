@@ -12,6 +12,9 @@
 // binary32 implementation of the same steps bit for bit.
 #include "dq_internal.h"
 
+// every step below is one binary32 operation; nothing may be fused
+#pragma clang fp contract(off)
+
 namespace dq {
 namespace {
 

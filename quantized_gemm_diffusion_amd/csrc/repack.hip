@@ -43,7 +43,7 @@ __device__ inline void nibble_record(const uint8_t *blk, int g, int i, uint32_t 
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int k_lo = 32 * c + 16 * g + 8 * h + e;
+      const int k_lo = 128 * g + 16 * c + 8 * h + e;
       const uint32_t lo = Q6 ? (q6k_code(blk, k_lo) & 15) : q4k_code(blk, k_lo);
       const uint32_t hi = Q6 ? (q6k_code(blk, k_lo + 4) & 15) : q4k_code(blk, k_lo + 4);
       w |= (lo | (hi << 4)) << (8 * e);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64) void repack_kernel(int64_t N, int nb, const uin
           for (int e = 0; e < 4; ++e)
             for (int s = 0; s < 4; ++s) {
               const int p = 4 * s + e;
-              w |= ((q6k_code(blk, 32 * c + 16 * g + p) >> 4) & 3) << (8 * e + 2 * s);
+              w |= ((q6k_code(blk, 128 * g + 16 * c + p) >> 4) & 3) << (8 * e + 2 * s);
             }
           rec[t] = w;
         }
@@ -105,11 +105,11 @@ __global__ __launch_bounds__(64) void repack_kernel(int64_t N, int nb, const uin
       *reinterpret_cast<i32x4 *>(tile + Q6K_QH_OFF + (i * 64 + lane) * 16) =
           i32x4{(int)rec[0], (int)rec[1], (int)rec[2], (int)rec[3]};
     }
-    // scales: [g][r][8 B], byte c = scale of sub-block 2c + g
+    // scales: [g][r][8 B], byte c = scale of sub-block 8g + c
     uint32_t s0 = 0, s1 = 0;
     if (valid)
       for (int c = 0; c < 8; ++c) {
-        const uint32_t sb = blk[192 + 2 * c + g];
+        const uint32_t sb = blk[192 + 8 * g + c];
         if (c < 4)
           s0 |= sb << (8 * c);
         else

@@ -2,8 +2,8 @@
 
 Written from the layout description in the library's private header: tiles of
 32 weight rows x one super-block, n-tile-major; per-lane 16-byte records for
-the 32x32x32 int8 matrix instruction (lane l: row l % 32, k-half g = l // 32,
-codes at k = 32c + 16g + p).  Used to check that the repack moves every code,
+the 32x32x32 int8 matrix instruction (lane l: row l % 32, half g = l // 32,
+codes of chunk c at k = 128g + 16c + p).  Used to check that the repack moves every code,
 scale and header bit to where the layout says, and nothing else.
 """
 from __future__ import annotations
@@ -24,7 +24,7 @@ def _nibble_records(rec: np.ndarray) -> np.ndarray:
                 c, h = 2 * i + t // 2, t % 2
                 for e in range(4):
                     byte = int(rec[i, lane, 4 * t + e])
-                    k = 32 * c + 16 * g + 8 * h + e
+                    k = 128 * g + 16 * c + 8 * h + e
                     out[r, k] = byte & 15
                     out[r, k + 4] = byte >> 4
     return out
@@ -50,11 +50,11 @@ def read_tile(type_: int, tile: np.ndarray):
                     byte = int(qh[i, lane, 4 * t + e])
                     for s in range(4):
                         p = 4 * s + e
-                        high[r, 32 * c + 16 * g + p] = (byte >> (2 * s)) & 3
+                        high[r, 128 * g + 16 * c + p] = (byte >> (2 * s)) & 3
     scp = tile[6144:6656].reshape(2, 32, 8).view(np.int8)
     sc = np.zeros((32, 16), np.int64)
     for g in range(2):
         for c in range(8):
-            sc[:, 2 * c + g] = scp[g, :, c]
+            sc[:, 8 * g + c] = scp[g, :, c]
     d_bits = tile[6656:6720].view(np.uint16)
     return d_bits, sc, low | (high << 4)

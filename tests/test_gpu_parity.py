@@ -277,3 +277,39 @@ def test_abi_errors_on_gpu(dq):
         dq.qgemm_rows(dq.Q4_K, canvas, idx, packed, 32,
                       ws=torch.zeros(16, dtype=torch.uint8, device=DEV))
     assert e.value.status == dq.DQ_EWORKSPACE
+
+
+# --------------------------------------------------------------------------- #
+# Every m-tiling of the GEMM (the launcher picks 1..5 m-tiles per workgroup   #
+# from M and N): shapes chosen so that each choice is exercised               #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("type_,M,N,K", [
+    (oracle.Q4_K, 160, 8192, 512),    # 5 m-tiles per workgroup
+    (oracle.Q6_K, 128, 8200, 512),    # 4, ragged N
+    (oracle.Q4_K, 96, 8192, 1280),    # 3, 5 super-blocks over 4 waves
+    (oracle.Q6_K, 64, 8192, 256),     # 2, a single super-block
+    (oracle.Q4_K, 150, 8224, 768),    # 5 with a ragged last m-tile
+])
+def test_qgemm_every_m_tiling(dq, type_, M, N, K):
+    W = _weights(type_, N, K, 300 + M, full_scales=True)
+    x = synth.activations(np.random.default_rng(400 + M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(type_, _t(xq), _t(xd), _t(xb), packed, N)
+    _sync()
+    yr, T = oracle.qgemm_ref(type_, xq, xd, W, N)
+    _check_tol(y.cpu().numpy(), yr, T, f"type {type_} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("type_,M", [(oracle.Q4_K, 160), (oracle.Q6_K, 128), (oracle.Q4_K, 64)])
+def test_superblock_sums_bit_exact_multi_tile(dq, type_, M):
+    N, K = 8192, 512
+    W = _weights(type_, N, K, 500 + M, full_scales=True)
+    x = synth.activations(np.random.default_rng(600 + M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    S, Mn = dq.debug_superblock_sums(type_, _t(xq), _t(xb), packed, N)
+    _sync()
+    oS, oMn = oracle.superblock_sums(type_, xq, xb, W, N)
+    assert np.array_equal(S.cpu().numpy(), oS)
+    assert np.array_equal(Mn.cpu().numpy(), oMn)
