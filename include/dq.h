@@ -60,9 +60,9 @@ const char *dq_last_error(void);
  * dq_packed_size -- bytes of the repacked matrix (host-only, no GPU work).
  *
  * The repacked layout holds the same bits as the GGUF blocks (4.5 bits per
- * Q4_K weight, 6.5625 bits per Q6_K weight), permuted into tiles of 32 weight
- * rows x one super-block; N is rounded up to a multiple of 32 with zero rows.
- * bytes = ceil(N/32) * 32 * (K/256) * block_bytes.
+ * Q4_K weight, 6.5625 bits per Q6_K weight), permuted into tiles of 16 weight
+ * rows x one super-block; N is rounded up to a multiple of 16 with zero rows.
+ * bytes = ceil(N/16) * 16 * (K/256) * block_bytes.
  * Errors: DQ_EUNSUPPORTED (type), DQ_EINVAL (K, N < 0, bytes NULL).
  * ------------------------------------------------------------------------ */
 int dq_packed_size(int type, int64_t N, int64_t K, size_t *bytes);

@@ -1,30 +1,30 @@
 // dq_internal.h -- private to libdq: tile layout, vector types and launchers.
 //
 // Packed weight layout (written by dq_repack_weights, read by the GEMMs).
-// Weights are cut into tiles of 32 weight rows (n) x one 256-wide super-block
+// Weights are cut into tiles of 16 weight rows (n) x one 256-wide super-block
 // (b); tiles are stored n-tile-major, so the tiles one n-tile needs over the
 // whole reduction are contiguous:  tile(nt, b) at ((nt * nb) + b) * TILE_BYTES.
 //
-// Inside a tile every plane is laid out for the 32x32x32 int8 MFMA: lane l of
-// a wave owns weight row n = l % 32 of the tile and, for each of the 8 MFMA
-// k-chunks c, the 16 codes at k = 128g + 16c + p (g = l / 32, p = 0..15).  So
-// lane half g covers k in [128g, 128g + 128): the matching activation bytes
-// of one row are a single 128-byte line.  A 16-byte per-lane record holds the
-// 4-bit parts of two chunks:
-// dword t (t = 0..3) covers chunk 2i + t/2 (record i), half h = t % 2, and its
-// byte e (e = 0..3) carries code p = 8h + e in the low nibble and code
-// p = 8h + 4 + e in the high nibble.  Records are [i][lane][16 B].
+// Inside a tile every plane is laid out for the 16x16x64 int8 MFMA: lane l of
+// a wave owns weight row n = l % 16 of the tile and the k-quarter kq = l / 16,
+// i.e. for each of the 4 MFMA k-chunks c the 16 codes at k = 64kq + 16c + p
+// (p = 0..15): lane quarter kq covers k in [64kq, 64kq + 64), so the matching
+// activation bytes of one row are a single 64-byte run.  A 16-byte per-lane
+// record holds the 4-bit parts of two chunks: dword t (t = 0..3) covers chunk
+// 2i + t/2 (record i), half h = t % 2, and its byte e (e = 0..3) carries code
+// p = 8h + e in the low nibble and code p = 8h + 4 + e in the high nibble.
+// Records are [i][lane][16 B].
 //
-//   Q4_K tile (4608 B = 32 x 144):
-//     [0, 512)     heads: per row n, the 16 GGUF header bytes d, dmin, scales[12]
-//     [512, 4608)  codes: 4 records x 64 lanes x 16 B (the layout above)
-//   Q6_K tile (6720 B = 32 x 210):
-//     [0, 4096)    low 4 bits of the codes: 4 records x 64 lanes x 16 B
-//     [4096, 6144) high 2 bits: 2 records x 64 lanes x 16 B; dword t of record
-//                  i covers chunk 4i + t; its byte e holds the 2-bit parts of
-//                  codes p = e, 4+e, 8+e, 12+e at bits 0, 2, 4, 6
-//     [6144, 6656) scales: [g][n][8 B], byte c = scale of sub-block 8g + c
-//     [6656, 6720) d: [n] fp16
+//   Q4_K tile (2304 B = 16 x 144):
+//     [0, 256)     heads: per row n, the 16 GGUF header bytes d, dmin, scales[12]
+//     [256, 2304)  codes: 2 records x 64 lanes x 16 B (the layout above)
+//   Q6_K tile (3360 B = 16 x 210):
+//     [0, 2048)    low 4 bits of the codes: 2 records x 64 lanes x 16 B
+//     [2048, 3072) high 2 bits: 1 record x 64 lanes x 16 B; dword t covers
+//                  chunk t; its byte e holds the 2-bit parts of codes
+//                  p = e, 4+e, 8+e, 12+e at bits 0, 2, 4, 6
+//     [3072, 3328) scales: [kq][n] dword, byte c = scale of sub-block 4kq + c
+//     [3328, 3360) d: [n] fp16
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,21 +33,22 @@
 namespace dq {
 
 constexpr int QK = 256;
-constexpr int TILE_N = 32;
+constexpr int TILE_N = 16;
 constexpr int Q4K_BLOCK = 144;
 constexpr int Q6K_BLOCK = 210;
-constexpr int Q4K_TILE = TILE_N * Q4K_BLOCK;  // 4608
-constexpr int Q6K_TILE = TILE_N * Q6K_BLOCK;  // 6720
-constexpr int Q4K_CODES_OFF = 512;
-constexpr int Q6K_QH_OFF = 4096;
-constexpr int Q6K_SC_OFF = 6144;
-constexpr int Q6K_D_OFF = 6656;
+constexpr int Q4K_TILE = TILE_N * Q4K_BLOCK;  // 2304
+constexpr int Q6K_TILE = TILE_N * Q6K_BLOCK;  // 3360
+constexpr int Q4K_CODES_OFF = 256;
+constexpr int Q6K_QH_OFF = 2048;
+constexpr int Q6K_SC_OFF = 3072;
+constexpr int Q6K_D_OFF = 3328;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));

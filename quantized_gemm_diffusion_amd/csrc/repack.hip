@@ -34,16 +34,16 @@ __device__ inline uint32_t q6k_code(const uint8_t *blk, int i) {
   return low4 | (high2 << 4);
 }
 
-// 16-byte record i of lane (g) for one row: two chunks, 4-bit parts.
+// 16-byte record i of lane quarter kq for one row: two chunks, 4-bit parts.
 template <bool Q6>
-__device__ inline void nibble_record(const uint8_t *blk, int g, int i, uint32_t out[4]) {
+__device__ inline void nibble_record(const uint8_t *blk, int kq, int i, uint32_t out[4]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int c = 2 * i + (t >> 1), h = t & 1;
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int k_lo = 128 * g + 16 * c + 8 * h + e;
+      const int k_lo = 64 * kq + 16 * c + 8 * h + e;
       const uint32_t lo = Q6 ? (q6k_code(blk, k_lo) & 15) : q4k_code(blk, k_lo);
       const uint32_t hi = Q6 ? (q6k_code(blk, k_lo + 4) & 15) : q4k_code(blk, k_lo + 4);
       w |= (lo | (hi << 4)) << (8 * e);
@@ -61,64 +61,55 @@ __global__ __launch_bounds__(64) void repack_kernel(int64_t N, int nb, const uin
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
   const int64_t nt = blockIdx.y;
-  const int r = lane & 31, g = lane >> 5;
+  const int r = lane & 15, kq = lane >> 4;
   const int64_t n = nt * TILE_N + r;
   const bool valid = n < N;
   const uint8_t *blk = src + (valid ? (n * nb + b) * BB : 0);
   uint8_t *tile = dst + (nt * nb + b) * TB;
 
   if (!Q6) {
-    if (g == 0) {
+    if (kq == 0) {
       uint32_t head[4] = {0, 0, 0, 0};
       if (valid)
         for (int t = 0; t < 16; ++t) head[t >> 2] |= (uint32_t)blk[t] << (8 * (t & 3));
       *reinterpret_cast<i32x4 *>(tile + 16 * r) =
           i32x4{(int)head[0], (int)head[1], (int)head[2], (int)head[3]};
     }
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       uint32_t rec[4] = {0, 0, 0, 0};
-      if (valid) nibble_record<false>(blk, g, i, rec);
+      if (valid) nibble_record<false>(blk, kq, i, rec);
       *reinterpret_cast<i32x4 *>(tile + Q4K_CODES_OFF + (i * 64 + lane) * 16) =
           i32x4{(int)rec[0], (int)rec[1], (int)rec[2], (int)rec[3]};
     }
   } else {
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       uint32_t rec[4] = {0, 0, 0, 0};
-      if (valid) nibble_record<true>(blk, g, i, rec);
+      if (valid) nibble_record<true>(blk, kq, i, rec);
       *reinterpret_cast<i32x4 *>(tile + (i * 64 + lane) * 16) =
           i32x4{(int)rec[0], (int)rec[1], (int)rec[2], (int)rec[3]};
     }
-    for (int i = 0; i < 2; ++i) {
+    {
       uint32_t rec[4] = {0, 0, 0, 0};
       if (valid) {
-        for (int t = 0; t < 4; ++t) {
-          const int c = 4 * i + t;
+        for (int c = 0; c < 4; ++c) {
           uint32_t w = 0;
           for (int e = 0; e < 4; ++e)
             for (int s = 0; s < 4; ++s) {
               const int p = 4 * s + e;
-              w |= ((q6k_code(blk, 128 * g + 16 * c + p) >> 4) & 3) << (8 * e + 2 * s);
+              w |= ((q6k_code(blk, 64 * kq + 16 * c + p) >> 4) & 3) << (8 * e + 2 * s);
             }
-          rec[t] = w;
+          rec[c] = w;
         }
       }
-      *reinterpret_cast<i32x4 *>(tile + Q6K_QH_OFF + (i * 64 + lane) * 16) =
+      *reinterpret_cast<i32x4 *>(tile + Q6K_QH_OFF + lane * 16) =
           i32x4{(int)rec[0], (int)rec[1], (int)rec[2], (int)rec[3]};
     }
-    // scales: [g][r][8 B], byte c = scale of sub-block 8g + c
-    uint32_t s0 = 0, s1 = 0;
+    // scales: [kq][r] dword, byte c = scale of sub-block 4kq + c
+    uint32_t sw = 0;
     if (valid)
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sb = blk[192 + 8 * g + c];
-        if (c < 4)
-          s0 |= sb << (8 * c);
-        else
-          s1 |= sb << (8 * (c - 4));
-      }
-    uint32_t *sp = reinterpret_cast<uint32_t *>(tile + Q6K_SC_OFF + (g * 32 + r) * 8);
-    sp[0] = s0;
-    sp[1] = s1;
-    if (g == 0) {
+      for (int c = 0; c < 4; ++c) sw |= (uint32_t)blk[192 + 4 * kq + c] << (8 * c);
+    *reinterpret_cast<uint32_t *>(tile + Q6K_SC_OFF + (kq * 16 + r) * 4) = sw;
+    if (kq == 0) {
       const uint16_t dv = valid ? (uint16_t)(blk[208] | (blk[209] << 8)) : 0;
       *reinterpret_cast<uint16_t *>(tile + Q6K_D_OFF + 2 * r) = dv;
     }

@@ -43,8 +43,8 @@ def test_status_strings(lib):
 @pytest.mark.parametrize("type_,N,K,exp", [
     (dq.Q4_K, 4096, 4096, 4096 * 16 * 144),
     (dq.Q6_K, 126464, 4096, 126464 * 16 * 210),
-    (dq.Q4_K, 33, 512, 64 * 2 * 144),      # rounded up to 32-row tiles
-    (dq.Q6_K, 1, 256, 32 * 210),
+    (dq.Q4_K, 33, 512, 48 * 2 * 144),      # rounded up to 16-row tiles
+    (dq.Q6_K, 1, 256, 16 * 210),
     (dq.Q4_K, 0, 256, 0),
 ])
 def test_packed_size(lib, type_, N, K, exp):

@@ -13,7 +13,7 @@ import oracle
 import synth
 from kq_fields import (encode_q4k_matrix, encode_q6k_matrix, random_q4k_fields,
                        random_q6k_fields)
-from packed_layout import read_tile
+from packed_layout import ROWS, TILE, read_tile
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -90,18 +90,18 @@ def test_quantize_strided_and_unaligned_rows(dq):
 # --------------------------------------------------------------------------- #
 @pytest.mark.parametrize("type_", [oracle.Q4_K, oracle.Q6_K])
 def test_repack_layout(dq, type_):
-    N, K = 70, 768  # three tiles, the last one ragged
+    N, K = 38, 768  # three tiles, the last one ragged
     nb = K // 256
     W = _weights(type_, N, K, 40, full_scales=True)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1))).cpu().numpy()
     assert packed.size == dq.packed_size(type_, N, K)
-    tb = 4608 if type_ == oracle.Q4_K else 6720
+    tb = TILE[type_]
     tiles = packed.reshape(-1, nb, tb)
     for nt in range(tiles.shape[0]):
         for b in range(nb):
             got = read_tile(type_, tiles[nt, b])
-            for r in range(32):
-                n = 32 * nt + r
+            for r in range(ROWS):
+                n = ROWS * nt + r
                 if type_ == oracle.Q4_K:
                     heads, q = got
                     if n >= N:
