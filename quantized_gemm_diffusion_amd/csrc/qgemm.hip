@@ -61,27 +61,51 @@ __device__ inline void q6k_digits(uint32_t codes, uint32_t sc2, uint32_t off2, u
   hi = __builtin_amdgcn_perm(uo << 1, ue << 1, 0x07030501u);
 }
 
-// All global reads go through buffer resources whose base is advanced with
-// scalar arithmetic, so per-lane offsets stay small 32-bit constants and the
-// hardware range check (num_records) returns zeros past the end of a buffer:
-// activation rows past M read as 0 without any per-lane clamping.
-constexpr int RSRC_FLAGS = 0x00020000;
+// All global reads are buffer loads that write LDS directly.  A buffer
+// descriptor (gfx9 layout: base address, stride 0, size in bytes, flags) is
+// built per load group from scalar values, so per-lane offsets stay small
+// 32-bit constants and the hardware range check (size) returns zeros past
+// the end of a buffer: activation rows past M read as 0 without any per-lane
+// clamping.
+constexpr int DESC_FLAGS = 0x00020000;
 
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
-  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7fffffff ? 0x7fffffffu : (uint32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, RSRC_FLAGS);
-}
-__device__ inline i32x4 ld4(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ inline uint2 ld2(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ inline uint32_t ld1(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+__device__ inline i32x4 desc(const void *base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), bytes < 0 ? 0 : bytes,
+               DESC_FLAGS};
 }
 
-// Raw per-lane weight data of one (n-tile, super-block) tile.
+// Buffer-to-LDS loads: M0 holds the LDS byte address; lane l writes its
+// element at M0 + l * size.  They are written as inline assembly so that the
+// compiler, which cannot tell the LDS slots of the ring apart, does not wait
+// for every one of them before each LDS read; all waits on them are explicit
+// (wait_vm below).  Descriptor and LDS address are wave-uniform.
+__device__ inline void dma16(const i32x4 &d, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(d)
+               : "memory");
+}
+__device__ inline void dma4(const i32x4 &d, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(d)
+               : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order).  The memory clobber keeps every LDS read
+// below the wait.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait for this wave's LDS reads, before a slot they read is refilled.
+__device__ inline void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Raw per-lane weight data of one (n-tile, super-block) tile, read from the
+// tile's copy in LDS (same byte layout as in global memory).
 struct RawQ4 {
   i32x4 head;    // d, dmin, scales[12] of this lane's row
   i32x4 rec[2];  // 4-bit codes, records 0..1
@@ -93,20 +117,19 @@ struct RawQ6 {
   uint32_t d;    // fp16 d of this lane's row in the low half
 };
 
-__device__ inline void load_w(const uint8_t *tile, int lane, int col, int kq, RawQ4 &r) {
-  const auto R = rsrc(tile, Q4K_TILE);
-  r.head = ld4(R, 16 * col);
+__device__ inline void read_w(const uint8_t *tile, int lane, int col, int kq, RawQ4 &r) {
+  r.head = *reinterpret_cast<const i32x4 *>(tile + 16 * col);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) r.rec[i] = ld4(R, Q4K_CODES_OFF + (i * 64 + lane) * 16);
+  for (int i = 0; i < 2; ++i)
+    r.rec[i] = *reinterpret_cast<const i32x4 *>(tile + Q4K_CODES_OFF + (i * 64 + lane) * 16);
 }
 
-__device__ inline void load_w(const uint8_t *tile, int lane, int col, int kq, RawQ6 &r) {
-  const auto R = rsrc(tile, Q6K_TILE);
+__device__ inline void read_w(const uint8_t *tile, int lane, int col, int kq, RawQ6 &r) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) r.rec[i] = ld4(R, (i * 64 + lane) * 16);
-  r.qh = ld4(R, Q6K_QH_OFF + lane * 16);
-  r.sw = ld1(R, Q6K_SC_OFF + (kq * 16 + col) * 4);
-  r.d = ld1(R, Q6K_D_OFF + 4 * (col >> 1)) >> (16 * (col & 1));
+  for (int i = 0; i < 2; ++i) r.rec[i] = *reinterpret_cast<const i32x4 *>(tile + (i * 64 + lane) * 16);
+  r.qh = *reinterpret_cast<const i32x4 *>(tile + Q6K_QH_OFF + lane * 16);
+  r.sw = *reinterpret_cast<const uint32_t *>(tile + Q6K_SC_OFF + (kq * 16 + col) * 4);
+  r.d = *reinterpret_cast<const uint32_t *>(tile + Q6K_D_OFF + 4 * (col >> 1)) >> (16 * (col & 1));
 }
 
 // Per-lane B operands of one super-block: two digit planes, the f16 min
@@ -190,55 +213,106 @@ __device__ inline void make_digits(const RawQ6 &w, int kq, Digits &D) {
   }
 }
 
-// Activation staging.  The 16 x 256 code bytes of one (m-block, super-block)
-// are read with coalesced loads (each 64-lane load covers 4 whole rows) into
-// this wave's LDS slab, rows padded to 272 bytes so that the MFMA fragment
-// reads (lane: row l % 16, bytes 64kq .. 64kq+63) are free of bank conflicts.
-// The loads for the next step are issued before the current step's MFMAs; the
-// slab is rewritten only after the current fragments are in VGPRs.
+// ---------------------------------------------------------------------------
+// Activation staging: buffer loads that write LDS directly.
+//
+// A step is one (16-row m-block, super-block) pair.  Its activation data go
+// from global memory straight into an LDS slab of the wave's own ring of R
+// slabs, D = R - 1 steps ahead of their use, so no VGPRs are held while the
+// loads are in flight and the wave only waits when a load is still missing
+// after D steps of work.  A slab holds
+//   codes : 16 rows x 256 int8; 16-byte unit u of row r holds global unit
+//           u ^ r, so the fragment reads (16 lanes = 16 rows at one column
+//           unit) fall in 16 distinct bank groups;
+//   d_x   : 64 floats, float i = d_x of row i % 16;
+//   bsum  : (Q4_K) 16 rows x 8 int32 code sums of the super-block.
+// Each buffer-to-LDS load writes 64 consecutive elements (one per lane) at the
+// LDS address held in M0; each lane chooses the global element it brings.
 constexpr int MBLK = 16;  // rows per m-block
-constexpr int SLAB_PITCH = 272;
-constexpr int SLAB_BYTES = MBLK * SLAB_PITCH + MBLK * 4;  // codes + d_x of the 16 rows
+constexpr int SLAB_DX = MBLK * QK;   // 4096
+constexpr int SLAB_BS = SLAB_DX + 256;
+template <bool Q6>
+constexpr int slab_bytes() {
+  return Q6 ? SLAB_BS : SLAB_BS + MBLK * 8 * 4;
+}
+// buffer-to-LDS loads per step
+template <bool Q6, bool DEBUG>
+constexpr int dma_per_step() {
+  return 4 + (DEBUG ? 0 : 1) + (Q6 ? 0 : 2);
+}
 
-struct ActLoad {
-  i32x4 v[4];  // row 4i + lane/16, bytes 16 * (lane % 16) .. +15, for i = 0..3
-  float dxv;   // d_x of row (lane % 16)
-  uint2 bs;    // code sums of sub-blocks 2kq, 2kq + 1 of row (lane % 16)
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Per-lane global offsets of the slab loads (relative to the step's bases).
+struct DmaLane {
+  int q[4];   // codes: load i brings rows 4i .. 4i+3
+  int dx;     // d_x of row lane % 16
+  int bs[2];  // code sums: load h brings rows 8h .. 8h+7
 };
 
-// Loads of step (m-block starting at row m_base, super-block b).  The
-// resource bases start at row m_base, so rows at or past M fall outside
-// num_records and read as zeros.
-template <bool Q6, bool DEBUG>
-__device__ inline void act_issue(const int8_t *q, const float *dx, const int32_t *bsum,
-                                 int64_t m_base, int64_t M, int64_t K, int nb, int b, int lane,
-                                 ActLoad &L) {
-  const int64_t rows_left = M - m_base;
-  const auto Rq = rsrc(q + m_base * K + (int64_t)b * QK, rows_left * K - (int64_t)b * QK);
-  const int voff = (lane >> 4) * (int)K + 16 * (lane & 15);
+__device__ inline DmaLane dma_lane(int lane, int K, int nb) {
+  DmaLane o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) L.v[i] = ld4(Rq, voff + 4 * i * (int)K);
-  const int r = lane & 15;
-  L.dxv = 0.f;
-  if (!DEBUG) {
-    const auto Rd = rsrc(dx + m_base * nb + b, (rows_left * nb - b) * 4);
-    L.dxv = __builtin_bit_cast(float, ld1(Rd, r * nb * 4));
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4), u = lane & 15;
+    o.q[i] = r * K + 16 * (u ^ r);
   }
-  L.bs = make_uint2(0u, 0u);
+  o.dx = (lane & 15) * nb * 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) o.bs[h] = (8 * h + (lane >> 3)) * (K / 32) * 4 + 4 * (lane & 7);
+  return o;
+}
+
+// Loads of step (m-block at row m_base, super-block b) into the slab at LDS
+// address `slab`.  Each descriptor starts at the step's first row and ends
+// after its last valid row, so rows at or past M read as zeros.
+template <bool Q6, bool DEBUG>
+__device__ inline void dma_step(uint32_t slab, const int8_t *q, const float *dx,
+                                const int32_t *bsum, int M, int K, int nb, int m_base, int b,
+                                const DmaLane &dl) {
+  const int left = M - m_base;
+  const int rows = left <= 0 ? 0 : (left >= MBLK ? MBLK : left);
+  const i32x4 dq_ = desc(q + (int64_t)m_base * K + b * QK, rows ? rows * K - b * QK : 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16(dq_, slab + 1024 * i, dl.q[i]);
+  if (!DEBUG) {
+    const i32x4 dd = desc(dx + (int64_t)m_base * nb + b, rows ? (rows * nb - b) * 4 : 0);
+    dma4(dd, slab + SLAB_DX, dl.dx);
+  }
   if (!Q6) {
-    const auto Rb = rsrc(bsum + m_base * (K / 32) + 8 * b, (rows_left * (K / 32) - 8 * b) * 4);
-    L.bs = ld2(Rb, r * (int)(K / 32) * 4 + 8 * (lane >> 4));
+    const i32x4 db =
+        desc(bsum + (int64_t)m_base * (K / 32) + 8 * b, rows ? (rows * (K / 32) - 8 * b) * 4 : 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dma4(db, slab + SLAB_BS + 256 * h, dl.bs[h]);
   }
 }
 
-__device__ inline void act_store(uint8_t *slab, int lane, const ActLoad &L) {
-  const int rsub = lane >> 4, c16 = lane & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<i32x4 *>(slab + (4 * i + rsub) * SLAB_PITCH + 16 * c16) = L.v[i];
-  // the four lane quarters hold the same 16 values: every lane writes, so no
-  // divergent branch sits between this write and the next step's reads
-  reinterpret_cast<float *>(slab + MBLK * SLAB_PITCH)[lane & 15] = L.dxv;
+// Weight tile of one (n-tile, super-block) into an LDS slot: 1 KB loads for
+// the records, 256 B loads for the tail.  Q6_K: the 32 bytes of d are brought
+// by a 256 B load whose lane l reads d word l % 8.
+template <bool Q6>
+constexpr int wslot_bytes() {
+  return Q6 ? Q6K_D_OFF + 256 : Q4K_TILE;
+}
+template <bool Q6>
+constexpr int dma_per_tile() {
+  return Q6 ? 5 : 3;
+}
+
+template <bool Q6>
+__device__ inline void dma_tile(uint32_t slot, const uint8_t *tile, int lane) {
+  const i32x4 d = desc(tile, Q6 ? Q6K_TILE : Q4K_TILE);
+  if (!Q6) {
+    dma16(d, slot, 16 * lane);
+    dma16(d, slot + 1024, 1024 + 16 * lane);
+    dma4(d, slot + 2048, 2048 + 4 * lane);
+  } else {
+    dma16(d, slot, 16 * lane);
+    dma16(d, slot + 1024, 1024 + 16 * lane);
+    dma16(d, slot + 2048, 2048 + 16 * lane);
+    dma4(d, slot + Q6K_SC_OFF, Q6K_SC_OFF + 4 * lane);
+    dma4(d, slot + Q6K_D_OFF, Q6K_D_OFF + 4 * (lane & 7));
+  }
 }
 
 // The MFMA part of one step and what its fold needs.
@@ -249,13 +323,12 @@ struct StepOut {
 };
 
 template <bool Q6>
-__device__ inline void step_mfma(const uint8_t *slab, int col, int kq, const Digits &D,
-                                 const uint2 &bs, StepOut &o) {
+__device__ inline void step_mfma(const uint8_t *slab, const int (&frag)[4], int col, int kq,
+                                 const Digits &D, StepOut &o) {
   i32x4 a[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    a[c] = *reinterpret_cast<const i32x4 *>(slab + col * SLAB_PITCH + 64 * kq + 16 * c);
-  o.x4 = *reinterpret_cast<const f32x4 *>(slab + MBLK * SLAB_PITCH + 16 * kq);
+  for (int c = 0; c < 4; ++c) a[c] = *reinterpret_cast<const i32x4 *>(slab + frag[c]);
+  o.x4 = *reinterpret_cast<const f32x4 *>(slab + SLAB_DX + 16 * kq);
   o.rl = i32x4{};
   o.rh = i32x4{};
 #pragma unroll
@@ -266,6 +339,7 @@ __device__ inline void step_mfma(const uint8_t *slab, int col, int kq, const Dig
   o.mnf = f32x4{};
   if (!Q6) {
     // bsum = lo6 + rest: both exact in f16 (rest is a multiple of 64, |rest| <= 4096)
+    const uint2 bs = *reinterpret_cast<const uint2 *>(slab + SLAB_BS + 32 * col + 8 * kq);
     f16x4 amin;
     const int v0 = (int)bs.x, v1 = (int)bs.y;
     const int l0 = v0 & 63, l1 = v1 & 63;
@@ -302,21 +376,45 @@ __device__ inline void step_debug(const StepOut &o, int64_t row0, int kq, int64_
 }
 
 constexpr int WAVES = 4;
-constexpr int MB_MAX = 10;
-constexpr int RED_FLOATS = (WAVES / 2) * MB_MAX * 4 * 64;  // reduction buffer
+
+// Launch shape of one GEMM variant: MB 16-row m-blocks per workgroup, R
+// activation slabs per wave (prefetch distance R - 1 steps) and W weight
+// slots per wave (weights W super-blocks ahead).
+template <int MB_, int R_, int W_>
+struct Shape {
+  static constexpr int MB = MB_, R = R_, W = W_;
+};
+
+template <bool Q6, class SH>
+constexpr int wave_lds() {
+  return SH::R * slab_bytes<Q6>() + SH::W * wslot_bytes<Q6>();
+}
+template <bool Q6, class SH>
+constexpr int lds_bytes() {
+  constexpr int ring = WAVES * wave_lds<Q6, SH>();
+  constexpr int red = (WAVES / 2) * SH::MB * 4 * 64 * 4;
+  return ring > red ? ring : red;
+}
+constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 
 // One workgroup of 4 waves: one 16-column n-tile x MB 16-row m-blocks x the
-// whole reduction.  Wave w takes super-blocks b = w, w + 4, ... and builds a
-// super-block's weight digits once for all MB m-blocks.  Loads run ahead: the
-// next super-block's weights during the current one, the next step's
-// activation slab during the current step.  Registers are capped so that at
-// least two workgroups share a CU (two waves per SIMD): one wave's MFMAs run
-// while another folds or waits.  The 4 f32 partial sums are added in LDS
-// (pairwise tree) at the end.
-// MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its own symbol so
-// profiles tell the two workloads apart), 2 = debug stores of S and Mn.
-template <int TYPE, int MB, int MODE>
-__global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int64_t M, int64_t N, int nb,
+// whole reduction.  Wave w takes super-blocks b = w, w + 4, ...; it builds a
+// super-block's weight digits once and runs the MB steps of that super-block
+// against them.  The 4 f32 partial sums are added in LDS (pairwise tree) at
+// the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its own
+// symbol so profiles tell the two workloads apart), 2 = debug stores of S, Mn.
+//
+// Load schedule of one wave (every load is a buffer-to-LDS load):
+//   prologue      : tiles of super-blocks 0 .. W-1, slabs of steps 0 .. D-1
+//   super-block i : wait for tile i; digits; refill its slot with tile i + W
+//     step s      : refill the slab read by step s - 1 with step s + D;
+//                   wait for step s; MFMAs; fold
+// Loads past the wave's last tile or step repeat the last one (valid memory
+// into a slot nobody reads again), so the number of loads issued after any
+// given load is fixed, and each wait is a constant vmcnt: at most that many
+// loads may still be outstanding when the awaited one must have landed.
+template <int TYPE, class SH, int MODE>
+__global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, int nb,
                                                               const int8_t *__restrict__ q,
                                                               const float *__restrict__ dx,
                                                               const int32_t *__restrict__ bsum,
@@ -326,71 +424,104 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int64_t M, int64_t
                                                               int32_t *__restrict__ dbg_Mn) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
+  constexpr int MB = SH::MB, R = SH::R, W = SH::W, D = R - 1;
   constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
-  constexpr int MR = MB * MBLK;
-  constexpr int LDS_BYTES = WAVES * SLAB_BYTES > RED_FLOATS * 4 ? WAVES * SLAB_BYTES : RED_FLOATS * 4;
-  static_assert(MB <= MB_MAX, "reduction buffer");
+  constexpr int SLAB = slab_bytes<Q6>(), WSLOT = wslot_bytes<Q6>();
+  constexpr int GA = dma_per_step<Q6, DEBUG>(), GW = dma_per_tile<Q6>();
+  // loads issued after tile i when it is awaited: first W super-blocks, then steady state
+  constexpr int WAIT_W0 = cap63((W - 1) * GW + D * GA);
+  constexpr int WAIT_W = cap63((W - 1) * GW + W * MB * GA);
+  constexpr int WAIT_A = D * GA;
+  static_assert(R >= 2 && WAIT_A < 64 && W >= 1, "pipeline shape");
+  static_assert(lds_bytes<Q6, SH>() <= 80 * 1024, "two workgroups per CU");
   using Raw = typename std::conditional<Q6, RawQ6, RawQ4>::type;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<Q6, SH>()];
 
   // the wave index is uniform across the wave; say so, so that every buffer
-  // resource built from it stays in scalar registers
+  // descriptor and LDS address derived from it stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int64_t nt = blockIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.y * MR;
+  const int m0 = (int)blockIdx.y * (MB * MBLK);
   const int64_t n = nt * TILE_N + col;
-  const int64_t K = (int64_t)nb * QK;
-  uint8_t *slab = lds + wave * SLAB_BYTES;
+  const int K = nb * QK;
+  // this wave's LDS: R activation slabs, then W weight slots
+  uint8_t *ring = lds + wave * wave_lds<Q6, SH>();
+  uint8_t *wslots = ring + R * SLAB;
+  const uint32_t ring_a = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
+  const uint32_t wslots_a = ring_a + R * SLAB;
 
   f32x4 acc[MB];
 #pragma unroll
   for (int t = 0; t < MB; ++t) acc[t] = f32x4{};
 
-  const uint8_t *tiles = packed + nt * nb * TB;
-  if (wave < nb) {
-    int b = wave;
-    Raw wcur, wnxt;
-    ActLoad al;
-    load_w(tiles + (int64_t)b * TB, lane, col, kq, wcur);
-    act_issue<Q6, DEBUG>(q, dx, bsum, m0, M, K, nb, b, lane, al);
-    load_w(tiles + (int64_t)(b + WAVES < nb ? b + WAVES : b) * TB, lane, col, kq, wnxt);
-    act_store(slab, lane, al);
-    uint2 bs = al.bs;
-    Digits D;
-    make_digits(wcur, kq, D);
-    for (;;) {
-      const bool last_b = b + WAVES >= nb;
-      const int bn = last_b ? b : b + WAVES;
+  const int nbw = wave < nb ? (nb - wave + WAVES - 1) / WAVES : 0;  // this wave's super-blocks
+  const int S = nbw * MB;                                           // and steps
+  if (S > 0) {
+    const uint8_t *tiles = packed + nt * nb * TB;
+    const DmaLane dl = dma_lane(lane, K, nb);
+    int frag[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) frag[c] = col * QK + 16 * ((4 * kq + c) ^ col);
+
+    auto issue_a = [&](int s, int slot) {
+      s = s < S ? s : S - 1;
+      const int bi = s / MB, t = s - bi * MB;
+      dma_step<Q6, DEBUG>(ring_a + slot * SLAB, q, dx, bsum, M, K, nb, m0 + MBLK * t,
+                          wave + WAVES * bi, dl);
+    };
+    auto issue_w = [&](int bi, int slot) {
+      bi = bi < nbw ? bi : nbw - 1;
+      dma_tile<Q6>(wslots_a + slot * WSLOT, tiles + (int64_t)(wave + WAVES * bi) * TB, lane);
+    };
+#pragma unroll
+    for (int i = 0; i < W; ++i) issue_w(i, i);
+#pragma unroll
+    for (int p = 0; p < D; ++p) issue_a(p, p);
+
+    int s_next = D;     // next step to load
+    int slot_next = D;  // its slab
+    int slot_use = 0;   // slab of the current step
+    int wslot = 0;      // slot of the current tile
+    for (int bi = 0; bi < nbw; ++bi) {
+      const int b = wave + WAVES * bi;
+      if (bi < W)
+        wait_vm<WAIT_W0>();
+      else
+        wait_vm<WAIT_W>();
+      Digits Dg;
+      {
+        Raw w;
+        read_w(wslots + wslot * WSLOT, lane, col, kq, w);
+        make_digits(w, kq, Dg);
+      }
+      wait_lds();
+      issue_w(bi + W, wslot);
+      wslot = wslot + 1 == W ? 0 : wslot + 1;
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
-        // next step's activations: (t+1, b), or (0, next super-block)
-        if (t + 1 < MB)
-          act_issue<Q6, DEBUG>(q, dx, bsum, m0 + MBLK * (t + 1), M, K, nb, b, lane, al);
-        else
-          act_issue<Q6, DEBUG>(q, dx, bsum, m0, M, K, nb, bn, lane, al);
+        wait_lds();  // the slab about to be refilled was read by the previous step
+        issue_a(s_next, slot_next);
+        ++s_next;
+        slot_next = slot_next + 1 == R ? 0 : slot_next + 1;
+        wait_vm<WAIT_A>();
         StepOut cur;
-        step_mfma<Q6>(slab, col, kq, D, bs, cur);
-        act_store(slab, lane, al);  // after this step's fragments are in VGPRs
-        bs = al.bs;
+        step_mfma<Q6>(ring + slot_use * SLAB, frag, col, kq, Dg, cur);
+        slot_use = slot_use + 1 == R ? 0 : slot_use + 1;
         if (DEBUG)
           step_debug<Q6>(cur, m0 + MBLK * t, kq, n, M, N, nb, b, dbg_S, dbg_Mn);
         else
-          step_fold<Q6>(cur, D.dw, D.dmw, acc[t]);
+          step_fold<Q6>(cur, Dg.dw, Dg.dmw, acc[t]);
       }
-      if (last_b) break;
-      b = bn;
-      wcur = wnxt;
-      load_w(tiles + (int64_t)(b + WAVES < nb ? b + WAVES : b) * TB, lane, col, kq, wnxt);
-      make_digits(wcur, kq, D);
     }
+    wait_vm<0>();  // no LDS write may land after this point
   }
   if (DEBUG) return;
 
   // cross-wave reduction: pairwise tree through LDS
   float *red = reinterpret_cast<float *>(lds);
-  __syncthreads();  // activation slabs no longer needed
+  __syncthreads();  // every wave is done with its ring
 #pragma unroll
   for (int half = WAVES / 2; half >= 1; half /= 2) {
     if (wave >= half && wave < 2 * half) {
@@ -415,52 +546,54 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int64_t M, int64_t
     for (int t = 0; t < MB; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + MBLK * t + 4 * kq + i;
-        if (row < M) y[row * ldy + n] = acc[t][i];
+        const int row = m0 + MBLK * t + 4 * kq + i;
+        if (row < M) y[(int64_t)row * ldy + n] = acc[t][i];
       }
   }
 }
 
-template <int TYPE, int MB>
+template <int TYPE, class SH>
 hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const int8_t *q, const float *d,
                    const int32_t *bsum, const uint8_t *packed, float *y, int64_t ldy,
                    int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream) {
-  dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N), (unsigned)((M + MBLK * MB - 1) / (MBLK * MB)));
+  dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N),
+            (unsigned)((M + MBLK * SH::MB - 1) / (MBLK * SH::MB)));
   dim3 block(64 * WAVES);
+  const int m = (int)M;
   if (mode == 2)
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, MB, 2>), grid, block, 0, stream, M, N, nb, q, d, bsum,
+    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 2>), grid, block, 0, stream, m, N, nb, q, d, bsum,
                        packed, y, ldy, dbg_S, dbg_Mn);
   else if (mode == 1)
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, MB, 1>), grid, block, 0, stream, M, N, nb, q, d, bsum,
+    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 1>), grid, block, 0, stream, m, N, nb, q, d, bsum,
                        packed, y, ldy, dbg_S, dbg_Mn);
   else
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, MB, 0>), grid, block, 0, stream, M, N, nb, q, d, bsum,
+    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 0>), grid, block, 0, stream, m, N, nb, q, d, bsum,
                        packed, y, ldy, dbg_S, dbg_Mn);
   return hipGetLastError();
 }
 
-// 16-row m-blocks per workgroup, from the compiled set of each type (the
-// sets leave out the sizes whose register demand exceeds the two-waves-per-
-// SIMD budget).  Prefer the largest MB (the weight digits are built once per
-// MB blocks) that still launches two waves per SIMD (n-tiles x m-chunks x 4
-// waves >= 2048) with at most one padded m-block per chunk; otherwise the
-// choice with the most waves.
-constexpr int MB_Q4[] = {8, 5, 4, 3, 2, 1};
-constexpr int MB_Q6[] = {10, 5, 4, 3, 2, 1};
+// Compiled variants, indexed by the number of 16-row m-blocks per workgroup.
+// Small MB (few steps per super-block) keeps more weight tiles in flight: the
+// weight stream is what the narrow GEMMs wait for.
+using V1 = Shape<1, 2, 3>;
+using V2 = Shape<2, 2, 3>;
+using V3 = Shape<3, 3, 2>;
+using V4 = Shape<4, 3, 2>;
+using V5 = Shape<5, 3, 1>;
+using V8 = Shape<8, 3, 1>;
+using V10 = Shape<10, 3, 1>;
+using V16 = Shape<16, 3, 1>;
+constexpr int MB_SET[] = {16, 10, 8, 5, 4, 3, 2, 1};
 
-template <int TYPE>
-constexpr bool has_mb(int mb) {
-  for (int v : (TYPE == 14 ? MB_Q6 : MB_Q4))
-    if (v == mb) return true;
-  return false;
-}
-
-template <int TYPE>
-int pick_mb(int64_t M, int64_t N) {
+// Prefer the largest MB (weight digits are built once per MB steps) that
+// still launches two waves per SIMD (n-tiles x m-chunks x 4 waves >= 2048)
+// with at most one padded m-block per chunk; otherwise the choice with the
+// most waves.
+inline int pick_mb(int64_t M, int64_t N) {
   const int64_t mblocks = (M + MBLK - 1) / MBLK, ntiles = (N + TILE_N - 1) / TILE_N;
   int best = 1;
   int64_t best_waves = -1;
-  for (int mb : (TYPE == 14 ? MB_Q6 : MB_Q4)) {
+  for (int mb : MB_SET) {
     if (mb > mblocks && mb != 1) continue;
     const int64_t chunks = (mblocks + mb - 1) / mb;
     const int64_t waste = chunks * mb - mblocks;
@@ -478,13 +611,10 @@ template <int TYPE>
 hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const int8_t *q, const float *d,
                        const int32_t *bsum, const uint8_t *packed, float *y, int64_t ldy,
                        int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream) {
-#define DQ_MB(V)                                                                          \
-  case V:                                                                                 \
-    if constexpr (has_mb<TYPE>(V))                                                        \
-      return launch2<TYPE, V>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, \
-                              stream);                                                    \
-    break
-  switch (pick_mb<TYPE>(M, N)) {
+#define DQ_MB(X) \
+  case X: return launch2<TYPE, V##X>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream)
+  switch (pick_mb(M, N)) {
+    DQ_MB(16);
     DQ_MB(10);
     DQ_MB(8);
     DQ_MB(5);
@@ -494,7 +624,7 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const int8_t *q, 
     default: break;
   }
 #undef DQ_MB
-  return launch2<TYPE, 1>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream);
+  return launch2<TYPE, V1>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream);
 }
 
 }  // namespace
