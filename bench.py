@@ -114,9 +114,7 @@ def main():
     acts = {"qkv": up(synth.activations(act_rng, L, K)), "o": up(synth.activations(act_rng, L, K)),
             "ffn": up(synth.activations(act_rng, L, K)),
             "down": up(synth.activations(act_rng, L, F))}
-    qb = {kk: (torch.empty((L, kk), dtype=torch.int8, device=dev),
-               torch.empty((L, kk // 256), dtype=torch.float32, device=dev),
-               torch.empty((L, kk // 32), dtype=torch.int32, device=dev)) for kk in (K, F)}
+    qbuf = {kk: torch.empty(dq.act_size(L, kk), dtype=torch.uint8, device=dev) for kk in (K, F)}
     outs = {name: torch.empty((L, N), dtype=torch.float32, device=dev)
             for name, _, N, _ in synth.llada_layer(1)}
     host_keep = {}
@@ -147,18 +145,16 @@ def main():
     def quant(name):
         x = acts[name]
         kk = x.shape[1]
-        q, d, b = qb[kk]
-        calls.append((lib.dq_quantize_act,
-                      (L, kk, x.data_ptr(), kk, q.data_ptr(), d.data_ptr(), b.data_ptr(), sp),
+        buf = qbuf[kk]
+        calls.append((lib.dq_quantize_act, (L, kk, x.data_ptr(), kk, buf.data_ptr(), sp),
                       "quantize", 0, quant_bytes(L, kk)))
-        return q, d, b
+        return buf
 
-    def gemm(lp, name, qdb):
+    def gemm(lp, name, buf):
         t, N, kk, pk = lp[name]
-        q, d, b = qdb
         y = outs[name]
-        calls.append((lib.dq_qgemm, (t, L, N, kk, q.data_ptr(), d.data_ptr(), b.data_ptr(),
-                                     pk.data_ptr(), y.data_ptr(), N, sp),
+        calls.append((lib.dq_qgemm, (t, L, N, kk, buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N,
+                                     sp),
                       f"qgemm_{'q4k' if t == Q4_K else 'q6k'}", 2 * L * N * kk,
                       gemm_bytes(t, L, N, kk)))
 

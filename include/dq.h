@@ -85,6 +85,30 @@ int dq_repack_weights(int type, int64_t N, int64_t K, const void *gguf, void *pa
                       hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * Quantized activations.  dq_quantize_act writes, and dq_qgemm /
+ * dq_debug_superblock_sums read, one device buffer of dq_act_size(M, K)
+ * bytes laid out for the GEMM's loads: rows are grouped in blocks of 16
+ * (MB = ceil(M/16) blocks; rows M .. 16*MB-1 are all-zero padding) and each
+ * (super-block b, row block mb) pair is one record of DQ_ACT_RECORD bytes at
+ * byte offset (b*MB + mb) * DQ_ACT_RECORD:
+ *   [0, 4096)     codes (int8).  Row r (0..15) of the block holds the 256
+ *                 codes of super-block b as 16 units of 16 bytes; unit u is
+ *                 stored at r*256 + 16*(u XOR r).
+ *   [4096, 4608)  code sums.  For row r and 32-wide group j (0..7) of the
+ *                 super-block, at 4096 + r*32 + j*4: the sum s of the group's
+ *                 32 codes as two IEEE binary16 values (lo, hi) with
+ *                 lo = s AND 63 (two's complement) and hi = s - lo; both are
+ *                 exact, and s = lo + hi.
+ *   [4608, 4672)  d_x of rows 0..15 (binary32).
+ *   [4672, 5120)  zero.
+ * ------------------------------------------------------------------------ */
+#define DQ_ACT_RECORD 5120
+
+/* Bytes of the quantized-activation buffer for M rows of length K (host-only).
+ * Errors: DQ_EINVAL (K, M < 0, bytes NULL, size beyond 2^32). */
+int dq_act_size(int64_t M, int64_t K, size_t *bytes);
+
+/* --------------------------------------------------------------------------
  * dq_quantize_act -- f32 activations -> int8 codes, one f32 scale per 256.
  *
  * Source: Architecture page, "Source map" (kernels/qgemm.mojo): activation
@@ -94,19 +118,18 @@ int dq_repack_weights(int type, int64_t N, int64_t K, const void *gguf, void *pa
  *   amax = max |x|; if amax == 0: d = 0 and every code is 0;
  *   else inv = 127/amax (correctly rounded), q = clamp(rint(x*inv), -127, 127)
  *   with ties to even, d = amax/127.
- *   bsum[m][k/32] = sum of the 32 codes of each group (int32).
+ *   code sums per 32 consecutive values (int32, stored as described above).
  * The codes, scales and sums are bit-identical to any binary32 implementation
  * of these steps.  Inputs must be finite; amax below 127/FLT_MAX is out of
  * domain.
  *
- *   x    : device f32, M rows, row stride ldx >= K floats; read only.
- *   q    : device int8 [M][K] (row stride K), 16-byte aligned.
- *   d    : device f32 [M][K/256].
- *   bsum : device int32 [M][K/32], 16-byte aligned.
+ *   x  : device f32, M rows, row stride ldx >= K floats; read only.
+ *   qa : device buffer of dq_act_size(M, K) bytes, 16-byte aligned; written
+ *        fully (padding rows and the zero tail of each record included).
  * Errors: DQ_EINVAL (shape, ldx < K, NULL, alignment), DQ_EHIP.
  * ------------------------------------------------------------------------ */
-int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *q, float *d,
-                    int32_t *bsum, hipStream_t stream);
+int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, void *qa,
+                    hipStream_t stream);
 
 /* --------------------------------------------------------------------------
  * dq_qgemm -- y[m][n] = sum_k w^[n][k] * x^[m][k] for int8 activations and a
@@ -122,19 +145,19 @@ int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *q
  * on int8 matrix cores and folds y += d_x*(d*S - dmin*Mn) in binary32.
  * |y - y_exact| stays far below 1e-4 * sum_k |w^ x^|.
  *
- *   q, d, bsum : the outputs of dq_quantize_act for these M rows (bsum may be
- *                NULL for Q6_K).
- *   packed     : output of dq_repack_weights for (type, N, K).
- *   y          : device f32, M rows, row stride ldy >= N; columns [0, N) of
- *                each row are written, nothing else.
+ *   qa     : the output of dq_quantize_act for these M rows and this K.
+ *   packed : output of dq_repack_weights for (type, N, K).
+ *   y      : device f32, M rows, row stride ldy >= N; columns [0, N) of
+ *            each row are written, nothing else.
  * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (shape, ldy < N, NULL, alignment), DQ_EHIP.
  * ------------------------------------------------------------------------ */
-int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *d,
-             const int32_t *bsum, const void *packed, float *y, int64_t ldy, hipStream_t stream);
+int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const void *qa, const void *packed,
+             float *y, int64_t ldy, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
  * dq_qgemm_rows_workspace -- workspace bytes dq_qgemm_rows needs for M
- * gathered rows of length K (host-only).
+ * gathered rows of length K (host-only): the index flags, then the quantized
+ * activations of the gathered rows.
  * ------------------------------------------------------------------------ */
 int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes);
 
@@ -172,11 +195,11 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
  *   Mn[(m*N + n)*(K/256) + b] = sum_j m_j * bsum_j   (Q4_K; 0 for Q6_K)
  * With every scale but sub-block j's set to 0 (and that one to 1) S equals
  * the sub-block dot dot_j, which is how per-sub-block dots are checked.
- * S and Mn are device int32 arrays of M*N*(K/256) entries.
+ * qa is a dq_quantize_act buffer (its d_x values are not used).  S and Mn are
+ * device int32 arrays of M*N*(K/256) entries.
  * ------------------------------------------------------------------------ */
-int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
-                             const int32_t *bsum, const void *packed, int32_t *S, int32_t *Mn,
-                             hipStream_t stream);
+int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const void *qa,
+                             const void *packed, int32_t *S, int32_t *Mn, hipStream_t stream);
 
 #ifdef __cplusplus
 }

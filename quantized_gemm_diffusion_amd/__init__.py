@@ -7,14 +7,17 @@ the library is missing, every call raises.  torch supplies device memory and
 the current stream; tensors must live on a GPU.
 
 Names follow the C ABI:
-  packed_size, repack_weights, quantize_act, qgemm, qgemm_rows_workspace,
-  qgemm_rows, debug_superblock_sums.
+  packed_size, repack_weights, act_size, quantize_act, qgemm,
+  qgemm_rows_workspace, qgemm_rows, debug_superblock_sums.
+Quantized activations travel as an ``Act`` (the device buffer in the record
+layout that include/dq.h documents, with its M and K).
 """
 from __future__ import annotations
 
 import ctypes
 import os
 import threading
+from typing import NamedTuple
 
 import torch
 
@@ -28,8 +31,17 @@ DQ_OK, DQ_EINVAL, DQ_EUNSUPPORTED, DQ_EWORKSPACE, DQ_EHIP = 0, 1, 2, 3, 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdq.so")
 
 EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_weights",
-           "dq_quantize_act", "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows",
-           "dq_debug_superblock_sums")
+           "dq_act_size", "dq_quantize_act", "dq_qgemm", "dq_qgemm_rows_workspace",
+           "dq_qgemm_rows", "dq_debug_superblock_sums")
+ACT_RECORD = 5120  # bytes per (super-block, 16-row block) record
+
+
+class Act(NamedTuple):
+    """Quantized activations: ``buf`` (uint8, act_size(M, K) bytes) for M rows of K."""
+    buf: torch.Tensor
+    M: int
+    K: int
+
 
 _lib = None
 _lock = threading.Lock()
@@ -59,11 +71,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         sigs = {
             "dq_packed_size": [i32, i64, i64, psz],
             "dq_repack_weights": [i32, i64, i64, vp, vp, vp],
-            "dq_quantize_act": [i64, i64, vp, i64, vp, vp, vp, vp],
-            "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp],
+            "dq_act_size": [i64, i64, psz],
+            "dq_quantize_act": [i64, i64, vp, i64, vp, vp],
+            "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
             "dq_qgemm_rows_workspace": [i64, i64, psz],
             "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
-            "dq_debug_superblock_sums": [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp],
+            "dq_debug_superblock_sums": [i32, i64, i64, i64, vp, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -118,58 +131,54 @@ def repack_weights(type_: int, N: int, K: int, gguf: torch.Tensor,
     return packed
 
 
-def quantize_act(x: torch.Tensor, q=None, d=None, bsum=None):
-    """f32 [M, K] (row stride >= K, unit column stride) -> (q int8, d f32, bsum int32)."""
+def act_size(M: int, K: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_act_size(M, K, ctypes.byref(out)), "dq_act_size")
+    return out.value
+
+
+def quantize_act(x: torch.Tensor, out: torch.Tensor | None = None) -> Act:
+    """f32 [M, K] (row stride >= K, unit column stride) -> Act."""
     lib = load_library()
     _need(x, torch.float32, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     M, K = x.shape
-    dev = x.device
-    q = torch.empty((M, K), dtype=torch.int8, device=dev) if q is None else q
-    d = torch.empty((M, K // QK), dtype=torch.float32, device=dev) if d is None else d
-    bsum = torch.empty((M, K // 32), dtype=torch.int32, device=dev) if bsum is None else bsum
-    _need(q, torch.int8, "q"), _need(d, torch.float32, "d"), _need(bsum, torch.int32, "bsum")
-    for t, shape, name in ((q, (M, K), "q"), (d, (M, K // QK), "d"), (bsum, (M, K // 32), "bsum")):
-        if tuple(t.shape) != shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous with shape {shape}")
-    _check(lib.dq_quantize_act(M, K, _ptr(x), x.stride(0) if M > 1 else K, _ptr(q), _ptr(d),
-                               _ptr(bsum), _stream(x)), "dq_quantize_act")
-    return q, d, bsum
+    nbytes = act_size(M, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _need(out, torch.uint8, "out")
+    if out.numel() < nbytes or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous buffer of at least {nbytes} bytes")
+    _check(lib.dq_quantize_act(M, K, _ptr(x), x.stride(0) if M > 1 else K, _ptr(out),
+                               _stream(x)), "dq_quantize_act")
+    return Act(out, M, K)
 
 
-def _check_operands(type_, q, d, bsum, packed, N):
-    """Shape/size checks that keep every kernel access inside the tensors."""
-    _need(q, torch.int8, "q")
-    if q.dim() != 2 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [M, K] int8 tensor")
-    M, K = q.shape
-    if d is not None:
-        _need(d, torch.float32, "d")
-        if tuple(d.shape) != (M, K // QK) or not d.is_contiguous():
-            raise ValueError(f"d must be contiguous [{M}, {K // QK}]")
-    if bsum is not None:
-        _need(bsum, torch.int32, "bsum")
-        if tuple(bsum.shape) != (M, K // 32) or not bsum.is_contiguous():
-            raise ValueError(f"bsum must be contiguous [{M}, {K // 32}]")
+def _check_operands(type_, act: Act, packed, N):
+    """Size checks that keep every kernel access inside the tensors."""
+    _need(act.buf, torch.uint8, "act.buf")
+    if act.buf.numel() < act_size(act.M, act.K) or not act.buf.is_contiguous():
+        raise ValueError("act.buf is smaller than act_size(M, K)")
     _need(packed, torch.uint8, "packed")
-    if packed.numel() < packed_size(type_, N, K) or not packed.is_contiguous():
+    if packed.numel() < packed_size(type_, N, act.K) or not packed.is_contiguous():
         raise ValueError("packed is smaller than packed_size(type, N, K)")
-    return M, K
+    return act.M, act.K
 
 
-def qgemm(type_: int, q: torch.Tensor, d: torch.Tensor, bsum: torch.Tensor | None,
-          packed: torch.Tensor, N: int, y: torch.Tensor | None = None) -> torch.Tensor:
-    """y [M, N] f32 = dequant(q, d) @ dequant(packed)^T."""
+def qgemm(type_: int, act: Act, packed: torch.Tensor, N: int,
+          y: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] f32 = dequant(act) @ dequant(packed)^T."""
     lib = load_library()
-    M, K = _check_operands(type_, q, d, bsum, packed, N)
+    M, K = _check_operands(type_, act, packed, N)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=q.device)
+        y = torch.empty((M, N), dtype=torch.float32, device=act.buf.device)
     _need(y, torch.float32, "y")
     if y.dim() != 2 or y.shape[0] != M or y.shape[1] < N or y.stride(1) != 1:
         raise ValueError("y must be [M, >=N] with unit column stride")
-    _check(lib.dq_qgemm(type_, M, N, K, _ptr(q), _ptr(d), _ptr(bsum), _ptr(packed), _ptr(y),
-                        y.stride(0) if M > 1 else N, _stream(q)), "dq_qgemm")
+    _check(lib.dq_qgemm(type_, M, N, K, _ptr(act.buf), _ptr(packed), _ptr(y),
+                        y.stride(0) if M > 1 else N, _stream(act.buf)), "dq_qgemm")
     return y
 
 
@@ -211,15 +220,15 @@ def qgemm_rows(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packed: torc
     return y, ws
 
 
-def debug_superblock_sums(type_: int, q: torch.Tensor, bsum: torch.Tensor | None,
-                          packed: torch.Tensor, N: int):
+def debug_superblock_sums(type_: int, act: Act, packed: torch.Tensor, N: int):
     """Exact per-(m, n, super-block) integers (S, Mn) from the GEMM kernel's own path."""
     lib = load_library()
-    M, K = _check_operands(type_, q, None, bsum, packed, N)
+    M, K = _check_operands(type_, act, packed, N)
     nb = K // QK
-    S = torch.empty((M, N, nb), dtype=torch.int32, device=q.device)
-    Mn = torch.empty((M, N, nb), dtype=torch.int32, device=q.device)
-    _check(lib.dq_debug_superblock_sums(type_, M, N, K, _ptr(q), _ptr(bsum), _ptr(packed),
-                                        _ptr(S), _ptr(Mn), _stream(q)),
+    dev = act.buf.device
+    S = torch.empty((M, N, nb), dtype=torch.int32, device=dev)
+    Mn = torch.empty((M, N, nb), dtype=torch.int32, device=dev)
+    _check(lib.dq_debug_superblock_sums(type_, M, N, K, _ptr(act.buf), _ptr(packed), _ptr(S),
+                                        _ptr(Mn), _stream(act.buf)),
            "dq_debug_superblock_sums")
     return S, Mn

@@ -2,6 +2,7 @@
 // checks on the host, then one or two kernel launches on the caller's stream.
 // Nothing here allocates device memory or synchronizes.
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -94,69 +95,82 @@ int dq_repack_weights(int type, int64_t N, int64_t K, const void *gguf, void *pa
                   "dq_repack_weights");
 }
 
-int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *q, float *d,
-                    int32_t *bsum, hipStream_t stream) {
+// Bytes of the quantized-activation records of M rows of length K; the GEMM
+// addresses them with 32-bit offsets.
+static int act_bytes(int64_t M, int64_t K, size_t *bytes) {
+  const int64_t nmb = (M + dq::ACT_ROWS - 1) / dq::ACT_ROWS;
+  const int64_t total = nmb * (K / dq::QK) * dq::ACT_RECORD;
+  if (total > INT32_MAX)
+    return fail(DQ_EINVAL, "M = %lld x K = %lld too large for one activation buffer",
+                (long long)M, (long long)K);
+  *bytes = (size_t)total;
+  return DQ_OK;
+}
+
+int dq_act_size(int64_t M, int64_t K, size_t *bytes) {
   if (int s = check_k(K)) return s;
   if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
+  if (int s = act_bytes(M, K, bytes)) return s;
+  return ok();
+}
+
+int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, void *qa,
+                    hipStream_t stream) {
+  size_t bytes = 0;
+  if (int s = dq_act_size(M, K, &bytes)) return s;
   if (ldx < K) return fail(DQ_EINVAL, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
   if (M == 0) return ok();
-  if (!x || !q || !d || !bsum) return fail(DQ_EINVAL, "NULL pointer argument");
-  if (!aligned(q, 16) || !aligned(bsum, 16) || !aligned(d, 4) || !aligned(x, 4))
-    return fail(DQ_EINVAL, "q and bsum must be 16-byte aligned, x and d 4-byte aligned");
-  return launched(dq::launch_quantize(M, K, x, ldx, nullptr, 0, q, d, bsum, nullptr, stream),
+  if (!x || !qa) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(qa, 16) || !aligned(x, 4))
+    return fail(DQ_EINVAL, "qa must be 16-byte aligned, x 4-byte aligned");
+  return launched(dq::launch_quantize(M, K, x, ldx, nullptr, 0, static_cast<uint8_t *>(qa),
+                                      nullptr, stream),
                   "dq_quantize_act");
 }
 
-static int check_gemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
-                      const float *d, const int32_t *bsum, const void *packed, bool need_d) {
+static int check_gemm(int type, int64_t M, int64_t N, int64_t K, const void *qa,
+                      const void *packed) {
   if (int s = check_type(type)) return s;
   if (int s = check_k(K)) return s;
   if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
   if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
-  if ((M + 31) / 32 > 2147483647LL || (N + 31) / 32 > 65535)
+  size_t bytes = 0;
+  if (int s = act_bytes(M, K, &bytes)) return s;
+  if ((N + dq::TILE_N - 1) / dq::TILE_N > INT32_MAX ||
+      (M + dq::ACT_ROWS - 1) / dq::ACT_ROWS > 65535)
     return fail(DQ_EINVAL, "M or N too large for the GEMM grid");
+  if ((K / dq::QK) * (int64_t)dq::Q6K_TILE > INT32_MAX)
+    return fail(DQ_EINVAL, "K too large for the GEMM's 32-bit tile offsets");
   if (M == 0 || N == 0) return DQ_OK;
-  if (!q || !packed || (need_d && !d)) return fail(DQ_EINVAL, "NULL pointer argument");
-  if (type == DQ_Q4_K && !bsum) return fail(DQ_EINVAL, "bsum is required for Q4_K");
-  if (!aligned(q, 16) || !aligned(packed, 16) || (bsum && !aligned(bsum, 16)) ||
-      (d && !aligned(d, 4)))
-    return fail(DQ_EINVAL, "q, bsum and packed must be 16-byte aligned, d 4-byte aligned");
+  if (!qa || !packed) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(qa, 16) || !aligned(packed, 16))
+    return fail(DQ_EINVAL, "qa and packed must be 16-byte aligned");
   return DQ_OK;
 }
 
-int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const int8_t *q, const float *d,
-             const int32_t *bsum, const void *packed, float *y, int64_t ldy, hipStream_t stream) {
-  if (int s = check_gemm(type, M, N, K, q, d, bsum, packed, true)) return s;
+int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const void *qa, const void *packed,
+             float *y, int64_t ldy, hipStream_t stream) {
+  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
   if (ldy < N) return fail(DQ_EINVAL, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
   if (M == 0 || N == 0) return ok();
   if (!y || !aligned(y, 4)) return fail(DQ_EINVAL, "y is NULL or not 4-byte aligned");
-  return launched(dq::launch_qgemm(type, 0, M, N, K, q, d, bsum,
-                                   static_cast<const uint8_t *>(packed), y, ldy, nullptr,
-                                   nullptr, stream),
+  return launched(dq::launch_qgemm(type, 0, M, N, K, static_cast<const uint8_t *>(qa),
+                                   static_cast<const uint8_t *>(packed), y, ldy, nullptr, nullptr,
+                                   stream),
                   "dq_qgemm");
 }
 
-// Workspace: [flags int32 x M | pad to 256] [q int8 M x K] [d f32 M x K/256 | pad]
-//            [bsum int32 M x K/32]
-static size_t rows_ws_layout(int64_t M, int64_t K, size_t *off_q, size_t *off_d,
-                             size_t *off_b) {
-  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-  size_t o = up((size_t)M * 4);
-  *off_q = o;
-  o = up(o + (size_t)M * (size_t)K);
-  *off_d = o;
-  o = up(o + (size_t)M * (size_t)(K / dq::QK) * 4);
-  *off_b = o;
-  o = up(o + (size_t)M * (size_t)(K / 32) * 4);
-  return o;
-}
+// Workspace: [flags int32 x M | pad to 256] [quantized-activation records]
+static size_t rows_ws_flags(int64_t M) { return ((size_t)M * 4 + 255) & ~(size_t)255; }
 
 int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes) {
   if (int s = check_k(K)) return s;
   if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
   if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
-  size_t a, b, c;
-  *bytes = rows_ws_layout(M, K, &a, &b, &c);
+  size_t act = 0;
+  if (int s = act_bytes(M, K, &act)) return s;
+  *bytes = rows_ws_flags(M) + act;
   return ok();
 }
 
@@ -174,36 +188,32 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
   if (!canvas || !idx || !packed || !y) return fail(DQ_EINVAL, "NULL pointer argument");
   if (!aligned(canvas, 4) || !aligned(idx, 4) || !aligned(y, 4) || !aligned(packed, 16))
     return fail(DQ_EINVAL, "canvas, idx, y must be 4-byte aligned, packed 16-byte aligned");
-  size_t off_q, off_d, off_b;
-  const size_t need = rows_ws_layout(M, K, &off_q, &off_d, &off_b);
+  size_t need = 0;
+  if (int s = dq_qgemm_rows_workspace(M, K, &need)) return s;
   if (!ws || ws_bytes < need)
     return fail(DQ_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
   if (!aligned(ws, 256)) return fail(DQ_EINVAL, "workspace must be 256-byte aligned");
-  if (int s = check_gemm(type, M, N, K, (const int8_t *)ws, (const float *)ws,
-                         (const int32_t *)ws, packed, true))
-    return s;
   uint8_t *w = static_cast<uint8_t *>(ws);
+  uint8_t *qa = w + rows_ws_flags(M);
+  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
   int32_t *flags = reinterpret_cast<int32_t *>(w);
-  int8_t *q = reinterpret_cast<int8_t *>(w + off_q);
-  float *d = reinterpret_cast<float *>(w + off_d);
-  int32_t *bs = reinterpret_cast<int32_t *>(w + off_b);
-  hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, q, d, bs, flags, stream);
+  hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
   if (e != hipSuccess) return launched(e, "dq_qgemm_rows (gather-quantize)");
-  return launched(dq::launch_qgemm(type, 1, M, N, K, q, d, bs, static_cast<const uint8_t *>(packed),
-                                   y, ldy, nullptr, nullptr, stream),
+  return launched(dq::launch_qgemm(type, 1, M, N, K, qa, static_cast<const uint8_t *>(packed), y,
+                                   ldy, nullptr, nullptr, stream),
                   "dq_qgemm_rows (gemm)");
 }
 
-int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const int8_t *q,
-                             const int32_t *bsum, const void *packed, int32_t *S, int32_t *Mn,
-                             hipStream_t stream) {
-  if (int s = check_gemm(type, M, N, K, q, nullptr, bsum, packed, false)) return s;
+int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const void *qa,
+                             const void *packed, int32_t *S, int32_t *Mn, hipStream_t stream) {
+  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
   if (M == 0 || N == 0) return ok();
   if (!S || !Mn || !aligned(S, 4) || !aligned(Mn, 4))
     return fail(DQ_EINVAL, "S and Mn must be non-NULL and 4-byte aligned");
-  return launched(dq::launch_qgemm(type, 2, M, N, K, q, nullptr, bsum,
-                                   static_cast<const uint8_t *>(packed), nullptr, N, S, Mn,
-                                   stream),
+  if ((int64_t)M * N * (K / dq::QK) > ((int64_t)1 << 40))
+    return fail(DQ_EINVAL, "debug output too large");
+  return launched(dq::launch_qgemm(type, 2, M, N, K, static_cast<const uint8_t *>(qa),
+                                   static_cast<const uint8_t *>(packed), nullptr, N, S, Mn, stream),
                   "dq_debug_superblock_sums");
 }
 

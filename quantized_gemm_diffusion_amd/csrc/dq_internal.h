@@ -43,6 +43,14 @@ constexpr int Q6K_QH_OFF = 2048;
 constexpr int Q6K_SC_OFF = 3072;
 constexpr int Q6K_D_OFF = 3328;
 
+// Quantized-activation records (the layout is part of the C ABI, see dq.h):
+// one per (super-block, 16-row block), super-block-major.
+constexpr int ACT_ROWS = 16;
+constexpr int ACT_RECORD = 5120;
+constexpr int ACT_SUMS_OFF = 4096;  // [16 rows][8 groups] binary16 (lo, hi)
+constexpr int ACT_DX_OFF = 4608;    // [16 rows] binary32
+constexpr int ACT_PAD_OFF = 4672;   // zero up to ACT_RECORD
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -54,14 +62,15 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Launchers (each returns the hipError_t of its launch).
+// Quantize M rows (row m = x[m], or x[idx[m]] when idx is given) into the
+// record layout; err[m] flags an index outside [0, L).
 hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, const int32_t *idx,
-                           int64_t L, int8_t *q, float *d, int32_t *bsum, int32_t *err,
-                           hipStream_t stream);
+                           int64_t L, uint8_t *qa, int32_t *err, hipStream_t stream);
 hipError_t launch_repack(int type, int64_t N, int64_t K, const uint8_t *src, uint8_t *dst,
                          hipStream_t stream);
 // mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers.
-hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const int8_t *q,
-                        const float *d, const int32_t *bsum, const uint8_t *packed, float *y,
-                        int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream);
+hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
+                        const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
+                        int32_t *dbg_Mn, hipStream_t stream);
 
 }  // namespace dq

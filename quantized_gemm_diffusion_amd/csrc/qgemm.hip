@@ -61,35 +61,35 @@ __device__ inline void q6k_digits(uint32_t codes, uint32_t sc2, uint32_t off2, u
   hi = __builtin_amdgcn_perm(uo << 1, ue << 1, 0x07030501u);
 }
 
-// All global reads are buffer loads that write LDS directly.  A buffer
-// descriptor (gfx9 layout: base address, stride 0, size in bytes, flags) is
-// built per load group from scalar values, so per-lane offsets stay small
-// 32-bit constants and the hardware range check (size) returns zeros past
-// the end of a buffer: activation rows past M read as 0 without any per-lane
-// clamping.
+// Every global read is a buffer load that writes LDS directly.  One buffer
+// descriptor (gfx9 layout: base address, stride 0, size in bytes, flags)
+// covers a whole operand; the per-load position is a wave-uniform scalar
+// offset plus a per-lane offset that never changes, so issuing a load costs
+// no vector instructions.  Every access is inside its operand by
+// construction.
 constexpr int DESC_FLAGS = 0x00020000;
 
-__device__ inline i32x4 desc(const void *base, int bytes) {
+__device__ inline i32x4 desc(const void *base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), bytes < 0 ? 0 : bytes,
-               DESC_FLAGS};
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, DESC_FLAGS};
 }
 
 // Buffer-to-LDS loads: M0 holds the LDS byte address; lane l writes its
 // element at M0 + l * size.  They are written as inline assembly so that the
 // compiler, which cannot tell the LDS slots of the ring apart, does not wait
 // for every one of them before each LDS read; all waits on them are explicit
-// (wait_vm below).  Descriptor and LDS address are wave-uniform.
-__device__ inline void dma16(const i32x4 &d, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+// (wait_vm below).  Descriptor, scalar offset and LDS address are
+// wave-uniform.
+__device__ inline void dma16(const i32x4 &d, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(d)
+               : "s"(lds), "v"(voff), "s"(d), "s"(soff)
                : "memory");
 }
-__device__ inline void dma4(const i32x4 &d, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+__device__ inline void dma4(const i32x4 &d, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(d)
+               : "s"(lds), "v"(voff), "s"(d), "s"(soff)
                : "memory");
 }
 
@@ -214,85 +214,31 @@ __device__ inline void make_digits(const RawQ6 &w, int kq, Digits &D) {
 }
 
 // ---------------------------------------------------------------------------
-// Activation staging: buffer loads that write LDS directly.
-//
-// A step is one (16-row m-block, super-block) pair.  Its activation data go
-// from global memory straight into an LDS slab of the wave's own ring of R
-// slabs, D = R - 1 steps ahead of their use, so no VGPRs are held while the
-// loads are in flight and the wave only waits when a load is still missing
-// after D steps of work.  A slab holds
-//   codes : 16 rows x 256 int8; 16-byte unit u of row r holds global unit
-//           u ^ r, so the fragment reads (16 lanes = 16 rows at one column
-//           unit) fall in 16 distinct bank groups;
-//   d_x   : 64 floats, float i = d_x of row i % 16;
-//   bsum  : (Q4_K) 16 rows x 8 int32 code sums of the super-block.
-// Each buffer-to-LDS load writes 64 consecutive elements (one per lane) at the
-// LDS address held in M0; each lane chooses the global element it brings.
-constexpr int MBLK = 16;  // rows per m-block
-constexpr int SLAB_DX = MBLK * QK;   // 4096
-constexpr int SLAB_BS = SLAB_DX + 256;
-template <bool Q6>
-constexpr int slab_bytes() {
-  return Q6 ? SLAB_BS : SLAB_BS + MBLK * 8 * 4;
-}
-// buffer-to-LDS loads per step
-template <bool Q6, bool DEBUG>
-constexpr int dma_per_step() {
-  return 4 + (DEBUG ? 0 : 1) + (Q6 ? 0 : 2);
-}
-
+// Staging.  A step is one (16-row block, super-block) pair; its activation
+// record (codes, code sums, d_x: one quantized-activation record) is copied
+// verbatim into an LDS slab of the wave's own ring of R slabs, D = R - 1
+// steps ahead of its use, by five 1 KB loads.  The codes arrive already
+// swizzled (16-byte unit u of row r at unit u ^ r), so the fragment reads (16
+// lanes = 16 rows at one column unit) fall in 16 distinct bank groups.
+// Weight tiles go the same way into W slots, W super-blocks ahead.
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// Per-lane global offsets of the slab loads (relative to the step's bases).
-struct DmaLane {
-  int q[4];   // codes: load i brings rows 4i .. 4i+3
-  int dx;     // d_x of row lane % 16
-  int bs[2];  // code sums: load h brings rows 8h .. 8h+7
-};
+constexpr int MBLK = ACT_ROWS;  // rows per m-block
+constexpr int SLAB = ACT_RECORD;
+constexpr int GA = ACT_RECORD / 1024;  // loads per step
 
-__device__ inline DmaLane dma_lane(int lane, int K, int nb) {
-  DmaLane o;
+__device__ inline void dma_record(const i32x4 &d, uint32_t slab, int soff, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * i + (lane >> 4), u = lane & 15;
-    o.q[i] = r * K + 16 * (u ^ r);
-  }
-  o.dx = (lane & 15) * nb * 4;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) o.bs[h] = (8 * h + (lane >> 3)) * (K / 32) * 4 + 4 * (lane & 7);
-  return o;
-}
-
-// Loads of step (m-block at row m_base, super-block b) into the slab at LDS
-// address `slab`.  Each descriptor starts at the step's first row and ends
-// after its last valid row, so rows at or past M read as zeros.
-template <bool Q6, bool DEBUG>
-__device__ inline void dma_step(uint32_t slab, const int8_t *q, const float *dx,
-                                const int32_t *bsum, int M, int K, int nb, int m_base, int b,
-                                const DmaLane &dl) {
-  const int left = M - m_base;
-  const int rows = left <= 0 ? 0 : (left >= MBLK ? MBLK : left);
-  const i32x4 dq_ = desc(q + (int64_t)m_base * K + b * QK, rows ? rows * K - b * QK : 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(dq_, slab + 1024 * i, dl.q[i]);
-  if (!DEBUG) {
-    const i32x4 dd = desc(dx + (int64_t)m_base * nb + b, rows ? (rows * nb - b) * 4 : 0);
-    dma4(dd, slab + SLAB_DX, dl.dx);
-  }
-  if (!Q6) {
-    const i32x4 db =
-        desc(bsum + (int64_t)m_base * (K / 32) + 8 * b, rows ? (rows * (K / 32) - 8 * b) * 4 : 0);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) dma4(db, slab + SLAB_BS + 256 * h, dl.bs[h]);
-  }
+  for (int i = 0; i < GA; ++i) dma16(d, slab + 1024 * i, 1024 * i + 16 * lane, soff);
 }
 
 // Weight tile of one (n-tile, super-block) into an LDS slot: 1 KB loads for
-// the records, 256 B loads for the tail.  Q6_K: the 32 bytes of d are brought
-// by a 256 B load whose lane l reads d word l % 8.
+// the records, 256 B loads for the tail.  Q6_K's 288-byte tail (scales and
+// d) is brought by two overlapping 256 B loads (bytes 3072.. and 3104..);
+// where they overlap they write the same bytes.
 template <bool Q6>
 constexpr int wslot_bytes() {
-  return Q6 ? Q6K_D_OFF + 256 : Q4K_TILE;
+  return Q6 ? 3376 : Q4K_TILE;
 }
 template <bool Q6>
 constexpr int dma_per_tile() {
@@ -300,18 +246,17 @@ constexpr int dma_per_tile() {
 }
 
 template <bool Q6>
-__device__ inline void dma_tile(uint32_t slot, const uint8_t *tile, int lane) {
-  const i32x4 d = desc(tile, Q6 ? Q6K_TILE : Q4K_TILE);
+__device__ inline void dma_tile(const i32x4 &d, uint32_t slot, int soff, int lane) {
   if (!Q6) {
-    dma16(d, slot, 16 * lane);
-    dma16(d, slot + 1024, 1024 + 16 * lane);
-    dma4(d, slot + 2048, 2048 + 4 * lane);
+    dma16(d, slot, 16 * lane, soff);
+    dma16(d, slot + 1024, 1024 + 16 * lane, soff);
+    dma4(d, slot + 2048, 2048 + 4 * lane, soff);
   } else {
-    dma16(d, slot, 16 * lane);
-    dma16(d, slot + 1024, 1024 + 16 * lane);
-    dma16(d, slot + 2048, 2048 + 16 * lane);
-    dma4(d, slot + Q6K_SC_OFF, Q6K_SC_OFF + 4 * lane);
-    dma4(d, slot + Q6K_D_OFF, Q6K_D_OFF + 4 * (lane & 7));
+    dma16(d, slot, 16 * lane, soff);
+    dma16(d, slot + 1024, 1024 + 16 * lane, soff);
+    dma16(d, slot + 2048, 2048 + 16 * lane, soff);
+    dma4(d, slot + Q6K_SC_OFF, Q6K_SC_OFF + 4 * lane, soff);
+    dma4(d, slot + Q6K_TILE - 256, Q6K_TILE - 256 + 4 * lane, soff);
   }
 }
 
@@ -328,7 +273,7 @@ __device__ inline void step_mfma(const uint8_t *slab, const int (&frag)[4], int 
   i32x4 a[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) a[c] = *reinterpret_cast<const i32x4 *>(slab + frag[c]);
-  o.x4 = *reinterpret_cast<const f32x4 *>(slab + SLAB_DX + 16 * kq);
+  o.x4 = *reinterpret_cast<const f32x4 *>(slab + ACT_DX_OFF + 16 * kq);
   o.rl = i32x4{};
   o.rh = i32x4{};
 #pragma unroll
@@ -338,15 +283,9 @@ __device__ inline void step_mfma(const uint8_t *slab, const int (&frag)[4], int 
   }
   o.mnf = f32x4{};
   if (!Q6) {
-    // bsum = lo6 + rest: both exact in f16 (rest is a multiple of 64, |rest| <= 4096)
-    const uint2 bs = *reinterpret_cast<const uint2 *>(slab + SLAB_BS + 32 * col + 8 * kq);
-    f16x4 amin;
-    const int v0 = (int)bs.x, v1 = (int)bs.y;
-    const int l0 = v0 & 63, l1 = v1 & 63;
-    amin[0] = (_Float16)(short)l0;
-    amin[1] = (_Float16)(short)(v0 - l0);
-    amin[2] = (_Float16)(short)l1;
-    amin[3] = (_Float16)(short)(v1 - l1);
+    // the code sums of groups 2kq, 2kq+1 of row `col`, each as the exact
+    // binary16 pair (lo, hi), against (m, m) of the same groups
+    const f16x4 amin = *reinterpret_cast<const f16x4 *>(slab + ACT_SUMS_OFF + 32 * col + 8 * kq);
     o.mnf = __builtin_amdgcn_mfma_f32_16x16x16f16(amin, D.bmin, o.mnf, 0, 0, 0);
   }
 }
@@ -387,7 +326,7 @@ struct Shape {
 
 template <bool Q6, class SH>
 constexpr int wave_lds() {
-  return SH::R * slab_bytes<Q6>() + SH::W * wslot_bytes<Q6>();
+  return SH::R * SLAB + SH::W * wslot_bytes<Q6>();
 }
 template <bool Q6, class SH>
 constexpr int lds_bytes() {
@@ -415,9 +354,8 @@ constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 // loads may still be outstanding when the awaited one must have landed.
 template <int TYPE, class SH, int MODE>
 __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, int nb,
-                                                              const int8_t *__restrict__ q,
-                                                              const float *__restrict__ dx,
-                                                              const int32_t *__restrict__ bsum,
+                                                              const uint8_t *__restrict__ qa,
+                                                              uint32_t qa_bytes,
                                                               const uint8_t *__restrict__ packed,
                                                               float *__restrict__ y, int64_t ldy,
                                                               int32_t *__restrict__ dbg_S,
@@ -426,8 +364,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
   constexpr bool DEBUG = MODE == 2;
   constexpr int MB = SH::MB, R = SH::R, W = SH::W, D = R - 1;
   constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
-  constexpr int SLAB = slab_bytes<Q6>(), WSLOT = wslot_bytes<Q6>();
-  constexpr int GA = dma_per_step<Q6, DEBUG>(), GW = dma_per_tile<Q6>();
+  constexpr int WSLOT = wslot_bytes<Q6>();
+  constexpr int GW = dma_per_tile<Q6>();
   // loads issued after tile i when it is awaited: first W super-blocks, then steady state
   constexpr int WAIT_W0 = cap63((W - 1) * GW + D * GA);
   constexpr int WAIT_W = cap63((W - 1) * GW + W * MB * GA);
@@ -437,15 +375,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
   using Raw = typename std::conditional<Q6, RawQ6, RawQ4>::type;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<Q6, SH>()];
 
-  // the wave index is uniform across the wave; say so, so that every buffer
-  // descriptor and LDS address derived from it stays in scalar registers
+  // the wave index is uniform across the wave; say so, so that every scalar
+  // offset and LDS address derived from it stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int64_t nt = blockIdx.x;
-  const int m0 = (int)blockIdx.y * (MB * MBLK);
+  const int mb0 = (int)blockIdx.y * MB;  // first 16-row block of this workgroup
+  const int nmb = (M + MBLK - 1) / MBLK;
   const int64_t n = nt * TILE_N + col;
-  const int K = nb * QK;
   // this wave's LDS: R activation slabs, then W weight slots
   uint8_t *ring = lds + wave * wave_lds<Q6, SH>();
   uint8_t *wslots = ring + R * SLAB;
@@ -459,21 +397,23 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
   const int nbw = wave < nb ? (nb - wave + WAVES - 1) / WAVES : 0;  // this wave's super-blocks
   const int S = nbw * MB;                                           // and steps
   if (S > 0) {
-    const uint8_t *tiles = packed + nt * nb * TB;
-    const DmaLane dl = dma_lane(lane, K, nb);
+    const i32x4 dqa = desc(qa, qa_bytes);
+    const i32x4 dw = desc(packed + nt * nb * TB, (uint32_t)(nb * TB));
     int frag[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) frag[c] = col * QK + 16 * ((4 * kq + c) ^ col);
 
+    // step s -> record of (super-block wave + 4 * (s / MB), block mb0 + s % MB);
+    // blocks past the last one re-load the last (their rows are never stored)
     auto issue_a = [&](int s, int slot) {
       s = s < S ? s : S - 1;
       const int bi = s / MB, t = s - bi * MB;
-      dma_step<Q6, DEBUG>(ring_a + slot * SLAB, q, dx, bsum, M, K, nb, m0 + MBLK * t,
-                          wave + WAVES * bi, dl);
+      const int mb = mb0 + t < nmb ? mb0 + t : nmb - 1;
+      dma_record(dqa, ring_a + slot * SLAB, ((wave + WAVES * bi) * nmb + mb) * ACT_RECORD, lane);
     };
     auto issue_w = [&](int bi, int slot) {
       bi = bi < nbw ? bi : nbw - 1;
-      dma_tile<Q6>(wslots_a + slot * WSLOT, tiles + (int64_t)(wave + WAVES * bi) * TB, lane);
+      dma_tile<Q6>(dw, wslots_a + slot * WSLOT, (wave + WAVES * bi) * TB, lane);
     };
 #pragma unroll
     for (int i = 0; i < W; ++i) issue_w(i, i);
@@ -510,7 +450,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
         step_mfma<Q6>(ring + slot_use * SLAB, frag, col, kq, Dg, cur);
         slot_use = slot_use + 1 == R ? 0 : slot_use + 1;
         if (DEBUG)
-          step_debug<Q6>(cur, m0 + MBLK * t, kq, n, M, N, nb, b, dbg_S, dbg_Mn);
+          step_debug<Q6>(cur, (int64_t)(mb0 + t) * MBLK, kq, n, M, N, nb, b, dbg_S, dbg_Mn);
         else
           step_fold<Q6>(cur, Dg.dw, Dg.dmw, acc[t]);
       }
@@ -546,43 +486,43 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
     for (int t = 0; t < MB; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = m0 + MBLK * t + 4 * kq + i;
+        const int row = (mb0 + t) * MBLK + 4 * kq + i;
         if (row < M) y[(int64_t)row * ldy + n] = acc[t][i];
       }
   }
 }
 
 template <int TYPE, class SH>
-hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const int8_t *q, const float *d,
-                   const int32_t *bsum, const uint8_t *packed, float *y, int64_t ldy,
-                   int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream) {
-  dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N),
-            (unsigned)((M + MBLK * SH::MB - 1) / (MBLK * SH::MB)));
+hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
+                   const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn,
+                   hipStream_t stream) {
+  const int64_t nmb = (M + MBLK - 1) / MBLK;
+  dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N), (unsigned)((nmb + SH::MB - 1) / SH::MB));
   dim3 block(64 * WAVES);
   const int m = (int)M;
+  const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
   if (mode == 2)
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 2>), grid, block, 0, stream, m, N, nb, q, d, bsum,
+    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 2>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
                        packed, y, ldy, dbg_S, dbg_Mn);
   else if (mode == 1)
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 1>), grid, block, 0, stream, m, N, nb, q, d, bsum,
+    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 1>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
                        packed, y, ldy, dbg_S, dbg_Mn);
   else
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 0>), grid, block, 0, stream, m, N, nb, q, d, bsum,
+    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 0>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
                        packed, y, ldy, dbg_S, dbg_Mn);
   return hipGetLastError();
 }
 
 // Compiled variants, indexed by the number of 16-row m-blocks per workgroup.
 // Small MB (few steps per super-block) keeps more weight tiles in flight: the
-// weight stream is what the narrow GEMMs wait for.
-using V1 = Shape<1, 2, 3>;
-using V2 = Shape<2, 2, 3>;
-using V3 = Shape<3, 3, 2>;
-using V4 = Shape<4, 3, 2>;
-using V5 = Shape<5, 3, 1>;
-using V8 = Shape<8, 3, 1>;
-using V10 = Shape<10, 3, 1>;
-using V16 = Shape<16, 3, 1>;
+// weight stream is what the narrow GEMMs wait for.  Each shape keeps two
+// workgroups per CU within the 160 KB of LDS.
+template <int TYPE, int MB>
+struct ShapeOf {
+  static constexpr bool SMALL = TYPE == 14 ? MB <= 4 : MB <= 2;
+  static constexpr bool MID = TYPE == 12 && (MB == 3 || MB == 4);
+  using type = Shape<MB, SMALL ? 2 : 3, SMALL ? 3 : (MID ? 2 : 1)>;
+};
 constexpr int MB_SET[] = {16, 10, 8, 5, 4, 3, 2, 1};
 
 // Prefer the largest MB (weight digits are built once per MB steps) that
@@ -608,11 +548,13 @@ inline int pick_mb(int64_t M, int64_t N) {
 }
 
 template <int TYPE>
-hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const int8_t *q, const float *d,
-                       const int32_t *bsum, const uint8_t *packed, float *y, int64_t ldy,
-                       int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream) {
-#define DQ_MB(X) \
-  case X: return launch2<TYPE, V##X>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream)
+hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
+                       const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
+                       int32_t *dbg_Mn, hipStream_t stream) {
+#define DQ_MB(X)                                                                          \
+  case X:                                                                                 \
+    return launch2<TYPE, typename ShapeOf<TYPE, X>::type>(mode, M, N, nb, qa, packed, y, ldy, \
+                                                          dbg_S, dbg_Mn, stream)
   switch (pick_mb(M, N)) {
     DQ_MB(16);
     DQ_MB(10);
@@ -624,18 +566,19 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const int8_t *q, 
     default: break;
   }
 #undef DQ_MB
-  return launch2<TYPE, V1>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream);
+  return launch2<TYPE, typename ShapeOf<TYPE, 1>::type>(mode, M, N, nb, qa, packed, y, ldy, dbg_S,
+                                                        dbg_Mn, stream);
 }
 
 }  // namespace
 
-hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const int8_t *q,
-                        const float *d, const int32_t *bsum, const uint8_t *packed, float *y,
-                        int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn, hipStream_t stream) {
+hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
+                        const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
+                        int32_t *dbg_Mn, hipStream_t stream) {
   const int nb = (int)(K / QK);
   if (type == 12)
-    return launch_type<12>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream);
-  return launch_type<14>(mode, M, N, nb, q, d, bsum, packed, y, ldy, dbg_S, dbg_Mn, stream);
+    return launch_type<12>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+  return launch_type<14>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
 }
 
 }  // namespace dq

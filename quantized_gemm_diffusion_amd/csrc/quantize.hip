@@ -1,15 +1,17 @@
 // quantize.hip -- f32 activations -> int8 codes, one binary32 scale per 256
-// values, and int32 code sums per 32 (mojo-dllm "Architecture" page, "Source
-// map": activation quantization, int8 with one scale per 256).  The gathered
-// variant reads canvas row idx[m] for output row m ("A forward pass", steps
-// 3-4: only the requested positions reach the output projection).
+// values, and code sums per 32 (mojo-dllm "Architecture" page, "Source map":
+// activation quantization, int8 with one scale per 256), written in the
+// record layout the GEMM loads (documented in dq.h).  The gathered variant
+// reads canvas row idx[m] for output row m ("A forward pass", steps 3-4: only
+// the requested positions reach the output projection).
 //
-// One wave64 per (row, 256-block): each lane owns 4 consecutive values.  The
-// block's max |x| is reduced across the wave (max is exact in any order),
-// then every lane applies inv = 127/amax (IEEE division), rint (ties to even)
-// and a clamp to [-127, 127]; the 8 lanes of each 32-group sum their codes.
-// All arithmetic is binary32 with no contraction, so codes match any other
-// binary32 implementation of the same steps bit for bit.
+// One wave64 per (row, 256-block), rows padded to a multiple of 16: each lane
+// owns 4 consecutive values.  The block's max |x| is reduced across the wave
+// (max is exact in any order), then every lane applies inv = 127/amax (IEEE
+// division), rint (ties to even) and a clamp to [-127, 127]; the 8 lanes of
+// each 32-group sum their codes.  All arithmetic is binary32 with no
+// contraction, so codes match any other binary32 implementation of the same
+// steps bit for bit.  Padding rows (m >= M) write zeros.
 #include "dq_internal.h"
 
 // every step below is one binary32 operation; nothing may be fused
@@ -21,26 +23,29 @@ namespace {
 constexpr int WAVES_PER_BLOCK = 4;
 
 template <bool VEC, bool GATHER>
-__global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int nb, const float *__restrict__ x,
-                                                       int64_t ldx, const int32_t *__restrict__ idx,
-                                                       int64_t L, int8_t *__restrict__ q,
-                                                       float *__restrict__ d,
-                                                       int32_t *__restrict__ bsum,
+__global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, int nb,
+                                                       const float *__restrict__ x, int64_t ldx,
+                                                       const int32_t *__restrict__ idx,
+                                                       int64_t L, uint8_t *__restrict__ qa,
                                                        int32_t *__restrict__ err) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
-  if (item >= M * nb) return;  // whole wave exits together
+  if (item >= Mpad * nb) return;  // whole wave exits together
   const int64_t m = item / nb;
   const int b = (int)(item - m * nb);
-  const int64_t K = (int64_t)nb * QK;
+  const int64_t mb = m / ACT_ROWS;
+  const int r = (int)(m - mb * ACT_ROWS);
+  const int64_t nmb = Mpad / ACT_ROWS;
+  uint8_t *rec = qa + ((int64_t)b * nmb + mb) * ACT_RECORD;
 
   int64_t src = m;
-  bool valid = true;
-  if (GATHER) {
-    const int32_t r = idx[m];
-    valid = r >= 0 && (int64_t)r < L;
-    src = valid ? r : 0;
-    if (b == 0 && lane == 0) err[m] = valid ? 0 : 1;
+  bool valid = m < M;
+  if (GATHER && valid) {
+    const int32_t s = idx[m];
+    const bool in_range = s >= 0 && (int64_t)s < L;
+    if (b == 0 && lane == 0) err[m] = in_range ? 0 : 1;
+    valid = in_range;
+    src = in_range ? s : 0;
   }
 
   float v[4] = {0.f, 0.f, 0.f, 0.f};
@@ -69,47 +74,58 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int nb, const 
     const float inv = 127.0f / amax;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float r = __builtin_rintf(v[i] * inv);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      c[i] = (int)r;
+      float t = __builtin_rintf(v[i] * inv);
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      c[i] = (int)t;
     }
   }
-  const uint32_t packed = (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) |
-                          ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)(c[3] & 255) << 24);
-  *reinterpret_cast<uint32_t *>(q + m * K + (int64_t)b * QK + 4 * lane) = packed;
+  // codes: lane owns bytes 4*lane .. 4*lane+3, i.e. unit u = lane/4 of the row
+  const uint32_t word = (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) |
+                        ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)(c[3] & 255) << 24);
+  const int u = lane >> 2;
+  *reinterpret_cast<uint32_t *>(rec + r * QK + 16 * (u ^ r) + 4 * (lane & 3)) = word;
 
   int s = c[0] + c[1] + c[2] + c[3];
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);
   s += __shfl_xor(s, 4, 64);
-  if ((lane & 7) == 0) bsum[m * (K / 32) + (int64_t)b * 8 + (lane >> 3)] = s;
-  if (lane == 0) d[m * nb + b] = amax != 0.0f ? amax / 127.0f : 0.0f;
+  if ((lane & 7) == 0) {
+    // (lo, hi) = (s & 63, s - lo): both exact in binary16
+    const int lo = s & 63;
+    const _Float16 h[2] = {(_Float16)(float)lo, (_Float16)(float)(s - lo)};
+    *reinterpret_cast<uint32_t *>(rec + ACT_SUMS_OFF + r * 32 + 4 * (lane >> 3)) =
+        __builtin_bit_cast(uint32_t, h);
+  }
+  if (lane == 0)
+    *reinterpret_cast<float *>(rec + ACT_DX_OFF + 4 * r) = amax != 0.0f ? amax / 127.0f : 0.0f;
+  // the record's zero tail: 448 bytes, 28 per row
+  if (lane < 7) *reinterpret_cast<uint32_t *>(rec + ACT_PAD_OFF + 28 * r + 4 * lane) = 0u;
 }
 
 }  // namespace
 
 hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, const int32_t *idx,
-                           int64_t L, int8_t *q, float *d, int32_t *bsum, int32_t *err,
-                           hipStream_t stream) {
+                           int64_t L, uint8_t *qa, int32_t *err, hipStream_t stream) {
   const int nb = (int)(K / QK);
-  const int64_t items = M * nb;
+  const int64_t Mpad = (M + ACT_ROWS - 1) / ACT_ROWS * ACT_ROWS;
+  const int64_t items = Mpad * nb;
   const int64_t blocks = (items + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldx % 4 == 0);
   dim3 grid((unsigned)blocks), block(64 * WAVES_PER_BLOCK);
   if (idx) {
     if (vec)
-      hipLaunchKernelGGL((quantize_kernel<true, true>), grid, block, 0, stream, M, nb, x, ldx,
-                         idx, L, q, d, bsum, err);
+      hipLaunchKernelGGL((quantize_kernel<true, true>), grid, block, 0, stream, M, Mpad, nb, x,
+                         ldx, idx, L, qa, err);
     else
-      hipLaunchKernelGGL((quantize_kernel<false, true>), grid, block, 0, stream, M, nb, x, ldx,
-                         idx, L, q, d, bsum, err);
+      hipLaunchKernelGGL((quantize_kernel<false, true>), grid, block, 0, stream, M, Mpad, nb, x,
+                         ldx, idx, L, qa, err);
   } else {
     if (vec)
-      hipLaunchKernelGGL((quantize_kernel<true, false>), grid, block, 0, stream, M, nb, x, ldx,
-                         idx, L, q, d, bsum, err);
+      hipLaunchKernelGGL((quantize_kernel<true, false>), grid, block, 0, stream, M, Mpad, nb, x,
+                         ldx, idx, L, qa, err);
     else
-      hipLaunchKernelGGL((quantize_kernel<false, false>), grid, block, 0, stream, M, nb, x, ldx,
-                         idx, L, q, d, bsum, err);
+      hipLaunchKernelGGL((quantize_kernel<false, false>), grid, block, 0, stream, M, Mpad, nb, x,
+                         ldx, idx, L, qa, err);
   }
   return hipGetLastError();
 }

@@ -63,24 +63,35 @@ def test_host_checks_return_codes(lib):
     assert lib.dq_packed_size(dq.Q4_K, -1, 256, ctypes.byref(out)) == dq.DQ_EINVAL
     assert lib.dq_packed_size(dq.Q4_K, 32, 256, None) == dq.DQ_EINVAL
     # NULL device pointers are refused before any launch
-    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 256, None, None, None, None, None, 32, None) == dq.DQ_EINVAL
-    assert lib.dq_qgemm(15, 4, 32, 256, None, None, None, None, None, 32, None) == dq.DQ_EUNSUPPORTED
-    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 16, 16, 16, 16, 16, 31, None) == dq.DQ_EINVAL  # ldy < N
-    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 16, 16, None, 16, 16, 32, None) == dq.DQ_EINVAL  # Q4_K needs bsum
-    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 8, 16, 16, 16, 16, 32, None) == dq.DQ_EINVAL  # q misaligned
-    assert lib.dq_quantize_act(4, 512, 16, 500, 16, 16, 16, None) == dq.DQ_EINVAL  # ldx < K
-    assert lib.dq_quantize_act(4, 100, 16, 100, 16, 16, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 256, None, None, None, 32, None) == dq.DQ_EINVAL
+    assert lib.dq_qgemm(15, 4, 32, 256, None, None, None, 32, None) == dq.DQ_EUNSUPPORTED
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 16, 16, 16, 31, None) == dq.DQ_EINVAL  # ldy < N
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 8, 16, 16, 32, None) == dq.DQ_EINVAL  # qa misaligned
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, 16, 16, None, 32, None) == dq.DQ_EINVAL  # y NULL
+    assert lib.dq_quantize_act(4, 512, 16, 500, 16, None) == dq.DQ_EINVAL  # ldx < K
+    assert lib.dq_quantize_act(4, 100, 16, 100, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_quantize_act(4, 512, 16, 512, 8, None) == dq.DQ_EINVAL  # qa misaligned
     assert lib.dq_repack_weights(dq.Q6_K, 32, 256, None, 16, None) == dq.DQ_EINVAL
     assert lib.dq_repack_weights(dq.Q6_K, 32, 256, 16, 8, None) == dq.DQ_EINVAL  # packed misaligned
+    assert lib.dq_act_size(1 << 20, 1 << 14, ctypes.byref(out)) == dq.DQ_EINVAL  # > 2^31 bytes
     # empty shapes are valid no-ops
-    assert lib.dq_qgemm(dq.Q4_K, 0, 32, 256, None, None, None, None, None, 32, None) == dq.DQ_OK
-    assert lib.dq_quantize_act(0, 256, None, 256, None, None, None, None) == dq.DQ_OK
+    assert lib.dq_qgemm(dq.Q4_K, 0, 32, 256, None, None, None, 32, None) == dq.DQ_OK
+    assert lib.dq_quantize_act(0, 256, None, 256, None, None) == dq.DQ_OK
+
+
+@pytest.mark.parametrize("M,K,exp", [
+    (160, 4096, 10 * 16 * 5120),
+    (1, 256, 5120),
+    (17, 512, 2 * 2 * 5120),     # rows rounded up to blocks of 16
+    (0, 256, 0),
+])
+def test_act_size(lib, M, K, exp):
+    assert dq.act_size(M, K) == exp
 
 
 def test_rows_workspace(lib):
     need = dq.qgemm_rows_workspace(32, 4096)
-    assert need >= 32 * 4 + 32 * 4096 + 32 * 16 * 4 + 32 * 128 * 4
-    assert need % 256 == 0
+    assert need == 256 + dq.act_size(32, 4096)  # flags, then the activation records
     # short workspace -> DQ_EWORKSPACE, before anything is launched
     st = lib.dq_qgemm_rows(dq.Q6_K, 160, 32, 126464, 4096, 256, 4096, 256, 256, 256, 126464,
                            256, need - 1, None)

@@ -11,6 +11,7 @@ be finite.
 import numpy as np
 import pytest
 
+import act_layout
 import oracle
 import synth
 
@@ -50,11 +51,12 @@ def _sampled_check(type_, xq, xd, W, y, seed, what):
 def _run_set(dq, layers, M, K_act, seed0):
     x = synth.activations(np.random.default_rng(seed0), M, K_act)
     xq, xd, xb = oracle.quantize_act(x)
-    q, d, b = dq.quantize_act(_t(x))
-    torch.cuda.synchronize()
-    assert np.array_equal(q.cpu().numpy(), xq) and np.array_equal(b.cpu().numpy(), xb)
-    assert np.array_equal(d.cpu().numpy(), xd)
-    return x, (xq, xd, xb), (q, d, b)
+    act = dq.quantize_act(_t(x))
+    q, d, b, padding_ok = act_layout.unpack(act.buf.cpu().numpy(), M, K_act)
+    assert padding_ok
+    assert np.array_equal(q, xq) and np.array_equal(b, xb)
+    assert np.array_equal(d, xd)
+    return x, (xq, xd, xb), act
 
 
 @pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
@@ -64,9 +66,9 @@ def test_llada_projection_full_size(dq, name):
     M = synth.LLADA["L"]
     W = synth.weights(np.random.default_rng(synth.seed(1, 1, ["q", "k", "v", "o", "gate", "up",
                                                               "down"].index(name))), type_, N, K)
-    _, (xq, xd, xb), (q, d, b) = _run_set(dq, None, M, K, 1000 + K)
+    _, (xq, xd, xb), act = _run_set(dq, None, M, K, 1000 + K)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    y = dq.qgemm(type_, q, d, b, packed, N).cpu().numpy()
+    y = dq.qgemm(type_, act, packed, N).cpu().numpy()
     _sampled_check(type_, xq, xd, W, y, 7, f"LLaDA {name}")
 
 
@@ -77,9 +79,9 @@ def test_dream_projection_full_size(dq, name):
     M = synth.DREAM["L"]
     W = synth.weights(np.random.default_rng(synth.seed(4, 0, ["q", "k", "v", "o", "gate", "up",
                                                               "down"].index(name))), type_, N, K)
-    _, (xq, xd, xb), (q, d, b) = _run_set(dq, None, M, K, 4000 + K)
+    _, (xq, xd, xb), act = _run_set(dq, None, M, K, 4000 + K)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    y = dq.qgemm(type_, q, d, b, packed, N).cpu().numpy()
+    y = dq.qgemm(type_, act, packed, N).cpu().numpy()
     _sampled_check(type_, xq, xd, W, y, 8, f"Dream {name}")
 
 

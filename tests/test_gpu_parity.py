@@ -14,6 +14,7 @@ import synth
 from kq_fields import (encode_q4k_matrix, encode_q6k_matrix, random_q4k_fields,
                        random_q6k_fields)
 from packed_layout import ROWS, TILE, read_tile
+import act_layout
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -41,6 +42,18 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def _act(dq, xq, xd, xb):
+    """Oracle-quantized activations in the library's record layout, on the GPU."""
+    M, K = xq.shape
+    return dq.Act(_t(act_layout.pack(xq, xd, xb)), M, K)
+
+
+def _unpack(act):
+    q, d, b, padding_ok = act_layout.unpack(act.buf.cpu().numpy(), act.M, act.K)
+    assert padding_ok, "padding rows or record tails are not zero"
+    return q, d, b
+
+
 def _weights(type_, N, K, seed, full_scales=False):
     rng = np.random.default_rng(seed)
     if type_ == oracle.Q4_K:
@@ -66,12 +79,11 @@ def test_quantize_bit_exact(dq, M, K, seed):
     x[0, :256] = 0.0  # a zero block
     if M > 1:
         x[1, 256 % K:256 % K + 3] = [254.0, 3.0, -5.0]  # halfway ties
-    q, d, b = dq.quantize_act(_t(x))
-    _sync()
+    q, d, b = _unpack(dq.quantize_act(_t(x)))
     xq, xd, xb = oracle.quantize_act(x)
-    assert np.array_equal(q.cpu().numpy(), xq)
-    assert np.array_equal(d.cpu().numpy().view(np.uint32), xd.view(np.uint32))
-    assert np.array_equal(b.cpu().numpy(), xb)
+    assert np.array_equal(q, xq)
+    assert np.array_equal(d.view(np.uint32), xd.view(np.uint32))
+    assert np.array_equal(b, xb)
 
 
 def test_quantize_strided_and_unaligned_rows(dq):
@@ -79,10 +91,9 @@ def test_quantize_strided_and_unaligned_rows(dq):
     big = synth.activations(rng, 9, 1024 + 65)
     xq, xd, xb = oracle.quantize_act(np.ascontiguousarray(big[:, 1:1025]))
     xt = _t(big)
-    q, d, b = dq.quantize_act(xt[:, 1:1025])  # row stride 1089, start off 16-byte alignment
-    _sync()
-    assert np.array_equal(q.cpu().numpy(), xq) and np.array_equal(b.cpu().numpy(), xb)
-    assert np.array_equal(d.cpu().numpy(), xd)
+    q, d, b = _unpack(dq.quantize_act(xt[:, 1:1025]))  # row stride 1089, off 16-byte alignment
+    assert np.array_equal(q, xq) and np.array_equal(b, xb)
+    assert np.array_equal(d, xd)
 
 
 # --------------------------------------------------------------------------- #
@@ -130,7 +141,7 @@ def test_superblock_sums_bit_exact(dq, type_, M, N, K):
     x = synth.activations(np.random.default_rng(60 + M), M, K)
     xq, xd, xb = oracle.quantize_act(x)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    S, Mn = dq.debug_superblock_sums(type_, _t(xq), _t(xb), packed, N)
+    S, Mn = dq.debug_superblock_sums(type_, _act(dq, xq, xd, xb), packed, N)
     _sync()
     oS, oMn = oracle.superblock_sums(type_, xq, xb, W, N)
     assert np.array_equal(S.cpu().numpy(), oS)
@@ -155,7 +166,7 @@ def test_subblock_dots_bit_exact(dq, type_):
         fj["sc"][..., j] = 1
         Wj = encode_q4k_matrix(fj) if type_ == oracle.Q4_K else encode_q6k_matrix(fj)
         packed = dq.repack_weights(type_, N, K, _t(Wj.reshape(-1)))
-        S, _ = dq.debug_superblock_sums(type_, _t(xq), _t(xb), packed, N)
+        S, _ = dq.debug_superblock_sums(type_, _act(dq, xq, xd, xb), packed, N)
         _sync()
         assert np.array_equal(S.cpu().numpy(), dots[..., j]), f"sub-block {j}"
 
@@ -171,7 +182,7 @@ def test_qgemm_within_tolerance(dq, type_, M, N, K):
     x = synth.activations(np.random.default_rng(90 + M), M, K)
     xq, xd, xb = oracle.quantize_act(x)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    y = dq.qgemm(type_, _t(xq), _t(xd), _t(xb), packed, N)
+    y = dq.qgemm(type_, _act(dq, xq, xd, xb), packed, N)
     _sync()
     yr, T = oracle.qgemm_ref(type_, xq, xd, W, N)
     _check_tol(y.cpu().numpy(), yr, T, f"type {type_} {M}x{N}x{K}")
@@ -183,7 +194,7 @@ def test_qgemm_strided_output_untouched_padding(dq):
     xq, xd, xb = oracle.quantize_act(synth.activations(np.random.default_rng(4), M, K))
     packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
     ybig = torch.full((M, N + 9), -7.0, device=DEV)
-    dq.qgemm(oracle.Q4_K, _t(xq), _t(xd), _t(xb), packed, N, y=ybig)
+    dq.qgemm(oracle.Q4_K, _act(dq, xq, xd, xb), packed, N, y=ybig)
     _sync()
     yb = ybig.cpu().numpy()
     assert np.all(yb[:, N:] == -7.0)
@@ -196,12 +207,12 @@ def test_qgemm_deterministic_and_power_of_two_scaling(dq):
     W = _weights(oracle.Q6_K, N, K, 5)
     x = synth.activations(np.random.default_rng(6), M, K)
     packed = dq.repack_weights(oracle.Q6_K, N, K, _t(W.reshape(-1)))
-    q, d, b = dq.quantize_act(_t(x))
-    y1 = dq.qgemm(oracle.Q6_K, q, d, b, packed, N).cpu().numpy()
-    y2 = dq.qgemm(oracle.Q6_K, q, d, b, packed, N).cpu().numpy()
+    a = dq.quantize_act(_t(x))
+    y1 = dq.qgemm(oracle.Q6_K, a, packed, N).cpu().numpy()
+    y2 = dq.qgemm(oracle.Q6_K, a, packed, N).cpu().numpy()
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
-    q3, d3, b3 = dq.quantize_act(_t(x * np.float32(2.0 ** -5)))
-    y3 = dq.qgemm(oracle.Q6_K, q3, d3, b3, packed, N).cpu().numpy()
+    a3 = dq.quantize_act(_t(x * np.float32(2.0 ** -5)))
+    y3 = dq.qgemm(oracle.Q6_K, a3, packed, N).cpu().numpy()
     assert np.array_equal(y3, y1 * np.float32(2.0 ** -5))
 
 
@@ -209,8 +220,8 @@ def test_zero_activations_give_zero(dq):
     M, N, K = 20, 64, 512
     W = _weights(oracle.Q4_K, N, K, 8)
     packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
-    q, d, b = dq.quantize_act(torch.zeros((M, K), device=DEV))
-    y = dq.qgemm(oracle.Q4_K, q, d, b, packed, N).cpu().numpy()
+    a = dq.quantize_act(torch.zeros((M, K), device=DEV))
+    y = dq.qgemm(oracle.Q4_K, a, packed, N).cpu().numpy()
     assert np.all(y == 0.0)
 
 
@@ -232,8 +243,7 @@ def test_rows_gather_matches_quantized_gemm(dq):
     assert np.array_equal(yn[2], yn[3])  # duplicate index, identical row
     assert not ws[: 4 * len(idx)].view(torch.int32).cpu().numpy().any()
     # gather-then-quantize equals quantize-then-gather, bit for bit
-    q, d, b = dq.quantize_act(_t(canvas))
-    yall = dq.qgemm(oracle.Q6_K, q, d, b, packed, N).cpu().numpy()
+    yall = dq.qgemm(oracle.Q6_K, dq.quantize_act(_t(canvas)), packed, N).cpu().numpy()
     assert np.array_equal(yn.view(np.uint32), yall[idx].view(np.uint32))
     # permuting idx permutes the rows
     perm = np.array([3, 5, 0, 1, 2, 4])
@@ -262,15 +272,21 @@ def test_rows_out_of_range_index_is_flagged_not_read(dq):
 # ABI errors through the binding on the GPU                                   #
 # --------------------------------------------------------------------------- #
 def test_abi_errors_on_gpu(dq):
-    q = torch.zeros((4, 512), dtype=torch.int8, device=DEV)
-    d = torch.zeros((4, 2), dtype=torch.float32, device=DEV)
-    b = torch.zeros((4, 16), dtype=torch.int32, device=DEV)
+    act = dq.quantize_act(torch.zeros((4, 512), device=DEV))
     packed = torch.zeros(dq.packed_size(dq.Q4_K, 32, 512), dtype=torch.uint8, device=DEV)
     with pytest.raises(ValueError):
-        dq.qgemm(dq.Q4_K, q, d, b, packed[:-1], 32)  # packed too small
-    with pytest.raises(dq.DQError) as e:
-        dq.qgemm(dq.Q4_K, q, d, None, packed, 32)
-    assert e.value.status == dq.DQ_EINVAL
+        dq.qgemm(dq.Q4_K, act, packed[:-1], 32)  # packed too small
+    with pytest.raises(ValueError):
+        dq.qgemm(dq.Q4_K, dq.Act(act.buf[:-16], 4, 512), packed, 32)  # activations too small
+    lib = dq.load_library()
+    y = torch.zeros((4, 32), device=DEV)
+    sp = torch.cuda.current_stream().cuda_stream
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 500, act.buf.data_ptr(), packed.data_ptr(),
+                        y.data_ptr(), 32, sp) == dq.DQ_EINVAL  # K not a multiple of 256
+    assert lib.dq_qgemm(dq.Q4_K, 4, 32, 512, act.buf.data_ptr() + 4, packed.data_ptr(),
+                        y.data_ptr(), 32, sp) == dq.DQ_EINVAL  # misaligned activations
+    assert lib.dq_qgemm(7, 4, 32, 512, act.buf.data_ptr(), packed.data_ptr(),
+                        y.data_ptr(), 32, sp) == dq.DQ_EUNSUPPORTED
     canvas = torch.zeros((8, 512), device=DEV)
     idx = torch.zeros(4, dtype=torch.int32, device=DEV)
     with pytest.raises(dq.DQError) as e:
@@ -280,22 +296,22 @@ def test_abi_errors_on_gpu(dq):
 
 
 # --------------------------------------------------------------------------- #
-# Every m-tiling of the GEMM (the launcher picks 1..5 m-tiles per workgroup   #
-# from M and N): shapes chosen so that each choice is exercised               #
+# m-tilings of the GEMM (the launcher picks the 16-row blocks per workgroup   #
+# from M and N): shapes chosen so that several choices are exercised          #
 # --------------------------------------------------------------------------- #
 @pytest.mark.parametrize("type_,M,N,K", [
-    (oracle.Q4_K, 160, 8192, 512),    # 5 m-tiles per workgroup
-    (oracle.Q6_K, 128, 8200, 512),    # 4, ragged N
-    (oracle.Q4_K, 96, 8192, 1280),    # 3, 5 super-blocks over 4 waves
-    (oracle.Q6_K, 64, 8192, 256),     # 2, a single super-block
-    (oracle.Q4_K, 150, 8224, 768),    # 5 with a ragged last m-tile
+    (oracle.Q4_K, 160, 8192, 512),    # 10 blocks of 16 rows in 2 workgroup rows
+    (oracle.Q6_K, 128, 8200, 512),    # ragged N
+    (oracle.Q4_K, 96, 8192, 1280),    # 5 super-blocks over 4 waves
+    (oracle.Q6_K, 64, 8192, 256),     # a single super-block
+    (oracle.Q4_K, 150, 8224, 768),    # a ragged last 16-row block
 ])
 def test_qgemm_every_m_tiling(dq, type_, M, N, K):
     W = _weights(type_, N, K, 300 + M, full_scales=True)
     x = synth.activations(np.random.default_rng(400 + M), M, K)
     xq, xd, xb = oracle.quantize_act(x)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    y = dq.qgemm(type_, _t(xq), _t(xd), _t(xb), packed, N)
+    y = dq.qgemm(type_, _act(dq, xq, xd, xb), packed, N)
     _sync()
     yr, T = oracle.qgemm_ref(type_, xq, xd, W, N)
     _check_tol(y.cpu().numpy(), yr, T, f"type {type_} {M}x{N}x{K}")
@@ -308,7 +324,7 @@ def test_superblock_sums_bit_exact_multi_tile(dq, type_, M):
     x = synth.activations(np.random.default_rng(600 + M), M, K)
     xq, xd, xb = oracle.quantize_act(x)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    S, Mn = dq.debug_superblock_sums(type_, _t(xq), _t(xb), packed, N)
+    S, Mn = dq.debug_superblock_sums(type_, _act(dq, xq, xd, xb), packed, N)
     _sync()
     oS, oMn = oracle.superblock_sums(type_, xq, xb, W, N)
     assert np.array_equal(S.cpu().numpy(), oS)
