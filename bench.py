@@ -8,12 +8,16 @@ pass"): for each of 32 layers, 4 activation quantizations (Q/K/V share one,
 O, gate/up share one, down) and the 7 projections Q, K, V, O (4096 x 4096
 Q4_K), gate, up (12288 x 4096 Q4_K) and down (4096 x 12288; Q6_K on odd
 layers, Q4_K on even), then the output projection on 32 gathered canvas rows
-(126,464 x 4096 Q6_K).  Every layer has its own seeded weights (4.6 GB in
-all, far above the 256 MB last-level cache), resident in HBM before timing.
+(126,464 x 4096 Q6_K).  Q, K and V read the same quantized input, so their
+weights are stacked at load time into one 12,288 x 4096 matrix and run as one
+GEMM (same bytes and operations, two launches fewer per layer).  Every layer
+has its own seeded weights (4.6 GB in all, far above the 256 MB last-level
+cache), resident in HBM before timing.
 
-Prints one JSON line: whole-step TOPS (value), HBM GB/s, the roofline of the
-dominant kernel measured with HIP events around its launches inside the timed
-region, and the CPU oracle timed on a bounded sample of the same workload.
+The timed steps replay the step captured as one HIP graph.  Prints one JSON
+line: whole-step TOPS (value), HBM GB/s, the roofline of the dominant kernel
+measured with HIP events around each of its launches (eager steps on the same
+stream), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -50,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--cpu-layers", type=int, default=6,
+    p.add_argument("--cpu-layers", type=int, default=16,
                    help="layers of the step the CPU oracle baseline runs on")
     p.add_argument("--cpu-threads", type=int, default=min(os.cpu_count() or 1, 16))
     p.add_argument("--no-cpu-baseline", action="store_true",
@@ -116,13 +120,18 @@ def main():
             "down": up(synth.activations(act_rng, L, F))}
     qbuf = {kk: torch.empty(dq.act_size(L, kk), dtype=torch.uint8, device=dev) for kk in (K, F)}
     outs = {name: torch.empty((L, N), dtype=torch.float32, device=dev)
-            for name, _, N, _ in synth.llada_layer(1)}
+            for name, N in (("qkv", 3 * K), ("o", K), ("gate", F), ("up", F), ("down", K))}
     host_keep = {}
     packed = []
     for layer in range(LAYERS):
-        lp = {}
+        mats = {}
         for p, (name, t, N, KK) in enumerate(synth.llada_layer(layer)):
-            W = synth.weights(np.random.default_rng(synth.seed(2, layer, p)), t, N, KK)
+            mats[name] = (t, N, KK, synth.weights(np.random.default_rng(synth.seed(2, layer, p)),
+                                                  t, N, KK))
+        # Q, K, V stacked along N: one 12288 x 4096 Q4_K matrix
+        mats["qkv"] = (Q4_K, 3 * K, K, np.concatenate([mats.pop(n)[3] for n in "qkv"]))
+        lp = {}
+        for name, (t, N, KK, W) in mats.items():
             if layer < args.cpu_layers:
                 host_keep[(layer, name)] = W
             g = up(W.reshape(-1))
@@ -146,22 +155,20 @@ def main():
         x = acts[name]
         kk = x.shape[1]
         buf = qbuf[kk]
-        calls.append((lib.dq_quantize_act, (L, kk, x.data_ptr(), kk, buf.data_ptr(), sp),
+        calls.append((lib.dq_quantize_act, (L, kk, x.data_ptr(), kk, buf.data_ptr()),
                       "quantize", 0, quant_bytes(L, kk)))
         return buf
 
     def gemm(lp, name, buf):
         t, N, kk, pk = lp[name]
         y = outs[name]
-        calls.append((lib.dq_qgemm, (t, L, N, kk, buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N,
-                                     sp),
-                      f"qgemm_{'q4k' if t == Q4_K else 'q6k'}", 2 * L * N * kk,
-                      gemm_bytes(t, L, N, kk)))
+        # one kind per GEMM shape: each kind is one kernel in a profile
+        kind = f"qgemm_{'q4k' if t == Q4_K else 'q6k'}_{L}x{N}x{kk}"
+        calls.append((lib.dq_qgemm, (t, L, N, kk, buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N),
+                      kind, 2 * L * N * kk, gemm_bytes(t, L, N, kk)))
 
     for lp in packed:
-        a = quant("qkv")
-        for n in ("q", "k", "v"):
-            gemm(lp, n, a)
+        gemm(lp, "qkv", quant("qkv"))
         gemm(lp, "o", quant("o"))
         a = quant("ffn")
         for n in ("gate", "up"):
@@ -171,36 +178,37 @@ def main():
     rows_bytes = V * (K // 256) * BLOCK[Q6_K] + ROWS * K * 4 + ROWS * 4 + ROWS * V * 4
     calls.append((lib.dq_qgemm_rows,
                   (Q6_K, L, ROWS, V, K, canvas.data_ptr(), K, idx.data_ptr(),
-                   out_packed.data_ptr(), logits.data_ptr(), V, ws.data_ptr(), ws.numel(), sp),
+                   out_packed.data_ptr(), logits.data_ptr(), V, ws.data_ptr(), ws.numel()),
                   "rows", 2 * ROWS * V * K, rows_bytes))
     step_ops = sum(c[3] for c in calls)
     step_bytes = sum(c[4] for c in calls)
 
-    def run_calls(brackets=None, kind=None):
-        """Launch one step; optionally record events around each launch of `kind`."""
+    def run_calls(sh, brackets=None, kind=None):
+        """Launch one step on stream handle sh; optionally record events around each
+        launch of `kind` (on the same stream)."""
         for fn, a, k, _, _ in calls:
             if brackets is not None and k == kind:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                rc = fn(*a)
+                rc = fn(*a, sh)
                 e1.record(stream)
                 brackets.append((e0, e1))
             else:
-                rc = fn(*a)
+                rc = fn(*a, sh)
             if rc:
                 raise RuntimeError(f"{fn.__name__}: {lib.dq_last_error().decode()}")
 
     # ------------------------------------------------------ warmup, calibrate
     for _ in range(args.warmup):
-        run_calls()
+        run_calls(sp)
     torch.cuda.synchronize()
     per_kind = {}
     evs = []
     for fn, a, k, ops, nbytes in calls:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        fn(*a)
+        fn(*a, sp)
         e1.record(stream)
         evs.append((k, e0, e1, ops, nbytes))
     torch.cuda.synchronize()
@@ -217,15 +225,43 @@ def main():
                for k, v in per_kind.items()}
     log("per-kind (isolated launches):", json.dumps(kernels))
 
+    # ------------------------------------------ the step as one HIP graph
+    # The step's 321 launches are captured once and replayed: the host then
+    # issues one launch per step instead of one per kernel.  The replay is
+    # checked against the eager step (both deterministic) before timing.
+    ref = {n: outs[n].clone() for n in ("qkv", "down")}
+    ref["logits"] = logits.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_calls(torch.cuda.current_stream().cuda_stream)
+    for t in list(outs.values()) + [logits]:
+        t.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    got = {"qkv": outs["qkv"], "down": outs["down"], "logits": logits}
+    for n, t in got.items():
+        if not torch.equal(t, ref[n]):
+            raise RuntimeError(f"graph replay differs from the eager step in {n}")
+
     # ------------------------------------------------------------- timed run
-    brackets = []
+    for _ in range(2):
+        graph.replay()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        run_calls(brackets, dominant)
+        graph.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = 1e3 * elapsed / args.steps
+
+    # --------------------------------- dominant kernel, launch by launch
+    # HIP events around every launch of the dominant kernel, on its stream,
+    # over the same number of eager steps.
+    brackets = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        run_calls(sp, brackets, dominant)
+    torch.cuda.synchronize()
     dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in brackets)
     dom_launches = per_kind[dominant][0] * args.steps
     dom_bytes = per_kind[dominant][3] / per_kind[dominant][0]  # per launch (average)
@@ -269,6 +305,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(dom_bytes),
                      "ops_per_launch": int(dom_ops), "launches": dom_launches},
         "kernels_isolated": kernels,
+        "step_timing": "HIP graph replay of the step's 321 launches",
         "device": torch.cuda.get_device_properties(dev).name,
     }
 
@@ -288,13 +325,15 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
     t0 = time.perf_counter()
     for layer in range(args.cpu_layers):
         quantized = {}
-        for p, (name, t, N, KK) in enumerate(synth.llada_layer(layer)):
-            src = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "ffn", "up": "ffn",
-                   "down": "down"}[name]
+        for name in ("qkv", "o", "gate", "up", "down"):
+            W = host_keep[(layer, name)]
+            t = Q6_K if W.shape[-1] == 210 else Q4_K
+            N, KK = W.shape[0], W.shape[1] * 256
+            src = {"qkv": "qkv", "o": "o", "gate": "ffn", "up": "ffn", "down": "down"}[name]
             if src not in quantized:
                 quantized[src] = oracle.quantize_act(xs[src])
             q, d, b = quantized[src]
-            oracle.qgemm_f32(t, q, d, b, host_keep[(layer, name)], N, threads=th)
+            oracle.qgemm_f32(t, q, d, b, W, N, threads=th)
             ops += 2 * L * N * KK
     nv = V // 4
     gq, gd, gb = oracle.qgemm_rows_inputs(canvas_np, idx_np)
@@ -303,7 +342,7 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
     dt = time.perf_counter() - t0
     return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": th, "kind": "oracle",
             "sample": f"oracle quantize + integer-decomposition GEMM on {args.cpu_layers} of 32 "
-                      f"layers (all 7 projections, L=160) and 1/4 of the 126464 vocab rows at "
+                      f"layers (all projections, L=160) and 1/4 of the 126464 vocab rows at "
                       f"M=32: {ops / 1e9:.1f} GOP in {dt:.1f} s"}
 
 

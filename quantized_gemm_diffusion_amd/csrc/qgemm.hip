@@ -274,6 +274,11 @@ __device__ inline void step_mfma(const uint8_t *slab, const int (&frag)[4], int 
 #pragma unroll
   for (int c = 0; c < 4; ++c) a[c] = *reinterpret_cast<const i32x4 *>(slab + frag[c]);
   o.x4 = *reinterpret_cast<const f32x4 *>(slab + ACT_DX_OFF + 16 * kq);
+  f16x4 amin = {};
+  if (!Q6) amin = *reinterpret_cast<const f16x4 *>(slab + ACT_SUMS_OFF + 32 * col + 8 * kq);
+  // issue every read of this slab here, a step before the slab is refilled,
+  // so the refill's wait for outstanding LDS reads finds them done
+  asm volatile("" ::: "memory");
   o.rl = i32x4{};
   o.rh = i32x4{};
 #pragma unroll
@@ -285,7 +290,6 @@ __device__ inline void step_mfma(const uint8_t *slab, const int (&frag)[4], int 
   if (!Q6) {
     // the code sums of groups 2kq, 2kq+1 of row `col`, each as the exact
     // binary16 pair (lo, hi), against (m, m) of the same groups
-    const f16x4 amin = *reinterpret_cast<const f16x4 *>(slab + ACT_SUMS_OFF + 32 * col + 8 * kq);
     o.mnf = __builtin_amdgcn_mfma_f32_16x16x16f16(amin, D.bmin, o.mnf, 0, 0, 0);
   }
 }
@@ -316,17 +320,16 @@ __device__ inline void step_debug(const StepOut &o, int64_t row0, int kq, int64_
 
 constexpr int WAVES = 4;
 
-// Launch shape of one GEMM variant: MB 16-row m-blocks per workgroup, R
-// activation slabs per wave (prefetch distance R - 1 steps) and W weight
-// slots per wave (weights W super-blocks ahead).
-template <int MB_, int R_, int W_>
+// Launch shape of one GEMM variant: MB 16-row m-blocks per workgroup and R
+// activation slabs per wave (prefetch distance R - 1 steps).
+template <int MB_, int R_>
 struct Shape {
-  static constexpr int MB = MB_, R = R_, W = W_;
+  static constexpr int MB = MB_, R = R_;
 };
 
 template <bool Q6, class SH>
 constexpr int wave_lds() {
-  return SH::R * SLAB + SH::W * wslot_bytes<Q6>();
+  return SH::R * SLAB + wslot_bytes<Q6>();
 }
 template <bool Q6, class SH>
 constexpr int lds_bytes() {
@@ -343,11 +346,17 @@ constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 // the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its own
 // symbol so profiles tell the two workloads apart), 2 = debug stores of S, Mn.
 //
-// Load schedule of one wave (every load is a buffer-to-LDS load):
-//   prologue      : tiles of super-blocks 0 .. W-1, slabs of steps 0 .. D-1
-//   super-block i : wait for tile i; digits; refill its slot with tile i + W
+// Load schedule of one wave (every load is a buffer-to-LDS load, and loads
+// complete in issue order, so a wait for one load also waits for every older
+// one):
+//   prologue      : tile of super-block 0, slabs of steps 0 .. D-1
+//   super-block i : wait for tile i; digits
 //     step s      : refill the slab read by step s - 1 with step s + D;
+//                   at step TW = max(0, MB - D - 1) of the super-block, also
+//                   refill the tile slot with tile i + 1;
 //                   wait for step s; MFMAs; fold
+// The tile load is issued as late as its latency allows: the first wait that
+// covers it is the one for the next super-block's tile, D + 1 steps later.
 // Loads past the wave's last tile or step repeat the last one (valid memory
 // into a slot nobody reads again), so the number of loads issued after any
 // given load is fixed, and each wait is a constant vmcnt: at most that many
@@ -362,15 +371,14 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
                                                               int32_t *__restrict__ dbg_Mn) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
-  constexpr int MB = SH::MB, R = SH::R, W = SH::W, D = R - 1;
+  constexpr int MB = SH::MB, R = SH::R, D = R - 1;
   constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
-  constexpr int WSLOT = wslot_bytes<Q6>();
   constexpr int GW = dma_per_tile<Q6>();
-  // loads issued after tile i when it is awaited: first W super-blocks, then steady state
-  constexpr int WAIT_W0 = cap63((W - 1) * GW + D * GA);
-  constexpr int WAIT_W = cap63((W - 1) * GW + W * MB * GA);
-  constexpr int WAIT_A = D * GA;
-  static_assert(R >= 2 && WAIT_A < 64 && W >= 1, "pipeline shape");
+  constexpr int TW = MB - D - 1 > 0 ? MB - D - 1 : 0;  // step that refills the tile slot
+  // loads issued after the awaited one: the next tile (D + 1 steps after its
+  // refill, or fewer when MB is small; the prologue issues D slabs after tile 0)
+  constexpr int WAIT_W = cap63((MB - 1 - TW < D ? MB - 1 - TW : D) * GA);
+  static_assert(R >= 2 && (D * GA + GW) < 64, "pipeline shape");
   static_assert(lds_bytes<Q6, SH>() <= 80 * 1024, "two workgroups per CU");
   using Raw = typename std::conditional<Q6, RawQ6, RawQ4>::type;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<Q6, SH>()];
@@ -384,11 +392,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
   const int mb0 = (int)blockIdx.y * MB;  // first 16-row block of this workgroup
   const int nmb = (M + MBLK - 1) / MBLK;
   const int64_t n = nt * TILE_N + col;
-  // this wave's LDS: R activation slabs, then W weight slots
+  // this wave's LDS: R activation slabs, then the tile slot
   uint8_t *ring = lds + wave * wave_lds<Q6, SH>();
-  uint8_t *wslots = ring + R * SLAB;
+  uint8_t *wslot = ring + R * SLAB;
   const uint32_t ring_a = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
-  const uint32_t wslots_a = ring_a + R * SLAB;
+  const uint32_t wslot_a = ring_a + R * SLAB;
 
   f32x4 acc[MB];
 #pragma unroll
@@ -411,41 +419,42 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
       const int mb = mb0 + t < nmb ? mb0 + t : nmb - 1;
       dma_record(dqa, ring_a + slot * SLAB, ((wave + WAVES * bi) * nmb + mb) * ACT_RECORD, lane);
     };
-    auto issue_w = [&](int bi, int slot) {
+    auto issue_w = [&](int bi) {
       bi = bi < nbw ? bi : nbw - 1;
-      dma_tile<Q6>(dw, wslots_a + slot * WSLOT, (wave + WAVES * bi) * TB, lane);
+      dma_tile<Q6>(dw, wslot_a, (wave + WAVES * bi) * TB, lane);
     };
-#pragma unroll
-    for (int i = 0; i < W; ++i) issue_w(i, i);
+    issue_w(0);
 #pragma unroll
     for (int p = 0; p < D; ++p) issue_a(p, p);
 
     int s_next = D;     // next step to load
     int slot_next = D;  // its slab
     int slot_use = 0;   // slab of the current step
-    int wslot = 0;      // slot of the current tile
     for (int bi = 0; bi < nbw; ++bi) {
       const int b = wave + WAVES * bi;
-      if (bi < W)
-        wait_vm<WAIT_W0>();
-      else
-        wait_vm<WAIT_W>();
+      wait_vm<WAIT_W>();
       Digits Dg;
       {
         Raw w;
-        read_w(wslots + wslot * WSLOT, lane, col, kq, w);
+        read_w(wslot, lane, col, kq, w);
         make_digits(w, kq, Dg);
       }
-      wait_lds();
-      issue_w(bi + W, wslot);
-      wslot = wslot + 1 == W ? 0 : wslot + 1;
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
-        wait_lds();  // the slab about to be refilled was read by the previous step
+        // the slab about to be refilled was read by the previous step, and
+        // at step TW the tile slot was read by this super-block's digits
+        wait_lds();
         issue_a(s_next, slot_next);
         ++s_next;
         slot_next = slot_next + 1 == R ? 0 : slot_next + 1;
-        wait_vm<WAIT_A>();
+        if (t == TW) issue_w(bi + 1);
+        // loads issued after this step's slab: D slabs, and the tile when it
+        // was issued at or after the slab (steps TW .. TW + D of the tile's
+        // super-block, all of which lie in this super-block)
+        if (t >= TW)
+          wait_vm<D * GA + GW>();
+        else
+          wait_vm<D * GA>();
         StepOut cur;
         step_mfma<Q6>(ring + slot_use * SLAB, frag, col, kq, Dg, cur);
         slot_use = slot_use + 1 == R ? 0 : slot_use + 1;
@@ -513,15 +522,11 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
   return hipGetLastError();
 }
 
-// Compiled variants, indexed by the number of 16-row m-blocks per workgroup.
-// Small MB (few steps per super-block) keeps more weight tiles in flight: the
-// weight stream is what the narrow GEMMs wait for.  Each shape keeps two
-// workgroups per CU within the 160 KB of LDS.
+// Compiled variants, indexed by the number of 16-row m-blocks per workgroup;
+// each keeps two workgroups per CU within the 160 KB of LDS.
 template <int TYPE, int MB>
 struct ShapeOf {
-  static constexpr bool SMALL = TYPE == 14 ? MB <= 4 : MB <= 2;
-  static constexpr bool MID = TYPE == 12 && (MB == 3 || MB == 4);
-  using type = Shape<MB, SMALL ? 2 : 3, SMALL ? 3 : (MID ? 2 : 1)>;
+  using type = Shape<MB, 3>;
 };
 constexpr int MB_SET[] = {16, 10, 8, 5, 4, 3, 2, 1};
 
