@@ -41,6 +41,7 @@ INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
 L, K, F, V, LAYERS, ROWS = 160, 4096, 12288, 126464, 32, 32
 Q4_K, Q6_K = 12, 14
 BLOCK = {Q4_K: 144, Q6_K: 210}
+COPY_MIB = 512
 KERNEL_SOURCES = ["quantized_gemm_diffusion_amd/csrc/qgemm.hip",
                   "quantized_gemm_diffusion_amd/csrc/dq_internal.h"]
 
@@ -59,6 +60,9 @@ def parse():
     p.add_argument("--cpu-threads", type=int, default=min(os.cpu_count() or 1, 16))
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (for profiler runs)")
+    p.add_argument("--counters", action="store_true",
+                   help="for hardware-counter runs: one eager step, then a plain copy of "
+                        f"{COPY_MIB} MiB (the byte-count calibration), no timing")
     return p.parse_args()
 
 
@@ -203,6 +207,15 @@ def main():
     for _ in range(args.warmup):
         run_calls(sp)
     torch.cuda.synchronize()
+    if args.counters:
+        run_calls(sp)
+        src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"counters mode: one step, then a {COPY_MIB} MiB copy")
+        return
     per_kind = {}
     evs = []
     for fn, a, k, ops, nbytes in calls:
