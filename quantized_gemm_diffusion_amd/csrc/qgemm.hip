@@ -260,47 +260,58 @@ __device__ inline void dma_tile(const i32x4 &d, uint32_t slot, int soff, int lan
   }
 }
 
-// The MFMA part of one step and what its fold needs.
-struct StepOut {
-  i32x4 rl, rh;
-  f32x4 mnf;
-  f32x4 x4;
+// One step's activation operands, read from the slab once and used against
+// every weight tile the wave owns.
+struct Frag {
+  i32x4 a[4];   // codes of row `col`, chunks 0..3 of this lane's k-quarter
+  f32x4 x4;     // d_x of rows 4kq .. 4kq+3
+  f16x4 amin;   // (Q4_K) code sums of groups 2kq, 2kq+1 of row `col`
 };
 
 template <bool Q6>
-__device__ inline void step_mfma(const uint8_t *slab, const int (&frag)[4], int col, int kq,
-                                 const Digits &D, StepOut &o) {
-  i32x4 a[4];
+__device__ inline void read_frag(const uint8_t *slab, const int (&frag)[4], int col, int kq,
+                                 Frag &f) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) a[c] = *reinterpret_cast<const i32x4 *>(slab + frag[c]);
-  o.x4 = *reinterpret_cast<const f32x4 *>(slab + ACT_DX_OFF + 16 * kq);
-  f16x4 amin = {};
-  if (!Q6) amin = *reinterpret_cast<const f16x4 *>(slab + ACT_SUMS_OFF + 32 * col + 8 * kq);
+  for (int c = 0; c < 4; ++c) f.a[c] = *reinterpret_cast<const i32x4 *>(slab + frag[c]);
+  f.x4 = *reinterpret_cast<const f32x4 *>(slab + ACT_DX_OFF + 16 * kq);
+  f.amin = f16x4{};
+  if (!Q6) f.amin = *reinterpret_cast<const f16x4 *>(slab + ACT_SUMS_OFF + 32 * col + 8 * kq);
   // issue every read of this slab here, a step before the slab is refilled,
   // so the refill's wait for outstanding LDS reads finds them done
   asm volatile("" ::: "memory");
+}
+
+// The MFMA part of one step for one weight tile.
+struct StepOut {
+  i32x4 rl, rh;
+  f32x4 mnf;
+};
+
+template <bool Q6>
+__device__ inline void step_mfma(const Frag &f, const Digits &D, StepOut &o) {
   o.rl = i32x4{};
   o.rh = i32x4{};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    o.rl = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[c], D.lo[c], o.rl, 0, 0, 0);
-    o.rh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[c], D.hi[c], o.rh, 0, 0, 0);
+    o.rl = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[c], D.lo[c], o.rl, 0, 0, 0);
+    o.rh = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[c], D.hi[c], o.rh, 0, 0, 0);
   }
   o.mnf = f32x4{};
   if (!Q6) {
     // the code sums of groups 2kq, 2kq+1 of row `col`, each as the exact
     // binary16 pair (lo, hi), against (m, m) of the same groups
-    o.mnf = __builtin_amdgcn_mfma_f32_16x16x16f16(amin, D.bmin, o.mnf, 0, 0, 0);
+    o.mnf = __builtin_amdgcn_mfma_f32_16x16x16f16(f.amin, D.bmin, o.mnf, 0, 0, 0);
   }
 }
 
 template <bool Q6>
-__device__ inline void step_fold(const StepOut &o, float dw, float dmw, f32x4 &acc) {
+__device__ inline void step_fold(const StepOut &o, const f32x4 &x4, float dw, float dmw,
+                                 f32x4 &acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s_int = Q6 ? o.rl[i] + o.rh[i] * 128 : o.rl[i] + o.rh[i] * 8;
     const float tv = Q6 ? dw * (float)s_int : dw * (float)s_int - dmw * o.mnf[i];
-    acc[i] += o.x4[i] * tv;
+    acc[i] += x4[i] * tv;
   }
 }
 
@@ -320,66 +331,71 @@ __device__ inline void step_debug(const StepOut &o, int64_t row0, int kq, int64_
 
 constexpr int WAVES = 4;
 
-// Launch shape of one GEMM variant: MB 16-row m-blocks per workgroup and R
-// activation slabs per wave (prefetch distance R - 1 steps).
-template <int MB_, int R_>
+// Launch shape of one GEMM variant: MB 16-row m-blocks per workgroup, NT
+// 16-column weight tiles per wave (every activation record and fragment read
+// feeds NT tiles), R activation slabs per wave (prefetch distance R - 1
+// steps) and OCC workgroups per CU (LDS and registers are sized for it).
+template <int MB_, int NT_, int R_, int OCC_ = 2>
 struct Shape {
-  static constexpr int MB = MB_, R = R_;
+  static constexpr int MB = MB_, NT = NT_, R = R_, OCC = OCC_;
 };
 
 template <bool Q6, class SH>
 constexpr int wave_lds() {
-  return SH::R * SLAB + wslot_bytes<Q6>();
+  return SH::R * SLAB + SH::NT * wslot_bytes<Q6>();
 }
 template <bool Q6, class SH>
 constexpr int lds_bytes() {
   constexpr int ring = WAVES * wave_lds<Q6, SH>();
-  constexpr int red = (WAVES / 2) * SH::MB * 4 * 64 * 4;
+  constexpr int red = (WAVES / 2) * SH::MB * SH::NT * 4 * 64 * 4;
   return ring > red ? ring : red;
 }
 constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 
-// One workgroup of 4 waves: one 16-column n-tile x MB 16-row m-blocks x the
+// One workgroup of 4 waves: NT 16-column n-tiles x MB 16-row m-blocks x the
 // whole reduction.  Wave w takes super-blocks b = w, w + 4, ...; it builds a
-// super-block's weight digits once and runs the MB steps of that super-block
-// against them.  The 4 f32 partial sums are added in LDS (pairwise tree) at
-// the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its own
-// symbol so profiles tell the two workloads apart), 2 = debug stores of S, Mn.
+// super-block's weight digits once per tile and runs the MB steps of that
+// super-block against them, each step reading its activation operands once
+// for all NT tiles.  The 4 f32 partial sums are added in LDS (pairwise tree)
+// at the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its
+// own symbol so profiles tell the two workloads apart), 2 = debug stores of
+// S and Mn.
 //
 // Load schedule of one wave (every load is a buffer-to-LDS load, and loads
 // complete in issue order, so a wait for one load also waits for every older
 // one):
-//   prologue      : tile of super-block 0, slabs of steps 0 .. D-1
-//   super-block i : wait for tile i; digits
+//   prologue      : tiles of super-block 0, slabs of steps 0 .. D-1
+//   super-block i : wait for its tiles; digits
 //     step s      : refill the slab read by step s - 1 with step s + D;
 //                   at step TW = max(0, MB - D - 1) of the super-block, also
-//                   refill the tile slot with tile i + 1;
+//                   refill the tile slots with super-block i + 1;
 //                   wait for step s; MFMAs; fold
-// The tile load is issued as late as its latency allows: the first wait that
-// covers it is the one for the next super-block's tile, D + 1 steps later.
-// Loads past the wave's last tile or step repeat the last one (valid memory
-// into a slot nobody reads again), so the number of loads issued after any
-// given load is fixed, and each wait is a constant vmcnt: at most that many
-// loads may still be outstanding when the awaited one must have landed.
+// The tile loads are issued as late as their latency allows: the first wait
+// that covers them is the one for the next super-block's tiles, D + 1 steps
+// later.  Loads past the wave's last tile or step repeat the last one (valid
+// memory into a slot nobody reads again), so the number of loads issued after
+// any given load is fixed, and each wait is a constant vmcnt: at most that
+// many loads may still be outstanding when the awaited one must have landed.
 template <int TYPE, class SH, int MODE>
-__global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, int nb,
-                                                              const uint8_t *__restrict__ qa,
-                                                              uint32_t qa_bytes,
-                                                              const uint8_t *__restrict__ packed,
-                                                              float *__restrict__ y, int64_t ldy,
-                                                              int32_t *__restrict__ dbg_S,
-                                                              int32_t *__restrict__ dbg_Mn) {
+__global__ __launch_bounds__(64 * WAVES, SH::OCC) void qgemm_kernel(int M, int64_t N, int nb,
+                                                                   const uint8_t *__restrict__ qa,
+                                                                   uint32_t qa_bytes,
+                                                                   const uint8_t *__restrict__ packed,
+                                                                   float *__restrict__ y, int64_t ldy,
+                                                                   int32_t *__restrict__ dbg_S,
+                                                                   int32_t *__restrict__ dbg_Mn) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
-  constexpr int MB = SH::MB, R = SH::R, D = R - 1;
+  constexpr int MB = SH::MB, NT = SH::NT, R = SH::R, D = R - 1;
   constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
-  constexpr int GW = dma_per_tile<Q6>();
-  constexpr int TW = MB - D - 1 > 0 ? MB - D - 1 : 0;  // step that refills the tile slot
-  // loads issued after the awaited one: the next tile (D + 1 steps after its
-  // refill, or fewer when MB is small; the prologue issues D slabs after tile 0)
+  constexpr int WSLOT = wslot_bytes<Q6>();
+  constexpr int GW = NT * dma_per_tile<Q6>();
+  constexpr int TW = MB - D - 1 > 0 ? MB - D - 1 : 0;  // step that refills the tile slots
+  // loads issued after the awaited one: the next tiles (D + 1 steps after their
+  // refill, or fewer when MB is small; the prologue issues D slabs after them)
   constexpr int WAIT_W = cap63((MB - 1 - TW < D ? MB - 1 - TW : D) * GA);
   static_assert(R >= 2 && (D * GA + GW) < 64, "pipeline shape");
-  static_assert(lds_bytes<Q6, SH>() <= 80 * 1024, "two workgroups per CU");
+  static_assert(lds_bytes<Q6, SH>() * SH::OCC <= 160 * 1024, "workgroups per CU");
   using Raw = typename std::conditional<Q6, RawQ6, RawQ4>::type;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<Q6, SH>()];
 
@@ -388,25 +404,34 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const int64_t nt = blockIdx.x;
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  const int64_t nt0 = (int64_t)blockIdx.x * NT;
   const int mb0 = (int)blockIdx.y * MB;  // first 16-row block of this workgroup
   const int nmb = (M + MBLK - 1) / MBLK;
-  const int64_t n = nt * TILE_N + col;
-  // this wave's LDS: R activation slabs, then the tile slot
+  // this wave's LDS: R activation slabs, then NT tile slots
   uint8_t *ring = lds + wave * wave_lds<Q6, SH>();
   uint8_t *wslot = ring + R * SLAB;
   const uint32_t ring_a = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
   const uint32_t wslot_a = ring_a + R * SLAB;
 
-  f32x4 acc[MB];
+  f32x4 acc[MB][NT];
 #pragma unroll
-  for (int t = 0; t < MB; ++t) acc[t] = f32x4{};
+  for (int t = 0; t < MB; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = f32x4{};
 
   const int nbw = wave < nb ? (nb - wave + WAVES - 1) / WAVES : 0;  // this wave's super-blocks
   const int S = nbw * MB;                                           // and steps
   if (S > 0) {
     const i32x4 dqa = desc(qa, qa_bytes);
-    const i32x4 dw = desc(packed + nt * nb * TB, (uint32_t)(nb * TB));
+    // a tile index past the last n-tile repeats the last one (its columns are
+    // not stored)
+    i32x4 dw[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t tj = nt0 + j < ntiles ? nt0 + j : ntiles - 1;
+      dw[j] = desc(packed + tj * nb * TB, (uint32_t)(nb * TB));
+    }
     int frag[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) frag[c] = col * QK + 16 * ((4 * kq + c) ^ col);
@@ -421,7 +446,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
     };
     auto issue_w = [&](int bi) {
       bi = bi < nbw ? bi : nbw - 1;
-      dma_tile<Q6>(dw, wslot_a, (wave + WAVES * bi) * TB, lane);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        dma_tile<Q6>(dw[j], wslot_a + j * WSLOT, (wave + WAVES * bi) * TB, lane);
     };
     issue_w(0);
 #pragma unroll
@@ -433,35 +460,42 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
     for (int bi = 0; bi < nbw; ++bi) {
       const int b = wave + WAVES * bi;
       wait_vm<WAIT_W>();
-      Digits Dg;
-      {
+      Digits Dg[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
         Raw w;
-        read_w(wslot, lane, col, kq, w);
-        make_digits(w, kq, Dg);
+        read_w(wslot + j * WSLOT, lane, col, kq, w);
+        make_digits(w, kq, Dg[j]);
       }
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
         // the slab about to be refilled was read by the previous step, and
-        // at step TW the tile slot was read by this super-block's digits
+        // at step TW the tile slots were read by this super-block's digits
         wait_lds();
         issue_a(s_next, slot_next);
         ++s_next;
         slot_next = slot_next + 1 == R ? 0 : slot_next + 1;
         if (t == TW) issue_w(bi + 1);
-        // loads issued after this step's slab: D slabs, and the tile when it
-        // was issued at or after the slab (steps TW .. TW + D of the tile's
-        // super-block, all of which lie in this super-block)
+        // loads issued after this step's slab: D slabs, and the tiles when
+        // they were issued at or after the slab (steps TW .. TW + D of the
+        // tiles' super-block, all of which lie in this super-block)
         if (t >= TW)
           wait_vm<D * GA + GW>();
         else
           wait_vm<D * GA>();
-        StepOut cur;
-        step_mfma<Q6>(ring + slot_use * SLAB, frag, col, kq, Dg, cur);
+        Frag f;
+        read_frag<Q6>(ring + slot_use * SLAB, frag, col, kq, f);
         slot_use = slot_use + 1 == R ? 0 : slot_use + 1;
-        if (DEBUG)
-          step_debug<Q6>(cur, (int64_t)(mb0 + t) * MBLK, kq, n, M, N, nb, b, dbg_S, dbg_Mn);
-        else
-          step_fold<Q6>(cur, Dg.dw, Dg.dmw, acc[t]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          StepOut cur;
+          step_mfma<Q6>(f, Dg[j], cur);
+          if (DEBUG)
+            step_debug<Q6>(cur, (int64_t)(mb0 + t) * MBLK, kq, (nt0 + j) * TILE_N + col, M,
+                           nt0 + j < ntiles ? N : 0, nb, b, dbg_S, dbg_Mn);
+          else
+            step_fold<Q6>(cur, f.x4, Dg[j].dw, Dg[j].dmw, acc[t][j]);
+        }
       }
     }
     wait_vm<0>();  // no LDS write may land after this point
@@ -469,35 +503,45 @@ __global__ __launch_bounds__(64 * WAVES, 2) void qgemm_kernel(int M, int64_t N, 
   if (DEBUG) return;
 
   // cross-wave reduction: pairwise tree through LDS
+  constexpr int PER = MB * NT * 4;  // partial sums per lane
   float *red = reinterpret_cast<float *>(lds);
   __syncthreads();  // every wave is done with its ring
 #pragma unroll
   for (int half = WAVES / 2; half >= 1; half /= 2) {
     if (wave >= half && wave < 2 * half) {
-      float *dst = red + (wave - half) * (MB * 4 * 64);
+      float *dst = red + (wave - half) * (PER * 64);
 #pragma unroll
       for (int t = 0; t < MB; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(t * 4 + i) * 64 + lane] = acc[t][i];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[((t * NT + j) * 4 + i) * 64 + lane] = acc[t][j][i];
     }
     __syncthreads();
     if (wave < half) {
-      const float *src = red + wave * (MB * 4 * 64);
+      const float *src = red + wave * (PER * 64);
 #pragma unroll
       for (int t = 0; t < MB; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] += src[(t * 4 + i) * 64 + lane];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][j][i] += src[((t * NT + j) * 4 + i) * 64 + lane];
     }
     __syncthreads();
   }
-  if (wave == 0 && n < N) {
+  if (wave == 0) {
 #pragma unroll
-    for (int t = 0; t < MB; ++t)
+    for (int j = 0; j < NT; ++j) {
+      const int64_t n = (nt0 + j) * TILE_N + col;
+      if (nt0 + j >= ntiles || n >= N) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (mb0 + t) * MBLK + 4 * kq + i;
-        if (row < M) y[(int64_t)row * ldy + n] = acc[t][i];
-      }
+      for (int t = 0; t < MB; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = (mb0 + t) * MBLK + 4 * kq + i;
+          if (row < M) y[(int64_t)row * ldy + n] = acc[t][j][i];
+        }
+    }
   }
 }
 
@@ -506,7 +550,8 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
                    const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn,
                    hipStream_t stream) {
   const int64_t nmb = (M + MBLK - 1) / MBLK;
-  dim3 grid((unsigned)((N + TILE_N - 1) / TILE_N), (unsigned)((nmb + SH::MB - 1) / SH::MB));
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  dim3 grid((unsigned)((ntiles + SH::NT - 1) / SH::NT), (unsigned)((nmb + SH::MB - 1) / SH::MB));
   dim3 block(64 * WAVES);
   const int m = (int)M;
   const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
@@ -522,20 +567,23 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
   return hipGetLastError();
 }
 
-// Compiled variants, indexed by the number of 16-row m-blocks per workgroup;
-// each keeps two workgroups per CU within the 160 KB of LDS.
+// Compiled variants, indexed by the number of 16-row m-blocks per workgroup:
+// two n-tiles per wave, and as many activation slabs (3 for Q4_K, 2 for the
+// larger Q6_K tiles) as keep two workgroups per CU within the 160 KB of LDS.
 template <int TYPE, int MB>
 struct ShapeOf {
-  using type = Shape<MB, 3>;
+  using type = Shape<MB, 2, TYPE == 14 ? 2 : 3>;
 };
-constexpr int MB_SET[] = {16, 10, 8, 5, 4, 3, 2, 1};
+constexpr int MB_SET[] = {8, 5, 4, 3, 2, 1};
 
 // Prefer the largest MB (weight digits are built once per MB steps) that
-// still launches two waves per SIMD (n-tiles x m-chunks x 4 waves >= 2048)
-// with at most one padded m-block per chunk; otherwise the choice with the
-// most waves.
+// still launches one wave per SIMD (pairs of n-tiles x m-chunks x 4 waves
+// >= 1024) with at most one padded m-block per chunk; otherwise the choice
+// with the most waves.
 inline int pick_mb(int64_t M, int64_t N) {
-  const int64_t mblocks = (M + MBLK - 1) / MBLK, ntiles = (N + TILE_N - 1) / TILE_N;
+  constexpr int NT = 2;  // n-tiles per wave in every compiled shape
+  const int64_t mblocks = (M + MBLK - 1) / MBLK;
+  const int64_t ntiles = ((N + TILE_N - 1) / TILE_N + NT - 1) / NT;
   int best = 1;
   int64_t best_waves = -1;
   for (int mb : MB_SET) {
@@ -543,7 +591,7 @@ inline int pick_mb(int64_t M, int64_t N) {
     const int64_t chunks = (mblocks + mb - 1) / mb;
     const int64_t waste = chunks * mb - mblocks;
     const int64_t waves = ntiles * chunks * WAVES;
-    if (waves >= 2048 && waste <= 1) return mb;
+    if (waves >= 1024 && waste <= 1) return mb;
     if (waves > best_waves) {
       best_waves = waves;
       best = mb;
@@ -561,8 +609,6 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
     return launch2<TYPE, typename ShapeOf<TYPE, X>::type>(mode, M, N, nb, qa, packed, y, ldy, \
                                                           dbg_S, dbg_Mn, stream)
   switch (pick_mb(M, N)) {
-    DQ_MB(16);
-    DQ_MB(10);
     DQ_MB(8);
     DQ_MB(5);
     DQ_MB(4);
