@@ -329,15 +329,15 @@ __device__ inline void step_debug(const StepOut &o, int64_t row0, int kq, int64_
   }
 }
 
-constexpr int WAVES = 4;
 
 // Launch shape of one GEMM variant: MB 16-row m-blocks per workgroup, NT
 // 16-column weight tiles per wave (every activation record and fragment read
 // feeds NT tiles), R activation slabs per wave (prefetch distance R - 1
-// steps) and OCC workgroups per CU (LDS and registers are sized for it).
-template <int MB_, int NT_, int R_, int OCC_ = 2>
+// steps), WAVES waves splitting the reduction, and OCC workgroups per CU
+// (LDS and registers are sized for it).
+template <int MB_, int NT_, int R_, int WAVES_, int OCC_>
 struct Shape {
-  static constexpr int MB = MB_, NT = NT_, R = R_, OCC = OCC_;
+  static constexpr int MB = MB_, NT = NT_, R = R_, WAVES = WAVES_, OCC = OCC_;
 };
 
 template <bool Q6, class SH>
@@ -346,18 +346,18 @@ constexpr int wave_lds() {
 }
 template <bool Q6, class SH>
 constexpr int lds_bytes() {
-  constexpr int ring = WAVES * wave_lds<Q6, SH>();
-  constexpr int red = (WAVES / 2) * SH::MB * SH::NT * 4 * 64 * 4;
+  constexpr int ring = SH::WAVES * wave_lds<Q6, SH>();
+  constexpr int red = (SH::WAVES / 2) * SH::MB * SH::NT * 4 * 64 * 4;
   return ring > red ? ring : red;
 }
 constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 
-// One workgroup of 4 waves: NT 16-column n-tiles x MB 16-row m-blocks x the
-// whole reduction.  Wave w takes super-blocks b = w, w + 4, ...; it builds a
+// One workgroup of WAVES waves: NT 16-column n-tiles x MB 16-row m-blocks x
+// the whole reduction.  Wave w takes super-blocks b = w, w + WAVES, ...; it builds a
 // super-block's weight digits once per tile and runs the MB steps of that
 // super-block against them, each step reading its activation operands once
-// for all NT tiles.  The 4 f32 partial sums are added in LDS (pairwise tree)
-// at the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its
+// for all NT tiles.  The WAVES f32 partial sums are added in LDS (pairwise
+// tree, fixed order) at the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its
 // own symbol so profiles tell the two workloads apart), 2 = debug stores of
 // S and Mn.
 //
@@ -377,7 +377,7 @@ constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 // any given load is fixed, and each wait is a constant vmcnt: at most that
 // many loads may still be outstanding when the awaited one must have landed.
 template <int TYPE, class SH, int MODE>
-__global__ __launch_bounds__(64 * WAVES, SH::OCC) void qgemm_kernel(int M, int64_t N, int nb,
+__global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, int64_t N, int nb,
                                                                    const uint8_t *__restrict__ qa,
                                                                    uint32_t qa_bytes,
                                                                    const uint8_t *__restrict__ packed,
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(64 * WAVES, SH::OCC) void qgemm_kernel(int M, int64
                                                                    int32_t *__restrict__ dbg_Mn) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
-  constexpr int MB = SH::MB, NT = SH::NT, R = SH::R, D = R - 1;
+  constexpr int MB = SH::MB, NT = SH::NT, R = SH::R, D = R - 1, WAVES = SH::WAVES;
   constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
   constexpr int WSLOT = wslot_bytes<Q6>();
   constexpr int GW = NT * dma_per_tile<Q6>();
@@ -552,7 +552,7 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
   const int64_t nmb = (M + MBLK - 1) / MBLK;
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
   dim3 grid((unsigned)((ntiles + SH::NT - 1) / SH::NT), (unsigned)((nmb + SH::MB - 1) / SH::MB));
-  dim3 block(64 * WAVES);
+  dim3 block(64 * SH::WAVES);
   const int m = (int)M;
   const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
   if (mode == 2)
@@ -569,46 +569,71 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
 
 // Compiled variants, indexed by the number of 16-row m-blocks per workgroup:
 // two n-tiles per wave, and as many activation slabs (3 for Q4_K, 2 for the
-// larger Q6_K tiles) as keep two workgroups per CU within the 160 KB of LDS.
-template <int TYPE, int MB>
+// larger Q6_K tiles) as keep the workgroups' LDS within the CU's 160 KB.
+// WAVES = 8 (one workgroup per CU) splits the reduction twice as finely as
+// WAVES = 4 (two workgroups per CU) over the same tile grid.
+template <int TYPE, int MB, int WAVES>
 struct ShapeOf {
-  using type = Shape<MB, 2, TYPE == 14 ? 2 : 3>;
+  using type = Shape<MB, 2, TYPE == 14 ? 2 : 3, WAVES, WAVES == 8 ? 1 : 2>;
 };
 constexpr int MB_SET[] = {8, 5, 4, 3, 2, 1};
+constexpr int NT_ALL = 2;  // n-tiles per wave in every compiled shape
 
-// Prefer the largest MB (weight digits are built once per MB steps) that
-// still launches one wave per SIMD (pairs of n-tiles x m-chunks x 4 waves
-// >= 1024) with at most one padded m-block per chunk; otherwise the choice
-// with the most waves.
-inline int pick_mb(int64_t M, int64_t N) {
-  constexpr int NT = 2;  // n-tiles per wave in every compiled shape
+struct Pick {
+  int mb, waves;
+};
+
+// Prefer the largest MB (weight digits are built once per MB steps) with at
+// most one padded m-block per m-chunk that gives at least one wave per SIMD
+// (1024 waves at 4 waves per workgroup).  Use 8 waves per workgroup only for
+// long reductions (each wave still gets 6 or more super-blocks, so its
+// pipeline fill and the deeper cross-wave sum stay small) and when that fills
+// the CUs in whole rounds better than 4 (one 8-wave or two 4-wave workgroups
+// per CU).
+inline Pick pick_shape(int64_t M, int64_t N, int64_t nb) {
   const int64_t mblocks = (M + MBLK - 1) / MBLK;
-  const int64_t ntiles = ((N + TILE_N - 1) / TILE_N + NT - 1) / NT;
-  int best = 1;
+  const int64_t tiles = ((N + TILE_N - 1) / TILE_N + NT_ALL - 1) / NT_ALL;
+  int mb = 1;
   int64_t best_waves = -1;
-  for (int mb : MB_SET) {
-    if (mb > mblocks && mb != 1) continue;
-    const int64_t chunks = (mblocks + mb - 1) / mb;
-    const int64_t waste = chunks * mb - mblocks;
-    const int64_t waves = ntiles * chunks * WAVES;
-    if (waves >= 1024 && waste <= 1) return mb;
+  for (int cand : MB_SET) {
+    if (cand > mblocks && cand != 1) continue;
+    const int64_t chunks = (mblocks + cand - 1) / cand;
+    const int64_t waste = chunks * cand - mblocks;
+    const int64_t waves = tiles * chunks * 4;
+    if (waves >= 1024 && waste <= 1) {
+      mb = cand;
+      break;
+    }
     if (waves > best_waves) {
       best_waves = waves;
-      best = mb;
+      mb = cand;
     }
   }
-  return best;
+  const int64_t wgs = tiles * ((mblocks + mb - 1) / mb);
+  constexpr int64_t CUS = 256;
+  // fraction of workgroup slots used over the whole launch, per wave count
+  auto fill = [&](int64_t per_cu) {
+    const int64_t slots = CUS * per_cu;
+    const int64_t rounds = (wgs + slots - 1) / slots;
+    return (double)wgs / (double)(rounds * slots);
+  };
+  const bool eight = nb >= 48 && fill(1) > fill(2) + 0.05;
+  return Pick{mb, eight ? 8 : 4};
 }
 
 template <int TYPE>
 hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
                        const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
                        int32_t *dbg_Mn, hipStream_t stream) {
-#define DQ_MB(X)                                                                          \
-  case X:                                                                                 \
-    return launch2<TYPE, typename ShapeOf<TYPE, X>::type>(mode, M, N, nb, qa, packed, y, ldy, \
-                                                          dbg_S, dbg_Mn, stream)
-  switch (pick_mb(M, N)) {
+  const Pick pk = pick_shape(M, N, nb);
+#define DQ_MB(X)                                                                               \
+  case X:                                                                                      \
+    if (pk.waves == 8)                                                                         \
+      return launch2<TYPE, typename ShapeOf<TYPE, X, 8>::type>(mode, M, N, nb, qa, packed, y,  \
+                                                               ldy, dbg_S, dbg_Mn, stream);    \
+    return launch2<TYPE, typename ShapeOf<TYPE, X, 4>::type>(mode, M, N, nb, qa, packed, y,    \
+                                                             ldy, dbg_S, dbg_Mn, stream)
+  switch (pk.mb) {
     DQ_MB(8);
     DQ_MB(5);
     DQ_MB(4);
@@ -617,8 +642,11 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
     default: break;
   }
 #undef DQ_MB
-  return launch2<TYPE, typename ShapeOf<TYPE, 1>::type>(mode, M, N, nb, qa, packed, y, ldy, dbg_S,
-                                                        dbg_Mn, stream);
+  if (pk.waves == 8)
+    return launch2<TYPE, typename ShapeOf<TYPE, 1, 8>::type>(mode, M, N, nb, qa, packed, y, ldy,
+                                                             dbg_S, dbg_Mn, stream);
+  return launch2<TYPE, typename ShapeOf<TYPE, 1, 4>::type>(mode, M, N, nb, qa, packed, y, ldy,
+                                                           dbg_S, dbg_Mn, stream);
 }
 
 }  // namespace

@@ -7,9 +7,9 @@
 //
 // One wave64 per (row, 256-block), rows padded to a multiple of 16: each lane
 // owns 4 consecutive values.  The block's max |x| is reduced across the wave
-// (max is exact in any order), then every lane applies inv = 127/amax (IEEE
-// division), rint (ties to even) and a clamp to [-127, 127]; the 8 lanes of
-// each 32-group sum their codes.  All arithmetic is binary32 with no
+// with DPP lane moves (max is exact in any order), then every lane applies
+// inv = 127/amax (IEEE division), rint (ties to even) and a clamp to
+// [-127, 127]; the 8 lanes of each 32-group sum their codes.  All arithmetic is binary32 with no
 // contraction, so codes match any other binary32 implementation of the same
 // steps bit for bit.  Padding rows (m >= M) write zeros.
 #include "dq_internal.h"
@@ -21,6 +21,41 @@ namespace dq {
 namespace {
 
 constexpr int WAVES_PER_BLOCK = 4;
+
+// Cross-lane moves inside a row of 16 lanes (DPP): quad permutations
+// [1,0,3,2] and [2,3,0,1], half-row mirror (lane i <-> 7-i of each 8) and
+// row mirror (lane i <-> 15-i).  Broadcasts of lane 15 / 31 into the next
+// row(s) finish a reduction over the wave in lane 63.
+constexpr int DPP_QUAD_1032 = 0xb1, DPP_QUAD_2301 = 0x4e;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// max |x| over the wave (max is exact in any order), the same in every lane
+__device__ inline float wave_max(float v) {
+  auto step = [](float a, int b) { return fmaxf(a, __builtin_bit_cast(float, b)); };
+  v = step(v, dpp<DPP_QUAD_1032>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_QUAD_2301>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_ROW_HALF_MIRROR>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_ROW_MIRROR>(__builtin_bit_cast(int, v)));
+  // lanes of rows 1 and 3 take the max with lane 15 of the row before, then
+  // rows 2 and 3 with lane 31: lane 63 holds the maximum of all 64 lanes
+  v = step(v, dpp<DPP_ROW_BCAST15, 0xa>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_ROW_BCAST31, 0xc>(__builtin_bit_cast(int, v)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// sum over each group of 8 lanes (the 32 codes of one group), in every lane
+__device__ inline int group8_sum(int s) {
+  s += dpp<DPP_QUAD_1032>(s);
+  s += dpp<DPP_QUAD_2301>(s);
+  s += dpp<DPP_ROW_HALF_MIRROR>(s);
+  return s;
+}
 
 template <bool VEC, bool GATHER>
 __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, int nb,
@@ -65,9 +100,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, 
     }
   }
 
-  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float amax =
+      wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
 
   int c[4] = {0, 0, 0, 0};
   if (amax != 0.0f) {
@@ -85,10 +119,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, 
   const int u = lane >> 2;
   *reinterpret_cast<uint32_t *>(rec + r * QK + 16 * (u ^ r) + 4 * (lane & 3)) = word;
 
-  int s = c[0] + c[1] + c[2] + c[3];
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
+  const int s = group8_sum(c[0] + c[1] + c[2] + c[3]);
   if ((lane & 7) == 0) {
     // (lo, hi) = (s & 63, s - lo): both exact in binary16
     const int lo = s & 63;
