@@ -347,7 +347,7 @@ constexpr int wave_lds() {
 template <bool Q6, class SH>
 constexpr int lds_bytes() {
   constexpr int ring = SH::WAVES * wave_lds<Q6, SH>();
-  constexpr int red = (SH::WAVES / 2) * SH::MB * SH::NT * 4 * 64 * 4;
+  constexpr int red = SH::WAVES * SH::MB * SH::NT * 4 * 64 * 4;
   return ring > red ? ring : red;
 }
 constexpr int cap63(int v) { return v > 63 ? 63 : v; }
@@ -382,6 +382,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
                                                                    uint32_t qa_bytes,
                                                                    const uint8_t *__restrict__ packed,
                                                                    float *__restrict__ y, int64_t ldy,
+                                                                   int y_vec,
                                                                    int32_t *__restrict__ dbg_S,
                                                                    int32_t *__restrict__ dbg_Mn) {
   constexpr bool Q6 = TYPE == 14;
@@ -502,45 +503,44 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
   }
   if (DEBUG) return;
 
-  // cross-wave reduction: pairwise tree through LDS
+  // Cross-wave reduction.  Every wave stores its partial sums to LDS; then
+  // wave w owns output tiles (t, j) = w, w + WAVES, ... and adds the WAVES
+  // partials of each element in wave order (the same order on every run).
+  // Lane L of the owning wave takes row r = 4 * ((L >> 2) & 3) + (L >> 4) and
+  // the 4 columns 4 * (L & 3) .. +3 of the tile: a 16-byte store per row
+  // segment, and each 16-lane group of the LDS reads hits 16 distinct bank
+  // groups.  Partial (t, j, i) of lane l sits at ((t * NT + j) * 4 + i) * 64 + l.
   constexpr int PER = MB * NT * 4;  // partial sums per lane
   float *red = reinterpret_cast<float *>(lds);
   __syncthreads();  // every wave is done with its ring
+  {
+    float *dst = red + wave * (PER * 64);
 #pragma unroll
-  for (int half = WAVES / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-      float *dst = red + (wave - half) * (PER * 64);
+    for (int t = 0; t < MB; ++t)
 #pragma unroll
-      for (int t = 0; t < MB; ++t)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[((t * NT + j) * 4 + i) * 64 + lane] = acc[t][j][i];
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float *src = red + wave * (PER * 64);
-#pragma unroll
-      for (int t = 0; t < MB; ++t)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][j][i] += src[((t * NT + j) * 4 + i) * 64 + lane];
-    }
-    __syncthreads();
+        for (int i = 0; i < 4; ++i) dst[((t * NT + j) * 4 + i) * 64 + lane] = acc[t][j][i];
   }
-  if (wave == 0) {
+  __syncthreads();
+  const int ri = lane >> 4, rq = (lane >> 2) & 3, c0 = 4 * (lane & 3);
+  const int r = 4 * rq + ri;
+  for (int p = wave; p < MB * NT; p += WAVES) {
+    const int t = p / NT, j = p - t * NT;
+    const int64_t n0 = (nt0 + j) * TILE_N + c0;
+    const int row = (mb0 + t) * MBLK + r;
+    const float *src = red + (p * 4 + ri) * 64 + 16 * rq + c0;
+    f32x4 v = *reinterpret_cast<const f32x4 *>(src);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t n = (nt0 + j) * TILE_N + col;
-      if (nt0 + j >= ntiles || n >= N) continue;
+    for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const f32x4 *>(src + w * (PER * 64));
+    if (nt0 + j >= ntiles || row >= M || n0 >= N) continue;
+    float *yp = y + (int64_t)row * ldy + n0;
+    if (y_vec && n0 + 3 < N) {
+      *reinterpret_cast<f32x4 *>(yp) = v;
+    } else {
 #pragma unroll
-      for (int t = 0; t < MB; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (mb0 + t) * MBLK + 4 * kq + i;
-          if (row < M) y[(int64_t)row * ldy + n] = acc[t][j][i];
-        }
+      for (int c = 0; c < 4; ++c)
+        if (n0 + c < N) yp[c] = v[c];
     }
   }
 }
@@ -555,15 +555,17 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
   dim3 block(64 * SH::WAVES);
   const int m = (int)M;
   const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
+  // rows of y can take 16-byte stores
+  const int y_vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);
   if (mode == 2)
     hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 2>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
-                       packed, y, ldy, dbg_S, dbg_Mn);
+                       packed, y, ldy, y_vec, dbg_S, dbg_Mn);
   else if (mode == 1)
     hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 1>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
-                       packed, y, ldy, dbg_S, dbg_Mn);
+                       packed, y, ldy, y_vec, dbg_S, dbg_Mn);
   else
     hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 0>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
-                       packed, y, ldy, dbg_S, dbg_Mn);
+                       packed, y, ldy, y_vec, dbg_S, dbg_Mn);
   return hipGetLastError();
 }
 
