@@ -545,6 +545,206 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow M (at most 32 rows, K of 8 to 16 super-blocks in pairs): the weight
+// stream is the whole cost (the output projection on the requested rows moves
+// 425 MB of weights for 32 rows), so the operands switch roles.  One
+// persistent workgroup per CU, of K/512 waves, walks n-tiles blockIdx.x,
+// blockIdx.x + grid, ...; wave w owns super-blocks w and w + K/512 and holds
+// their activation fragments in registers for the whole launch.  The loop
+// then only streams weight tiles: buffer-to-LDS loads into S slots per wave,
+// explicit waits as in the canvas kernel.  A slot is refilled as soon as its
+// tile has been read into registers, so S n-tiles are in flight while one is
+// being computed.  The waves'
+// partial sums of each tile meet in LDS (double buffered: one barrier per
+// tile) and waves 0 .. MB-1 add them in wave order and store.
+constexpr int NW_WAVES = 8;  // most waves per narrow workgroup
+constexpr int NW_KB = 2;     // super-blocks per wave
+
+// Output stores of the narrow kernel, through a buffer resource over the
+// wave's 16-row block of y: a lane whose element is not stored passes an
+// offset past the resource's size, which the hardware drops.  Every call is
+// one store instruction whatever the lanes hold, so the explicit weight-load
+// waits can count them.  The trailing s_nop covers the one wait state a VALU
+// write to the data registers of a wider-than-8-byte store needs.
+__device__ inline void bstore4(const i32x4 &d, uint32_t off, const f32x4 &v) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" ::"v"(v), "v"(off), "s"(d)
+               : "memory");
+}
+__device__ inline void bstore1(const i32x4 &d, uint32_t off, float v) {
+  asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(d) : "memory");
+}
+constexpr uint32_t NW_DROP = 0x80000000u;  // offset past every narrow store resource
+
+template <bool Q6, int MB, int S>
+constexpr int narrow_lds() {
+  return 2 * NW_WAVES * MB * 4 * 64 * 4 + NW_WAVES * S * NW_KB * wslot_bytes<Q6>();
+}
+
+template <int TYPE, int MB, int S, bool VEC>
+__global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
+    int M, int64_t N, int nb, const uint8_t *__restrict__ qa, const uint8_t *__restrict__ packed,
+    float *__restrict__ y, int64_t ldy) {
+  constexpr bool Q6 = TYPE == 14;
+  constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
+  constexpr int WSLOT = wslot_bytes<Q6>();
+  constexpr int SET = NW_KB * WSLOT;                      // one n-tile of one wave
+  constexpr int DPS = NW_KB * dma_per_tile<Q6>();         // loads per set
+  constexpr int SC = VEC ? 1 : 4;                         // stores per tile (storing waves)
+  constexpr int PER = MB * 4 * 64;                        // partial sums per wave per tile
+  static_assert(S >= 2 && (S - 1) * DPS + S * SC < 64, "pipeline shape");
+  static_assert(narrow_lds<Q6, MB, S>() <= 160 * 1024, "LDS");
+  using Raw = typename std::conditional<Q6, RawQ6, RawQ4>::type;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[narrow_lds<Q6, MB, S>()];
+  float *red = reinterpret_cast<float *>(lds);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  const int nmb = (M + MBLK - 1) / MBLK;  // == MB
+  const int nw = nb / NW_KB;              // waves in this workgroup
+  const int64_t G = gridDim.x;
+
+  // this wave's activation operands, for the whole launch
+  Frag act[NW_KB][MB];
+#pragma unroll
+  for (int i = 0; i < NW_KB; ++i) {
+    const int b = wave + nw * i;
+#pragma unroll
+    for (int t = 0; t < MB; ++t) {
+      const uint8_t *rec = qa + ((int64_t)b * nmb + t) * ACT_RECORD;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        act[i][t].a[c] = *reinterpret_cast<const i32x4 *>(rec + col * QK + 16 * ((4 * kq + c) ^ col));
+      act[i][t].x4 = *reinterpret_cast<const f32x4 *>(rec + ACT_DX_OFF + 16 * kq);
+      act[i][t].amin = f16x4{};
+      if (!Q6) act[i][t].amin = *reinterpret_cast<const f16x4 *>(rec + ACT_SUMS_OFF + 32 * col + 8 * kq);
+    }
+  }
+  // all of them in before the first weight load: from here on the only
+  // memory loads in flight are this wave's weight tiles
+  __builtin_amdgcn_s_waitcnt(0);
+
+  uint8_t *slots = lds + 2 * NW_WAVES * PER * 4 + wave * S * SET;
+  const uint32_t slots_a = (uint32_t)(uintptr_t)(lds_ptr_t)slots;
+  // tiles of n-tile blockIdx.x + kk * grid (past the end: the last n-tile,
+  // whose slot is never read) into slot `slot`
+  auto issue = [&](int64_t kk, int slot) {
+    int64_t nt = blockIdx.x + kk * G;
+    nt = nt < ntiles ? nt : ntiles - 1;
+    const i32x4 d = desc(packed + nt * nb * TB, (uint32_t)(nb * TB));
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i)
+      dma_tile<Q6>(d, slots_a + slot * SET + i * WSLOT, (wave + nw * i) * TB, lane);
+  };
+
+  // the storing wave's resource: rows 16 t .. 16 t + 15 of y
+  const bool storer = wave < MB;
+  const int t_st = storer ? wave : 0;
+  const int rows_st = M - MBLK * t_st < MBLK ? M - MBLK * t_st : MBLK;
+  const i32x4 dy = desc(y + (int64_t)t_st * MBLK * ldy,
+                        (uint32_t)(((int64_t)(rows_st - 1) * ldy + N) * 4));
+  const int ri = lane >> 4, rq = (lane >> 2) & 3, c0 = 4 * (lane & 3);
+  const int r_st = 4 * rq + ri;  // this lane's row and first column in the tile
+
+#pragma unroll
+  for (int p = 0; p < S; ++p) issue(p, p);
+
+  int slot = 0;
+  for (int64_t k = 0;; ++k) {
+    const int64_t nt = blockIdx.x + k * G;
+    if (nt >= ntiles) break;
+    // younger than this tile's loads: the next S - 1 sets, and the stores of
+    // the last S tiles (fewer in the first tiles: then the wait only waits
+    // longer)
+    if (storer && k >= S)
+      wait_vm<(S - 1) * DPS + S * SC>();
+    else
+      wait_vm<(S - 1) * DPS>();
+    Raw w[NW_KB];
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) read_w(slots + slot * SET + i * WSLOT, lane, col, kq, w[i]);
+    // the slot is free once its reads are in: refill it with the tile S ahead
+    wait_lds();
+    issue(k + S, slot);
+    slot = slot + 1 == S ? 0 : slot + 1;
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int t = 0; t < MB; ++t) acc[t] = f32x4{};
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) {
+      Digits Dg;
+      make_digits(w[i], kq, Dg);
+#pragma unroll
+      for (int t = 0; t < MB; ++t) {
+        StepOut o;
+        step_mfma<Q6>(act[i][t], Dg, o);
+        step_fold<Q6>(o, act[i][t].x4, Dg.dw, Dg.dmw, acc[t]);
+      }
+    }
+
+    // partial sums into this tile's buffer; the buffer alternates, so the one
+    // written here was last read before the previous tile's barrier
+    float *dst = red + (int)(k & 1) * NW_WAVES * PER + wave * PER;
+#pragma unroll
+    for (int t = 0; t < MB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(t * 4 + i) * 64 + lane] = acc[t][i];
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (storer) {
+      const float *src = red + (int)(k & 1) * NW_WAVES * PER + (t_st * 4 + ri) * 64 + 16 * rq + c0;
+      f32x4 v = *reinterpret_cast<const f32x4 *>(src);
+      for (int ww = 1; ww < nw; ++ww) v += *reinterpret_cast<const f32x4 *>(src + ww * PER);
+      const int64_t n0 = nt * TILE_N + c0;
+      const uint32_t off = (uint32_t)(((int64_t)r_st * ldy + n0) * 4);
+      const bool row_ok = r_st < rows_st;
+      if (VEC) {
+        bstore4(dy, row_ok && n0 < N ? off : NW_DROP, v);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bstore1(dy, row_ok && n0 + c < N ? off + 4 * c : NW_DROP, v[c]);
+      }
+    }
+  }
+  wait_vm<0>();  // no LDS write may land after the workgroup ends
+}
+
+// Narrow launches: one workgroup per CU (fewer if there are fewer tiles).
+constexpr int NW_CUS = 256;
+
+template <int TYPE, int MB>
+hipError_t launch_narrow(int64_t M, int64_t N, int nb, const uint8_t *qa, const uint8_t *packed,
+                         float *y, int64_t ldy, hipStream_t stream) {
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  dim3 grid((unsigned)(ntiles < NW_CUS ? ntiles : NW_CUS)), block(64 * (nb / NW_KB));
+  const bool vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0) && (N % 4 == 0);
+  // Q6_K tiles are larger: two slots per wave fit beside the sums, Q4_K three
+  constexpr int S = TYPE == 14 ? 2 : 3;
+  const int m = (int)M;
+  if (vec)
+    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, true>), grid, block, 0, stream, m, N, nb,
+                       qa, packed, y, ldy);
+  else
+    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, false>), grid, block, 0, stream, m, N,
+                       nb, qa, packed, y, ldy);
+  return hipGetLastError();
+}
+
+// The narrow kernel serves up to 2 blocks of 16 rows, K of 8 to 16 super-blocks
+// in pairs (2 per wave, at least 4 waves), enough n-tiles to give every CU a
+// stream, a row stride that keeps a 16-row block of y under 2 GB (its store
+// offsets are 32-bit, with the top bit marking a dropped store), and not the
+// debug mode.
+inline bool use_narrow(int mode, int64_t M, int64_t N, int nb, int64_t ldy) {
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  return mode != 2 && M <= 2 * MBLK && nb % NW_KB == 0 && nb >= 4 * NW_KB &&
+         nb <= NW_WAVES * NW_KB && ntiles >= 4 * NW_CUS && ldy <= (int64_t(1) << 25);
+}
+
 template <int TYPE, class SH>
 hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
                    const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn,
@@ -657,6 +857,14 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
                         const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
                         int32_t *dbg_Mn, hipStream_t stream) {
   const int nb = (int)(K / QK);
+  if (use_narrow(mode, M, N, nb, ldy)) {
+    const bool two = M > MBLK;
+    if (type == 12)
+      return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, y, ldy, stream)
+                 : launch_narrow<12, 1>(M, N, nb, qa, packed, y, ldy, stream);
+    return two ? launch_narrow<14, 2>(M, N, nb, qa, packed, y, ldy, stream)
+               : launch_narrow<14, 1>(M, N, nb, qa, packed, y, ldy, stream);
+  }
   if (type == 12)
     return launch_type<12>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
   return launch_type<14>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);

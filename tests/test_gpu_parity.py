@@ -329,3 +329,30 @@ def test_superblock_sums_bit_exact_multi_tile(dq, type_, M):
     oS, oMn = oracle.superblock_sums(type_, xq, xb, W, N)
     assert np.array_equal(S.cpu().numpy(), oS)
     assert np.array_equal(Mn.cpu().numpy(), oMn)
+
+
+# --------------------------------------------------------------------------- #
+# Narrow M (at most 32 rows, K of 8 to 16 super-blocks, at least 1,024        #
+# n-tiles): the persistent weight-streaming kernel.  Every output is compared #
+# with the oracle; padding columns of a strided output stay untouched.        #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("type_,M,N,K,pad", [
+    (oracle.Q6_K, 32, 16400, 4096, 0),   # two 16-row blocks, 8 waves, ragged last n-tile
+    (oracle.Q4_K, 17, 16390, 2048, 0),   # ragged rows, N % 4 != 0 (element stores), 4 waves
+    (oracle.Q6_K, 1, 20000, 3584, 0),    # one row, 7 waves
+    (oracle.Q4_K, 32, 16384, 4096, 3),   # row stride N + 3 (element stores)
+    (oracle.Q6_K, 16, 32776, 2560, 0),   # 5 waves, many n-tiles per workgroup
+    (oracle.Q4_K, 5, 16384, 4096, 0),    # one partial 16-row block, vector stores
+])
+def test_qgemm_narrow_m(dq, type_, M, N, K, pad):
+    W = _weights(type_, N, K, 700 + M + K // 256, full_scales=True)
+    x = synth.activations(np.random.default_rng(800 + M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    ybig = torch.full((M, N + pad), -7.0, device=DEV)
+    dq.qgemm(type_, _act(dq, xq, xd, xb), packed, N, y=ybig)
+    _sync()
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, N:] == -7.0)
+    yr, T = oracle.qgemm_ref(type_, xq, xd, W, N)
+    _check_tol(yb[:, :N], yr, T, f"narrow type {type_} {M}x{N}x{K}")
