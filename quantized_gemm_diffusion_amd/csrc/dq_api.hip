@@ -137,8 +137,11 @@ static int check_gemm(int type, int64_t M, int64_t N, int64_t K, const void *qa,
   if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
   size_t bytes = 0;
   if (int s = act_bytes(M, K, &bytes)) return s;
-  if ((N + dq::TILE_N - 1) / dq::TILE_N > INT32_MAX ||
-      (M + dq::ACT_ROWS - 1) / dq::ACT_ROWS > 65535)
+  // the canvas GEMM's one-dimensional grid: at most (N/32) x (M/16) workgroups
+  // of at most 512 work-items, all numbered in 32 bits
+  const int64_t ncg = (N + 2 * dq::TILE_N - 1) / (2 * dq::TILE_N);
+  const int64_t nmb = (M + dq::ACT_ROWS - 1) / dq::ACT_ROWS;
+  if (ncg * nmb * 512 > (int64_t)UINT32_MAX)
     return fail(DQ_EINVAL, "M or N too large for the GEMM grid");
   if ((K / dq::QK) * (int64_t)dq::Q6K_TILE > INT32_MAX)
     return fail(DQ_EINVAL, "K too large for the GEMM's 32-bit tile offsets");

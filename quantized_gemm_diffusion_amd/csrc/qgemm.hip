@@ -12,8 +12,9 @@
 // one int32 MFMA accumulation over the whole 256-wide super-block yields S.
 //   Q4_K: sc = 8*sh + sl with sl, sh in [0, 7]; the digits q*sl and q*sh are
 //         at most 105, and S = R(q*sl) + 8 * R(q*sh).
-//   Q6_K: v = sc * (q - 32) in [-4064, 4096]; lo = v & 127, hi = v >> 7 (in
-//         [-32, 32]), and S = R(lo) + 128 * R(hi).
+//   Q6_K: v = sc * (q - 32) in [-4064, 4096] = 256 * hi + lo with lo in
+//         [-128, 127] and hi = (v + 128) >> 8 in [-16, 16] (balanced base-256
+//         digits), and S = R(lo) + 256 * R(hi).
 // Every partial sum is an exact int32 (|S| <= 30.7e6 for Q4_K, 1.34e8 for
 // Q6_K).  The Q4_K min term is a 16-deep contraction per super-block done on
 // the f16 MFMA with operands that are exact in f16: bsum = lo6 + rest
@@ -47,7 +48,10 @@ __device__ inline uint32_t byte_pair(uint32_t x, int i) {
   return __builtin_amdgcn_perm(0u, x, 0x0c000c00u | (uint32_t)i | ((uint32_t)i << 16));
 }
 
-// Q6_K: 4 codes (bytes) -> lo / hi digit bytes of v = sc * (q - 32).
+// Q6_K: 4 codes (bytes) -> lo / hi digit bytes of v = sc * (q - 32).  off2
+// holds 128 - 32 * sc, so each 16-bit lane computes v + 128: its high byte is
+// hi, and its low byte with the top bit flipped is the low byte of v, i.e. lo
+// as a two's-complement byte.
 __device__ inline void q6k_digits(uint32_t codes, uint32_t sc2, uint32_t off2, uint32_t &lo,
                                   uint32_t &hi) {
   // even codes (bytes 0, 2) and odd codes (bytes 1, 3) in 16-bit lanes
@@ -56,9 +60,8 @@ __device__ inline void q6k_digits(uint32_t codes, uint32_t sc2, uint32_t off2, u
   const s16x2 s2 = __builtin_bit_cast(s16x2, sc2), o2 = __builtin_bit_cast(s16x2, off2);
   const uint32_t ue = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, ev) * s2 + o2);
   const uint32_t uo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, od) * s2 + o2);
-  lo = __builtin_amdgcn_perm(uo, ue, 0x06020400u) & 0x7f7f7f7fu;
-  // byte 1 of (v << 1) is v >> 7 as a two's-complement byte (|v| < 2^14)
-  hi = __builtin_amdgcn_perm(uo << 1, ue << 1, 0x07030501u);
+  lo = __builtin_amdgcn_perm(uo, ue, 0x06020400u) ^ 0x80808080u;
+  hi = __builtin_amdgcn_perm(uo, ue, 0x07030501u);
 }
 
 // Every global read is a buffer load that writes LDS directly.  One buffer
@@ -195,7 +198,7 @@ __device__ inline void make_digits(const RawQ6 &w, int kq, Digits &D) {
       const int c = 2 * i + h;
       const int sc = (int)(int8_t)((w.sw >> (8 * c)) & 255);
       const uint32_t sc2 = ((uint32_t)sc & 0xffffu) * 0x10001u;
-      const uint32_t off2 = ((uint32_t)(-32 * sc) & 0xffffu) * 0x10001u;
+      const uint32_t off2 = ((uint32_t)(128 - 32 * sc) & 0xffffu) * 0x10001u;
       const uint32_t u = (uint32_t)w.qh[c];
       const uint32_t w0 = (uint32_t)w.rec[i][2 * h], w1 = (uint32_t)w.rec[i][2 * h + 1];
       const uint32_t codes[4] = {(w0 & 0x0f0f0f0fu) | ((u << 4) & 0x30303030u),
@@ -309,7 +312,7 @@ __device__ inline void step_fold(const StepOut &o, const f32x4 &x4, float dw, fl
                                  f32x4 &acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int s_int = Q6 ? o.rl[i] + o.rh[i] * 128 : o.rl[i] + o.rh[i] * 8;
+    const int s_int = Q6 ? o.rl[i] + o.rh[i] * 256 : o.rl[i] + o.rh[i] * 8;
     const float tv = Q6 ? dw * (float)s_int : dw * (float)s_int - dmw * o.mnf[i];
     acc[i] += x4[i] * tv;
   }
@@ -323,7 +326,7 @@ __device__ inline void step_debug(const StepOut &o, int64_t row0, int kq, int64_
     const int64_t row = row0 + 4 * kq + i;
     if (row < M && n < N) {
       const int64_t o_ = (row * N + n) * nb + b;
-      dbg_S[o_] = Q6 ? o.rl[i] + o.rh[i] * 128 : o.rl[i] + o.rh[i] * 8;
+      dbg_S[o_] = Q6 ? o.rl[i] + o.rh[i] * 256 : o.rl[i] + o.rh[i] * 8;
       dbg_Mn[o_] = Q6 ? 0 : (int32_t)o.mnf[i];
     }
   }
@@ -351,6 +354,25 @@ constexpr int lds_bytes() {
   return ring > red ? ring : red;
 }
 constexpr int cap63(int v) { return v > 63 ? 63 : v; }
+
+// Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8), and
+// each XCD has its own L2.  The nrg row groups of one column group read the
+// same weight tiles, so they are placed 8 apart in launch order: they run on
+// one XCD at about the same time, and the tiles come from HBM once.  Column
+// groups past the last complete set of 8 are numbered in order.
+constexpr int XCDS = 8;
+__device__ inline void place(int id, int ncg, int nrg, int &cg, int &rg) {
+  const int full = ncg / XCDS * XCDS;
+  if (id < full * nrg) {
+    const int slot = id / XCDS, xcd = id - slot * XCDS;
+    cg = slot / nrg * XCDS + xcd;
+    rg = slot % nrg;
+  } else {
+    const int t = id - full * nrg;
+    cg = full + t / nrg;
+    rg = t % nrg;
+  }
+}
 
 // One workgroup of WAVES waves: NT 16-column n-tiles x MB 16-row m-blocks x
 // the whole reduction.  Wave w takes super-blocks b = w, w + WAVES, ...; it builds a
@@ -406,9 +428,11 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
-  const int64_t nt0 = (int64_t)blockIdx.x * NT;
-  const int mb0 = (int)blockIdx.y * MB;  // first 16-row block of this workgroup
   const int nmb = (M + MBLK - 1) / MBLK;
+  int cg, rg;  // column group (NT n-tiles) and row group (MB m-blocks) of this workgroup
+  place((int)blockIdx.x, (int)((ntiles + NT - 1) / NT), (nmb + MB - 1) / MB, cg, rg);
+  const int64_t nt0 = (int64_t)cg * NT;
+  const int mb0 = rg * MB;  // first 16-row block of this workgroup
   // this wave's LDS: R activation slabs, then NT tile slots
   uint8_t *ring = lds + wave * wave_lds<Q6, SH>();
   uint8_t *wslot = ring + R * SLAB;
@@ -751,7 +775,7 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
                    hipStream_t stream) {
   const int64_t nmb = (M + MBLK - 1) / MBLK;
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
-  dim3 grid((unsigned)((ntiles + SH::NT - 1) / SH::NT), (unsigned)((nmb + SH::MB - 1) / SH::MB));
+  dim3 grid((unsigned)(((ntiles + SH::NT - 1) / SH::NT) * ((nmb + SH::MB - 1) / SH::MB)));
   dim3 block(64 * SH::WAVES);
   const int m = (int)M;
   const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
