@@ -78,23 +78,15 @@ __device__ inline i32x4 desc(const void *base, uint32_t bytes) {
 }
 
 // Buffer-to-LDS loads: M0 holds the LDS byte address; lane l writes its
-// element at M0 + l * size.  They are written as inline assembly so that the
+// element at M0 + offset + l * size, and the immediate offset moves the
+// global address by the same amount, so consecutive pieces of one copy share
+// an M0 value.  A write of M0 needs one wait state before a load that uses
+// it (the s_nop).  They are written as inline assembly so that the
 // compiler, which cannot tell the LDS slots of the ring apart, does not wait
 // for every one of them before each LDS read; all waits on them are explicit
 // (wait_vm below).  Descriptor, scalar offset and LDS address are
-// wave-uniform.
-__device__ inline void dma16(const i32x4 &d, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(d), "s"(soff)
-               : "memory");
-}
-__device__ inline void dma4(const i32x4 &d, uint32_t lds, int voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(d), "s"(soff)
-               : "memory");
-}
+// wave-uniform.  The copies themselves (dma_record, dma_tile) follow the
+// record and tile layouts below.
 
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (they complete in issue order).  The memory clobber keeps every LDS read
@@ -230,9 +222,21 @@ constexpr int MBLK = ACT_ROWS;  // rows per m-block
 constexpr int SLAB = ACT_RECORD;
 constexpr int GA = ACT_RECORD / 1024;  // loads per step
 
+// A record: 1 KB pieces at offsets 0 .. 3072 from one M0, the last from a
+// second (the immediate offset stops at 4095).
 __device__ inline void dma_record(const i32x4 &d, uint32_t slab, int soff, int lane) {
-#pragma unroll
-  for (int i = 0; i < GA; ++i) dma16(d, slab + 1024 * i, 1024 * i + 16 * lane, soff);
+  static_assert(GA == 5, "record copy is five 1 KB pieces");
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %2, %4, %5 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %2, %4, %5 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %4, %5 offen lds"
+      :
+      : "s"(slab), "s"(slab + 4096), "v"(16 * lane), "v"(4096 + 16 * lane), "s"(d), "s"(soff)
+      : "memory");
 }
 
 // Weight tile of one (n-tile, super-block) into an LDS slot: 1 KB loads for
@@ -250,16 +254,27 @@ constexpr int dma_per_tile() {
 
 template <bool Q6>
 __device__ inline void dma_tile(const i32x4 &d, uint32_t slot, int soff, int lane) {
+  static_assert(Q6K_SC_OFF == 3072 && Q6K_TILE - 256 == 3104, "Q6_K tile tail offsets");
   if (!Q6) {
-    dma16(d, slot, 16 * lane, soff);
-    dma16(d, slot + 1024, 1024 + 16 * lane, soff);
-    dma4(d, slot + 2048, 2048 + 4 * lane, soff);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen offset:1024 lds\n\t"
+        "buffer_load_dword %2, %3, %4 offen offset:2048 lds"
+        :
+        : "s"(slot), "v"(16 * lane), "v"(4 * lane), "s"(d), "s"(soff)
+        : "memory");
   } else {
-    dma16(d, slot, 16 * lane, soff);
-    dma16(d, slot + 1024, 1024 + 16 * lane, soff);
-    dma16(d, slot + 2048, 2048 + 16 * lane, soff);
-    dma4(d, slot + Q6K_SC_OFF, Q6K_SC_OFF + 4 * lane, soff);
-    dma4(d, slot + Q6K_TILE - 256, Q6K_TILE - 256 + 4 * lane, soff);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen offset:2048 lds\n\t"
+        "buffer_load_dword %2, %3, %4 offen offset:3072 lds\n\t"
+        "buffer_load_dword %2, %3, %4 offen offset:3104 lds"
+        :
+        : "s"(slot), "v"(16 * lane), "v"(4 * lane), "s"(d), "s"(soff)
+        : "memory");
   }
 }
 
