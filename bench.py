@@ -10,7 +10,8 @@ Q4_K), gate, up (12288 x 4096 Q4_K) and down (4096 x 12288; Q6_K on odd
 layers, Q4_K on even), then the output projection on 32 gathered canvas rows
 (126,464 x 4096 Q6_K).  Q, K and V read the same quantized input, so their
 weights are stacked at load time into one 12,288 x 4096 matrix and run as one
-GEMM (same bytes and operations, two launches fewer per layer).  Every layer
+GEMM (same bytes and operations, two launches fewer per layer); gate and up
+likewise share an input and run as one 24,576 x 4096 GEMM.  Every layer
 has its own seeded weights (4.6 GB in all, far above the 256 MB last-level
 cache), resident in HBM before timing.
 
@@ -124,7 +125,7 @@ def main():
             "down": up(synth.activations(act_rng, L, F))}
     qbuf = {kk: torch.empty(dq.act_size(L, kk), dtype=torch.uint8, device=dev) for kk in (K, F)}
     outs = {name: torch.empty((L, N), dtype=torch.float32, device=dev)
-            for name, N in (("qkv", 3 * K), ("o", K), ("gate", F), ("up", F), ("down", K))}
+            for name, N in (("qkv", 3 * K), ("o", K), ("gateup", 2 * F), ("down", K))}
     host_keep = {}
     packed = []
     for layer in range(LAYERS):
@@ -134,6 +135,8 @@ def main():
                                                   t, N, KK))
         # Q, K, V stacked along N: one 12288 x 4096 Q4_K matrix
         mats["qkv"] = (Q4_K, 3 * K, K, np.concatenate([mats.pop(n)[3] for n in "qkv"]))
+        # gate and up stacked along N: one 24576 x 4096 Q4_K matrix
+        mats["gateup"] = (Q4_K, 2 * F, K, np.concatenate([mats.pop(n)[3] for n in ("gate", "up")]))
         lp = {}
         for name, (t, N, KK, W) in mats.items():
             if layer < args.cpu_layers:
@@ -174,9 +177,7 @@ def main():
     for lp in packed:
         gemm(lp, "qkv", quant("qkv"))
         gemm(lp, "o", quant("o"))
-        a = quant("ffn")
-        for n in ("gate", "up"):
-            gemm(lp, n, a)
+        gemm(lp, "gateup", quant("ffn"))
         gemm(lp, "down", quant("down"))
     # gathered f32 rows and the index list stand in for pre-quantized activations
     rows_bytes = V * (K // 256) * BLOCK[Q6_K] + ROWS * K * 4 + ROWS * 4 + ROWS * V * 4
@@ -239,7 +240,7 @@ def main():
     log("per-kind (isolated launches):", json.dumps(kernels))
 
     # ------------------------------------------ the step as one HIP graph
-    # The step's 321 launches are captured once and replayed: the host then
+    # The step's launches are captured once and replayed: the host then
     # issues one launch per step instead of one per kernel.  The replay is
     # checked against the eager step (both deterministic) before timing.
     ref = {n: outs[n].clone() for n in ("qkv", "down")}
@@ -318,7 +319,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(dom_bytes),
                      "ops_per_launch": int(dom_ops), "launches": dom_launches},
         "kernels_isolated": kernels,
-        "step_timing": "HIP graph replay of the step's 321 launches",
+        "step_timing": f"HIP graph replay of the step's {len(calls)} launches",
         "device": torch.cuda.get_device_properties(dev).name,
     }
 
@@ -338,11 +339,11 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
     t0 = time.perf_counter()
     for layer in range(args.cpu_layers):
         quantized = {}
-        for name in ("qkv", "o", "gate", "up", "down"):
+        for name in ("qkv", "o", "gateup", "down"):
             W = host_keep[(layer, name)]
             t = Q6_K if W.shape[-1] == 210 else Q4_K
             N, KK = W.shape[0], W.shape[1] * 256
-            src = {"qkv": "qkv", "o": "o", "gate": "ffn", "up": "ffn", "down": "down"}[name]
+            src = {"qkv": "qkv", "o": "o", "gateup": "ffn", "down": "down"}[name]
             if src not in quantized:
                 quantized[src] = oracle.quantize_act(xs[src])
             q, d, b = quantized[src]
