@@ -132,6 +132,53 @@ int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, void *qa,
                     hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * dq_swiglu_quantize_act -- the down projection's input, silu(gate) * up,
+ * quantized as dq_quantize_act does, in one pass.
+ *
+ * Source: Architecture page, "A forward pass", step 2 (the FFN applies SiLU
+ * to gate, multiplies by up and quantizes again for down); "Source map"
+ * (SwiGLU among the GPU kernels).  Per element, all in IEEE binary32 with no
+ * contraction:  x = (g / (1 + e)) * u,  e = exp(-g) computed as: clamp t to
+ * [-87, 88]; n = rint(t * 1.44269502f); r = (t - n*0.693145751953125f)
+ * - n*1.42860677e-06f; p = the degree-7 Taylor polynomial of e^r with
+ * coefficients 1/k! rounded to binary32, by Horner from 1/7!; e = p * 2^n.
+ * Then x is quantized by the dq_quantize_act rule; codes, scales and sums are
+ * bit-identical to any binary32 implementation of these steps.  Inputs must
+ * be finite.
+ *
+ *   gu : device f32, M rows of [gate (F values) | up (F values)], row stride
+ *        ldgu >= 2F floats (the output of a stacked gate/up GEMM); read only.
+ *   qa : device buffer of dq_act_size(M, F) bytes, 16-byte aligned; written
+ *        fully, in the layout above.
+ * Errors: DQ_EINVAL (F % 256, ldgu < 2F, NULL, alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_swiglu_quantize_act(int64_t M, int64_t F, const float *gu, int64_t ldgu, void *qa,
+                           hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_rmsnorm_quantize_act -- RMSNorm of each row, then the quantizer, in one
+ * pass (the input of Q/K/V and of gate/up).
+ *
+ * Source: Architecture page, "A forward pass", step 2 (RMSNorm, then one
+ * int8 quantization reused by Q, K and V); "Source map" (RMSNorm among the
+ * GPU kernels).  Per row, IEEE binary32 with no contraction: 256 partial sums
+ * of squares, partial j over the 4-value groups j, j + 256, j + 512, ... in
+ * increasing order (one square and one addition at a time); a halving tree,
+ * at h = 128, 64, ..., 1: partial[j] += partial[j + h]; mean = partial[0] / K;
+ * rinv = 1 / sqrt(mean + eps) (both correctly rounded); y = (x * rinv) *
+ * gamma.  Then y is quantized by the dq_quantize_act rule, bit-identical to
+ * any binary32 implementation of these steps.  Inputs must be finite.
+ *
+ *   x     : device f32, M rows, row stride ldx >= K floats; read only.
+ *   gamma : device f32, K weights; read only.
+ *   eps   : finite, >= 0.
+ *   qa    : device buffer of dq_act_size(M, K) bytes, 16-byte aligned.
+ * Errors: DQ_EINVAL (K, ldx < K, eps, NULL, alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_rmsnorm_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx,
+                            const float *gamma, float eps, void *qa, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * dq_qgemm -- y[m][n] = sum_k w^[n][k] * x^[m][k] for int8 activations and a
  * repacked K-quant weight matrix.
  *

@@ -61,6 +61,13 @@ def _load():
             lib.dqo_decode_q6k.argtypes = [vp] * 4
             lib.dqo_dequant_row.argtypes = [ctypes.c_int, vp, i64, vp]
             lib.dqo_quantize_act.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+            lib.dqo_exp_f32.restype = ctypes.c_float
+            lib.dqo_exp_f32.argtypes = [ctypes.c_float]
+            lib.dqo_silu_mul.restype = ctypes.c_float
+            lib.dqo_silu_mul.argtypes = [ctypes.c_float, ctypes.c_float]
+            lib.dqo_swiglu_quantize_act.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+            lib.dqo_rmsnorm_quantize_act.argtypes = [i64, i64, vp, i64, vp, ctypes.c_float,
+                                                     vp, vp, vp]
             lib.dqo_subdots.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, i64, i64, vp]
             lib.dqo_superblock_sums.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp,
                                                 i64, i64, vp, vp]
@@ -70,7 +77,8 @@ def _load():
                                                  vp, vp]
             lib.dqo_qgemm_f32.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, i64,
                                           i64, vp, i64]
-            for name in ("dqo_dequant_row", "dqo_quantize_act", "dqo_subdots",
+            for name in ("dqo_dequant_row", "dqo_quantize_act", "dqo_swiglu_quantize_act",
+                         "dqo_rmsnorm_quantize_act", "dqo_subdots",
                          "dqo_superblock_sums", "dqo_qgemm_ref", "dqo_qgemm_ref_points",
                          "dqo_qgemm_f32"):
                 getattr(lib, name).restype = ctypes.c_int
@@ -164,6 +172,48 @@ def quantize_act(x: np.ndarray):
     d = np.zeros((M, K // QK), np.float32)
     bs = np.zeros((M, K // 32), np.int32)
     _check(lib.dqo_quantize_act(M, K, _p(x), K, _p(q), _p(d), _p(bs)))
+    return q, d, bs
+
+
+def exp_f32(t) -> np.ndarray:
+    """The defined binary32 exponential used by SiLU (dq_oracle.c, dqo_exp_f32), elementwise."""
+    lib = _load()
+    t = np.asarray(t, dtype=np.float32)
+    return np.array([lib.dqo_exp_f32(float(v)) for v in t.ravel()], np.float32).reshape(t.shape)
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """silu(g) * u in the defined binary32 steps, elementwise (small arrays)."""
+    lib = _load()
+    g = np.asarray(g, dtype=np.float32)
+    u = np.broadcast_to(np.asarray(u, dtype=np.float32), g.shape)
+    return np.array([lib.dqo_silu_mul(float(a), float(b)) for a, b in zip(g.ravel(), u.ravel())],
+                    np.float32).reshape(g.shape)
+
+
+def swiglu_quantize_act(gu: np.ndarray, F: int):
+    """gu f32 M x (>= 2F): [gate | up] -> quantized silu(gate) * up, as quantize_act returns."""
+    lib = _load()
+    gu = np.ascontiguousarray(gu, dtype=np.float32)
+    M, ld = gu.shape
+    q = np.zeros((M, F), np.int8)
+    d = np.zeros((M, F // QK), np.float32)
+    bs = np.zeros((M, F // 32), np.int32)
+    _check(lib.dqo_swiglu_quantize_act(M, F, _p(gu), ld, _p(q), _p(d), _p(bs)))
+    return q, d, bs
+
+
+def rmsnorm_quantize_act(x: np.ndarray, gamma: np.ndarray, eps: float):
+    """RMSNorm of each row of x (f32 M x K) with weight gamma (K), then quantize_act."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    M, K = x.shape
+    q = np.zeros((M, K), np.int8)
+    d = np.zeros((M, K // QK), np.float32)
+    bs = np.zeros((M, K // 32), np.int32)
+    _check(lib.dqo_rmsnorm_quantize_act(M, K, _p(x), K, _p(gamma), float(eps), _p(q), _p(d),
+                                        _p(bs)))
     return q, d, bs
 
 

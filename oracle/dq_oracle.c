@@ -194,6 +194,103 @@ int dqo_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, int8_t *
 }
 
 /* ------------------------------------------------------------------------ */
+/* The producers of the GEMM inputs (Architecture page, "A forward pass",    */
+/* step 2: RMSNorm, then one int8 quantization for Q, K and V; the FFN       */
+/* applies SiLU to gate, multiplies by up, and quantizes again for down;     */
+/* "Source map": RMSNorm and SwiGLU among the ops).  The codes must come out */
+/* identical on every implementation, so each producer is defined here as a  */
+/* fixed sequence of binary32 operations (no contraction), including the     */
+/* order of its one reduction and its exponential.                           */
+/* ------------------------------------------------------------------------ */
+
+/* exp for SiLU, defined as: clamp t to [-87, 88]; n = rint(t * log2(e));   */
+/* r = (t - n*L1) - n*L2 with L1 + L2 = ln 2 split so that n*L1 is exact     */
+/* (Cody and Waite's range reduction); p = the degree-7 Taylor polynomial    */
+/* of e^r with coefficients 1/k! rounded to binary32, evaluated by Horner;   */
+/* result = p * 2^n, with 2^n built from its exponent bits (exact).          */
+float dqo_exp_f32(float t) {
+  if (t > 88.0f) t = 88.0f;
+  if (t < -87.0f) t = -87.0f;
+  const float n = rintf(t * 1.44269502f);
+  const float r = (t - n * 0.693145751953125f) - n * 1.42860677e-06f;
+  float p = 1.98412698e-04f;  /* 1/7! */
+  p = p * r + 1.38888889e-03f; /* 1/6! */
+  p = p * r + 8.33333377e-03f; /* 1/5! */
+  p = p * r + 4.16666679e-02f; /* 1/4! */
+  p = p * r + 1.66666672e-01f; /* 1/3! */
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const int e = (int)n;
+  const uint32_t bits = (uint32_t)(e + 127) << 23;
+  float scale;
+  memcpy(&scale, &bits, sizeof scale);
+  return p * scale;
+}
+
+/* SwiGLU input of the down projection: silu(g) * u = (g / (1 + exp(-g))) * u */
+float dqo_silu_mul(float g, float u) {
+  const float e = dqo_exp_f32(-g);
+  const float den = 1.0f + e;
+  const float s = g / den;
+  return s * u;
+}
+
+/* gu holds M rows of [gate (F values) | up (F values)], leading dimension  */
+/* ldgu >= 2F; the down projection's input x = silu(gate) * up (M x F) is    */
+/* quantized by dqo_quantize_act.                                            */
+int dqo_swiglu_quantize_act(int64_t M, int64_t F, const float *gu, int64_t ldgu, int8_t *q,
+                            float *d, int32_t *bsum) {
+  if (F % QK || ldgu < 2 * F) return -1;
+  float *x = (float *)malloc(sizeof(float) * (size_t)(M * F > 0 ? M * F : 1));
+  if (!x) return -2;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < F; ++k) x[m * F + k] = dqo_silu_mul(gu[m * ldgu + k], gu[m * ldgu + F + k]);
+  int rc = dqo_quantize_act(M, F, x, F, q, d, bsum);
+  free(x);
+  return rc;
+}
+
+/* RMSNorm of one row, then the quantizer.  The sum of squares is formed in  */
+/* a fixed order: 256 partial sums, partial j taking the 4-value groups      */
+/* g = j, j + 256, j + 512, ... (values 4g .. 4g+3) in increasing order, one */
+/* square and one addition at a time; then a halving tree, at h = 128, 64,   */
+/* ..., 1: partial[j] += partial[j + h] for j < h.  With ss = partial[0]:    */
+/*   mean = ss / K;  rinv = 1 / sqrt(mean + eps)  (both correctly rounded);  */
+/*   y[k] = (x[k] * rinv) * gamma[k].                                        */
+int dqo_rmsnorm_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx,
+                             const float *gamma, float eps, int8_t *q, float *d,
+                             int32_t *bsum) {
+  if (K % QK || ldx < K) return -1;
+  float *y = (float *)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
+  if (!y) return -2;
+  for (int64_t m = 0; m < M; ++m) {
+    const float *xr = x + m * ldx;
+    float part[256];
+    for (int j = 0; j < 256; ++j) part[j] = 0.0f;
+    for (int64_t g = 0; 4 * g < K; ++g) {
+      const int j = (int)(g % 256);
+      for (int i = 0; i < 4; ++i) {
+        const float v = xr[4 * g + i];
+        const float sq = v * v;
+        part[j] = part[j] + sq;
+      }
+    }
+    for (int h = 128; h >= 1; h /= 2)
+      for (int j = 0; j < h; ++j) part[j] = part[j] + part[j + h];
+    const float mean = part[0] / (float)K;
+    const float rinv = 1.0f / sqrtf(mean + eps);
+    for (int64_t k = 0; k < K; ++k) {
+      const float t = xr[k] * rinv;
+      y[m * K + k] = t * gamma[k];
+    }
+  }
+  int rc = dqo_quantize_act(M, K, y, K, q, d, bsum);
+  free(y);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-sub-block integer dots.  For activation row m, weight row n,          */
 /* super-block b and sub-block j:                                            */
 /*   Q4_K (J = 8, width 32):  dot = sum q_w * q_x        (q_w in [0,15])     */

@@ -7,8 +7,8 @@ the library is missing, every call raises.  torch supplies device memory and
 the current stream; tensors must live on a GPU.
 
 Names follow the C ABI:
-  packed_size, repack_weights, act_size, quantize_act, qgemm,
-  qgemm_rows_workspace, qgemm_rows, debug_superblock_sums.
+  packed_size, repack_weights, act_size, quantize_act, swiglu_quantize_act,
+  rmsnorm_quantize_act, qgemm, qgemm_rows_workspace, qgemm_rows, debug_superblock_sums.
 Quantized activations travel as an ``Act`` (the device buffer in the record
 layout that include/dq.h documents, with its M and K).
 """
@@ -31,8 +31,8 @@ DQ_OK, DQ_EINVAL, DQ_EUNSUPPORTED, DQ_EWORKSPACE, DQ_EHIP = 0, 1, 2, 3, 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdq.so")
 
 EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_weights",
-           "dq_act_size", "dq_quantize_act", "dq_qgemm", "dq_qgemm_rows_workspace",
-           "dq_qgemm_rows", "dq_debug_superblock_sums")
+           "dq_act_size", "dq_quantize_act", "dq_swiglu_quantize_act", "dq_rmsnorm_quantize_act",
+           "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_debug_superblock_sums")
 ACT_RECORD = 5120  # bytes per (super-block, 16-row block) record
 
 
@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dq_repack_weights": [i32, i64, i64, vp, vp, vp],
             "dq_act_size": [i64, i64, psz],
             "dq_quantize_act": [i64, i64, vp, i64, vp, vp],
+            "dq_swiglu_quantize_act": [i64, i64, vp, i64, vp, vp],
+            "dq_rmsnorm_quantize_act": [i64, i64, vp, i64, vp, ctypes.c_float, vp, vp],
             "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
             "dq_qgemm_rows_workspace": [i64, i64, psz],
             "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
@@ -153,6 +155,47 @@ def quantize_act(x: torch.Tensor, out: torch.Tensor | None = None) -> Act:
         raise ValueError(f"out must be a contiguous buffer of at least {nbytes} bytes")
     _check(lib.dq_quantize_act(M, K, _ptr(x), x.stride(0) if M > 1 else K, _ptr(out),
                                _stream(x)), "dq_quantize_act")
+    return Act(out, M, K)
+
+
+def _act_out(M: int, K: int, out, dev):
+    nbytes = act_size(M, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _need(out, torch.uint8, "out")
+    if out.numel() < nbytes or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous buffer of at least {nbytes} bytes")
+    return out
+
+
+def swiglu_quantize_act(gu: torch.Tensor, F: int, out: torch.Tensor | None = None) -> Act:
+    """f32 [M, >= 2F] rows of [gate | up] -> Act of silu(gate) * up (M x F)."""
+    lib = load_library()
+    _need(gu, torch.float32, "gu")
+    if gu.dim() != 2 or gu.stride(1) != 1 or gu.shape[1] < 2 * F:
+        raise ValueError("gu must be 2-D [M, >= 2F] with unit column stride")
+    M = gu.shape[0]
+    out = _act_out(M, F, out, gu.device)
+    _check(lib.dq_swiglu_quantize_act(M, F, _ptr(gu), gu.stride(0) if M > 1 else 2 * F,
+                                      _ptr(out), _stream(gu)), "dq_swiglu_quantize_act")
+    return Act(out, M, F)
+
+
+def rmsnorm_quantize_act(x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                         out: torch.Tensor | None = None) -> Act:
+    """f32 [M, K] -> Act of RMSNorm(x) * gamma."""
+    lib = load_library()
+    _need(x, torch.float32, "x")
+    _need(gamma, torch.float32, "gamma")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    if gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous vector of K weights")
+    out = _act_out(M, K, out, x.device)
+    _check(lib.dq_rmsnorm_quantize_act(M, K, _ptr(x), x.stride(0) if M > 1 else K, _ptr(gamma),
+                                       float(eps), _ptr(out), _stream(x)),
+           "dq_rmsnorm_quantize_act")
     return Act(out, M, K)
 
 

@@ -1,6 +1,7 @@
 // dq_api.hip -- the C ABI of libdq (declared in include/dq.h): argument
 // checks on the host, then one or two kernel launches on the caller's stream.
 // Nothing here allocates device memory or synchronizes.
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -127,6 +128,35 @@ int dq_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx, void *qa,
   return launched(dq::launch_quantize(M, K, x, ldx, nullptr, 0, static_cast<uint8_t *>(qa),
                                       nullptr, stream),
                   "dq_quantize_act");
+}
+
+int dq_swiglu_quantize_act(int64_t M, int64_t F, const float *gu, int64_t ldgu, void *qa,
+                           hipStream_t stream) {
+  size_t bytes = 0;
+  if (int s = dq_act_size(M, F, &bytes)) return s;
+  if (ldgu < 2 * F)
+    return fail(DQ_EINVAL, "ldgu = %lld < 2F = %lld", (long long)ldgu, (long long)(2 * F));
+  if (M == 0) return ok();
+  if (!gu || !qa) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(qa, 16) || !aligned(gu, 4))
+    return fail(DQ_EINVAL, "qa must be 16-byte aligned, gu 4-byte aligned");
+  return launched(dq::launch_swiglu_quantize(M, F, gu, ldgu, static_cast<uint8_t *>(qa), stream),
+                  "dq_swiglu_quantize_act");
+}
+
+int dq_rmsnorm_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx,
+                            const float *gamma, float eps, void *qa, hipStream_t stream) {
+  size_t bytes = 0;
+  if (int s = dq_act_size(M, K, &bytes)) return s;
+  if (ldx < K) return fail(DQ_EINVAL, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(DQ_EINVAL, "eps must be finite and >= 0");
+  if (M == 0) return ok();
+  if (!x || !gamma || !qa) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(qa, 16) || !aligned(x, 4) || !aligned(gamma, 4))
+    return fail(DQ_EINVAL, "qa must be 16-byte aligned, x and gamma 4-byte aligned");
+  return launched(dq::launch_rmsnorm_quantize(M, K, x, ldx, gamma, eps, static_cast<uint8_t *>(qa),
+                                              stream),
+                  "dq_rmsnorm_quantize_act");
 }
 
 static int check_gemm(int type, int64_t M, int64_t N, int64_t K, const void *qa,

@@ -66,6 +66,11 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // record layout; err[m] flags an index outside [0, L).
 hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, const int32_t *idx,
                            int64_t L, uint8_t *qa, int32_t *err, hipStream_t stream);
+hipError_t launch_swiglu_quantize(int64_t M, int64_t F, const float *gu, int64_t ldgu,
+                                  uint8_t *qa, hipStream_t stream);
+hipError_t launch_rmsnorm_quantize(int64_t M, int64_t K, const float *x, int64_t ldx,
+                                   const float *gamma, float eps, uint8_t *qa,
+                                   hipStream_t stream);
 hipError_t launch_repack(int type, int64_t N, int64_t K, const uint8_t *src, uint8_t *dst,
                          hipStream_t stream);
 // mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers.

@@ -12,6 +12,13 @@
 // [-127, 127]; the 8 lanes of each 32-group sum their codes.  All arithmetic is binary32 with no
 // contraction, so codes match any other binary32 implementation of the same
 // steps bit for bit.  Padding rows (m >= M) write zeros.
+//
+// Two fused producers run the same quantizer on what the layer computes just
+// before a GEMM ("A forward pass", step 2: RMSNorm, then one quantization for
+// Q, K and V; the FFN applies SiLU to gate, multiplies by up and quantizes
+// again for down; "Source map": RMSNorm and SwiGLU among the GPU kernels).
+// Each is a fixed sequence of binary32 operations, including the order of
+// its reduction and its exponential, so the codes are reproducible exactly.
 #include "dq_internal.h"
 
 // every step below is one binary32 operation; nothing may be fused
@@ -57,6 +64,44 @@ __device__ inline int group8_sum(int s) {
   return s;
 }
 
+// The quantizer for one (row, 256-block): lane l holds values 4l .. 4l+3 in
+// v; the wave writes row r of the record at rec.  Every lane of the wave
+// takes part (the maximum and the group sums are reductions over the wave).
+__device__ inline void quantize_lane(const float (&v)[4], uint8_t *__restrict__ rec, int r,
+                                     int lane) {
+  const float amax =
+      wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+
+  int c[4] = {0, 0, 0, 0};
+  if (amax != 0.0f) {
+    const float inv = 127.0f / amax;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float t = __builtin_rintf(v[i] * inv);
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      c[i] = (int)t;
+    }
+  }
+  // codes: lane owns bytes 4*lane .. 4*lane+3, i.e. unit u = lane/4 of the row
+  const uint32_t word = (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) |
+                        ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)(c[3] & 255) << 24);
+  const int u = lane >> 2;
+  *reinterpret_cast<uint32_t *>(rec + r * QK + 16 * (u ^ r) + 4 * (lane & 3)) = word;
+
+  const int s = group8_sum(c[0] + c[1] + c[2] + c[3]);
+  if ((lane & 7) == 0) {
+    // (lo, hi) = (s & 63, s - lo): both exact in binary16
+    const int lo = s & 63;
+    const _Float16 h[2] = {(_Float16)(float)lo, (_Float16)(float)(s - lo)};
+    *reinterpret_cast<uint32_t *>(rec + ACT_SUMS_OFF + r * 32 + 4 * (lane >> 3)) =
+        __builtin_bit_cast(uint32_t, h);
+  }
+  if (lane == 0)
+    *reinterpret_cast<float *>(rec + ACT_DX_OFF + 4 * r) = amax != 0.0f ? amax / 127.0f : 0.0f;
+  // the record's zero tail: 448 bytes, 28 per row
+  if (lane < 7) *reinterpret_cast<uint32_t *>(rec + ACT_PAD_OFF + 28 * r + 4 * lane) = 0u;
+}
+
 template <bool VEC, bool GATHER>
 __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, int nb,
                                                        const float *__restrict__ x, int64_t ldx,
@@ -100,37 +145,141 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, 
     }
   }
 
-  const float amax =
-      wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  quantize_lane(v, rec, r, lane);
+}
 
-  int c[4] = {0, 0, 0, 0};
-  if (amax != 0.0f) {
-    const float inv = 127.0f / amax;
+
+// exp as the SwiGLU producer defines it: clamp t to [-87, 88]; n = rint(t *
+// log2 e); r = (t - n*L1) - n*L2, where L1 + L2 = ln 2 and L1 has few enough
+// significant bits that n*L1 is exact (Cody and Waite's reduction); the
+// degree-7 Taylor polynomial of e^r (coefficients 1/k! in binary32) by
+// Horner; times 2^n, built exactly from its exponent bits.
+__device__ inline float dq_exp(float t) {
+  t = fminf(fmaxf(t, -87.0f), 88.0f);
+  const float n = __builtin_rintf(t * 1.44269502f);
+  const float r = (t - n * 0.693145751953125f) - n * 1.42860677e-06f;
+  float p = 1.98412698e-04f;
+  p = p * r + 1.38888889e-03f;
+  p = p * r + 8.33333377e-03f;
+  p = p * r + 4.16666679e-02f;
+  p = p * r + 1.66666672e-01f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return p * __builtin_bit_cast(float, (uint32_t)((int)n + 127) << 23);
+}
+
+// silu(g) * u = (g / (1 + exp(-g))) * u
+__device__ inline float silu_mul(float g, float u) {
+  const float den = 1.0f + dq_exp(-g);
+  const float s = g / den;
+  return s * u;
+}
+
+// Down-projection input: row m of gu holds [gate (F) | up (F)]; one wave per
+// (row, 256-block) of silu(gate) * up.
+template <bool VEC>
+__global__ __launch_bounds__(256) void swiglu_quantize_kernel(int64_t M, int64_t Mpad, int nb,
+                                                              const float *__restrict__ gu,
+                                                              int64_t ldgu,
+                                                              uint8_t *__restrict__ qa) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
+  if (item >= Mpad * nb) return;  // whole wave exits together
+  const int64_t m = item / nb;
+  const int b = (int)(item - m * nb);
+  const int64_t mb = m / ACT_ROWS;
+  const int r = (int)(m - mb * ACT_ROWS);
+  uint8_t *rec = qa + ((int64_t)b * (Mpad / ACT_ROWS) + mb) * ACT_RECORD;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m < M) {
+    const float *gp = gu + m * ldgu + (int64_t)b * QK + 4 * lane;
+    const float *up = gp + (int64_t)nb * QK;
+    float g[4], u[4];
+    if (VEC) {
+      const f32x4 tg = *reinterpret_cast<const f32x4 *>(gp);
+      const f32x4 tu = *reinterpret_cast<const f32x4 *>(up);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t = __builtin_rintf(v[i] * inv);
-      t = fminf(fmaxf(t, -127.0f), 127.0f);
-      c[i] = (int)t;
+      for (int i = 0; i < 4; ++i) {
+        g[i] = tg[i];
+        u[i] = tu[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g[i] = gp[i];
+        u[i] = up[i];
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = silu_mul(g[i], u[i]);
   }
-  // codes: lane owns bytes 4*lane .. 4*lane+3, i.e. unit u = lane/4 of the row
-  const uint32_t word = (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) |
-                        ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)(c[3] & 255) << 24);
-  const int u = lane >> 2;
-  *reinterpret_cast<uint32_t *>(rec + r * QK + 16 * (u ^ r) + 4 * (lane & 3)) = word;
+  quantize_lane(v, rec, r, lane);
+}
 
-  const int s = group8_sum(c[0] + c[1] + c[2] + c[3]);
-  if ((lane & 7) == 0) {
-    // (lo, hi) = (s & 63, s - lo): both exact in binary16
-    const int lo = s & 63;
-    const _Float16 h[2] = {(_Float16)(float)lo, (_Float16)(float)(s - lo)};
-    *reinterpret_cast<uint32_t *>(rec + ACT_SUMS_OFF + r * 32 + 4 * (lane >> 3)) =
-        __builtin_bit_cast(uint32_t, h);
+// RMSNorm then quantize: one workgroup of 4 waves per (padded) row.  The sum
+// of squares is formed in the order the producer defines: thread j keeps a
+// partial over the 4-value groups j, j + 256, ... in increasing order (one
+// square and one addition at a time), then a halving tree in LDS, at h = 128,
+// 64, ..., 1: partial[j] += partial[j + h].  mean = ss / K, rinv =
+// 1 / sqrt(mean + eps), y = (x * rinv) * gamma; wave w then quantizes blocks
+// w, w + 4, ... of y.
+constexpr int NORM_THREADS = 256;
+
+template <bool VEC>
+__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
+    int64_t M, int64_t Mpad, int nb, const float *__restrict__ x, int64_t ldx,
+    const float *__restrict__ gamma, float eps, uint8_t *__restrict__ qa) {
+  __shared__ float part[NORM_THREADS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m = blockIdx.x;
+  const int64_t mb = m / ACT_ROWS;
+  const int r = (int)(m - mb * ACT_ROWS);
+  const int64_t K = (int64_t)nb * QK;
+  const bool valid = m < M;  // uniform across the workgroup
+  const float *xr = x + (valid ? m : 0) * ldx;
+
+  float rinv = 0.0f;
+  if (valid) {
+    float acc = 0.0f;
+    for (int64_t g = tid; 4 * g < K; g += NORM_THREADS) {
+      float v[4];
+      if (VEC) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(xr + 4 * g);
+        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = xr[4 * g + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sq = v[i] * v[i];
+        acc = acc + sq;
+      }
+    }
+    part[tid] = acc;
+    __syncthreads();
+    for (int h = NORM_THREADS / 2; h >= 1; h >>= 1) {
+      if (tid < h) part[tid] = part[tid] + part[tid + h];
+      __syncthreads();
+    }
+    const float mean = part[0] / (float)K;
+    rinv = 1.0f / __builtin_sqrtf(mean + eps);
   }
-  if (lane == 0)
-    *reinterpret_cast<float *>(rec + ACT_DX_OFF + 4 * r) = amax != 0.0f ? amax / 127.0f : 0.0f;
-  // the record's zero tail: 448 bytes, 28 per row
-  if (lane < 7) *reinterpret_cast<uint32_t *>(rec + ACT_PAD_OFF + 28 * r + 4 * lane) = 0u;
+
+  for (int b = wave; b < nb; b += NORM_THREADS / 64) {
+    uint8_t *rec = qa + ((int64_t)b * (Mpad / ACT_ROWS) + mb) * ACT_RECORD;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      const int64_t k0 = (int64_t)b * QK + 4 * lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float t = xr[k0 + i] * rinv;
+        v[i] = t * gamma[k0 + i];
+      }
+    }
+    quantize_lane(v, rec, r, lane);
+  }
 }
 
 }  // namespace
@@ -158,6 +307,38 @@ hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, co
       hipLaunchKernelGGL((quantize_kernel<false, false>), grid, block, 0, stream, M, Mpad, nb, x,
                          ldx, idx, L, qa, err);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quantize(int64_t M, int64_t F, const float *gu, int64_t ldgu,
+                                  uint8_t *qa, hipStream_t stream) {
+  const int nb = (int)(F / QK);
+  const int64_t Mpad = (M + ACT_ROWS - 1) / ACT_ROWS * ACT_ROWS;
+  const int64_t blocks = (Mpad * nb + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
+  const bool vec = (reinterpret_cast<uintptr_t>(gu) % 16 == 0) && (ldgu % 4 == 0);
+  dim3 grid((unsigned)blocks), block(64 * WAVES_PER_BLOCK);
+  if (vec)
+    hipLaunchKernelGGL((swiglu_quantize_kernel<true>), grid, block, 0, stream, M, Mpad, nb, gu,
+                       ldgu, qa);
+  else
+    hipLaunchKernelGGL((swiglu_quantize_kernel<false>), grid, block, 0, stream, M, Mpad, nb, gu,
+                       ldgu, qa);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize(int64_t M, int64_t K, const float *x, int64_t ldx,
+                                   const float *gamma, float eps, uint8_t *qa,
+                                   hipStream_t stream) {
+  const int nb = (int)(K / QK);
+  const int64_t Mpad = (M + ACT_ROWS - 1) / ACT_ROWS * ACT_ROWS;
+  const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldx % 4 == 0);
+  dim3 grid((unsigned)Mpad), block(NORM_THREADS);
+  if (vec)
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<true>), grid, block, 0, stream, M, Mpad, nb, x,
+                       ldx, gamma, eps, qa);
+  else
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<false>), grid, block, 0, stream, M, Mpad, nb, x,
+                       ldx, gamma, eps, qa);
   return hipGetLastError();
 }
 

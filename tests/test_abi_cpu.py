@@ -74,9 +74,21 @@ def test_host_checks_return_codes(lib):
     assert lib.dq_repack_weights(dq.Q6_K, 32, 256, None, 16, None) == dq.DQ_EINVAL
     assert lib.dq_repack_weights(dq.Q6_K, 32, 256, 16, 8, None) == dq.DQ_EINVAL  # packed misaligned
     assert lib.dq_act_size(1 << 20, 1 << 14, ctypes.byref(out)) == dq.DQ_EINVAL  # > 2^31 bytes
+    # the fused producers
+    assert lib.dq_swiglu_quantize_act(4, 512, 16, 1000, 16, None) == dq.DQ_EINVAL  # ldgu < 2F
+    assert lib.dq_swiglu_quantize_act(4, 300, 16, 600, 16, None) == dq.DQ_EINVAL  # F % 256
+    assert lib.dq_swiglu_quantize_act(4, 512, None, 1024, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_swiglu_quantize_act(4, 512, 16, 1024, 8, None) == dq.DQ_EINVAL  # qa misaligned
+    assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 500, 16, 1e-5, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, 16, -1.0, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, 16, float("nan"), 16, None) == dq.DQ_EINVAL
+    assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, None, 1e-5, 16, None) == dq.DQ_EINVAL
+    assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, 16, 1e-5, 8, None) == dq.DQ_EINVAL
     # empty shapes are valid no-ops
     assert lib.dq_qgemm(dq.Q4_K, 0, 32, 256, None, None, None, 32, None) == dq.DQ_OK
     assert lib.dq_quantize_act(0, 256, None, 256, None, None) == dq.DQ_OK
+    assert lib.dq_swiglu_quantize_act(0, 256, None, 512, None, None) == dq.DQ_OK
+    assert lib.dq_rmsnorm_quantize_act(0, 256, None, 256, None, 0.0, None, None) == dq.DQ_OK
 
 
 @pytest.mark.parametrize("M,K,exp", [

@@ -11,6 +11,11 @@
   from the fields; with unit scales the sums reduce to numpy.matmul.
 * Reference GEMM: numpy float64 brute force from the fields; the oracle's own
   f32 output through the integer decomposition lies within 1e-6 * T.
+* Fused producers: the defined exp within 2 ulp of numpy's float64 exp over
+  its range (and its clamps), SiLU times up against float64, SwiGLU and
+  RMSNorm closed forms (exact codes for integer inputs), exact power-of-two
+  scaling invariance, and RMSNorm against the float64 formula within the
+  quantizer's rounding.
 """
 import os
 
@@ -324,3 +329,79 @@ def test_rows_inputs_gather_then_quantize():
     q, d, bs = oracle.qgemm_rows_inputs(canvas, idx)
     qa, da, ba = oracle.quantize_act(canvas)
     assert np.array_equal(q, qa[idx]) and np.array_equal(d, da[idx]) and np.array_equal(bs, ba[idx])
+
+
+# --------------------------------------------------------------------------- #
+# The fused producers of the GEMM inputs (Architecture page, "A forward pass",  #
+# step 2: RMSNorm, then the Q/K/V quantization; SiLU on gate times up, then the #
+# down quantization).  Pinned to numpy's float64 functions, closed forms and    #
+# exact scaling identities.                                                     #
+# --------------------------------------------------------------------------- #
+def test_exp_within_two_ulp_of_float64_over_its_range():
+    t = np.concatenate([np.linspace(-87.0, 88.0, 40001, dtype=np.float32),
+                        np.float32([0.0, -0.0, 1e-8, -1e-8, 0.3465, -0.3466, 87.99, -86.99])])
+    e = oracle.exp_f32(t).astype(np.float64)
+    ref = np.exp(t.astype(np.float64))
+    assert np.all(np.abs(e - ref) <= 2.0 * 2.0 ** -23 * ref)
+    assert oracle.exp_f32([0.0])[0] == 1.0
+    # clamped outside [-87, 88]
+    assert oracle.exp_f32([100.0])[0] == oracle.exp_f32([88.0])[0]
+    assert oracle.exp_f32([-1e30])[0] == oracle.exp_f32([-87.0])[0]
+
+
+def test_silu_mul_against_float64_and_closed_forms():
+    rng = np.random.default_rng(11)
+    g = np.concatenate([rng.normal(0, 4, 3000), [0.0, 1.0, -1.0, 30.0, -30.0, 80.0, -80.0]])
+    g = g.astype(np.float32)
+    u = rng.normal(0, 2, g.size).astype(np.float32)
+    got = oracle.silu_mul(g, u).astype(np.float64)
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    ref = g64 / (1.0 + np.exp(-g64)) * u64
+    assert np.all(np.abs(got - ref) <= 8 * 2.0 ** -24 * np.abs(ref) + 1e-37)
+    assert oracle.silu_mul([0.0], [5.0])[0] == 0.0
+    # for large g, 1 + e^-g rounds to 1 and silu(g) * u is g * u exactly
+    assert oracle.silu_mul([50.0], [3.0])[0] == np.float32(150.0)
+
+
+def test_swiglu_quantize_closed_form():
+    # gate = 50 makes silu(gate) = 50 exactly; up holds integers with |max| 127,
+    # so the codes are up itself and d = 50
+    rng = np.random.default_rng(12)
+    F = 512
+    up = rng.integers(-127, 128, (3, F)).astype(np.float32)
+    up[:, 0] = 127.0
+    up[:, 256] = -127.0
+    gu = np.concatenate([np.full((3, F), 50.0, np.float32), up], axis=1)
+    q, d, b = oracle.swiglu_quantize_act(gu, F)
+    assert np.array_equal(q, up.astype(np.int8))
+    assert np.all(d == 50.0)
+    assert np.array_equal(b, up.reshape(3, F // 32, 32).sum(axis=2).astype(np.int32))
+    # up = 0 gives all-zero codes and scales
+    gu0 = np.concatenate([rng.normal(0, 1, (2, F)).astype(np.float32),
+                          np.zeros((2, F), np.float32)], axis=1)
+    q0, d0, b0 = oracle.swiglu_quantize_act(gu0, F)
+    assert not q0.any() and not d0.any() and not b0.any()
+
+
+def test_rmsnorm_quantize_closed_forms_and_scaling():
+    K = 1024
+    rng = np.random.default_rng(13)
+    gamma = rng.integers(-127, 128, K).astype(np.float32)
+    gamma[0], gamma[300], gamma[600], gamma[900] = 127.0, -127.0, 127.0, -127.0
+    # all-ones rows: the sum of squares is K exactly, rinv = 1 with eps = 0, y = gamma
+    q, d, b = oracle.rmsnorm_quantize_act(np.ones((2, K), np.float32), gamma, 0.0)
+    assert np.array_equal(q[0], gamma.astype(np.int8)) and np.all(d == 1.0)
+    # with eps = 0 every step scales exactly by powers of two: 2^k x gives the same codes
+    x = rng.normal(0, 1, (4, K)).astype(np.float32)
+    g2 = rng.normal(1, 0.1, K).astype(np.float32)
+    q1, d1, _ = oracle.rmsnorm_quantize_act(x, g2, 0.0)
+    q2, d2, _ = oracle.rmsnorm_quantize_act(x * np.float32(64.0), g2, 0.0)
+    assert np.array_equal(q1, q2) and np.array_equal(d1, d2)
+    # the normalized values agree with the float64 formula (the codes then follow the
+    # quantizer, pinned above): compare dequantized values within the code rounding
+    eps = 1e-5
+    q3, d3, _ = oracle.rmsnorm_quantize_act(x, g2, eps)
+    x64 = x.astype(np.float64)
+    y = x64 / np.sqrt(np.mean(x64 * x64, axis=1, keepdims=True) + eps) * g2.astype(np.float64)
+    deq = q3.astype(np.float64) * np.repeat(d3.astype(np.float64), 256, axis=1)
+    assert np.all(np.abs(deq - y) <= np.repeat(d3.astype(np.float64), 256, axis=1) * 0.5001 + 1e-6)
