@@ -4,8 +4,10 @@
 One timed step is one LLaDA-8B denoising step's GEMM work at canvas L = 160
 (heatdrop.ai card, "What it does": each step reruns the whole model over the
 canvas, so the runtime is a stream of GEMMs; Architecture page, "A forward
-pass"): for each of 32 layers, 4 activation quantizations (Q/K/V share one,
-O, gate/up share one, down) and the 7 projections Q, K, V, O (4096 x 4096
+pass"): for each of 32 layers, 4 activation quantizations (RMSNorm fused in
+front of the one Q/K/V share and of the one gate/up share; O's input as is;
+SiLU(gate) * up fused in front of down's, taken straight from the gate/up
+GEMM's output) and the 7 projections Q, K, V, O (4096 x 4096
 Q4_K), gate, up (12288 x 4096 Q4_K) and down (4096 x 12288; Q6_K on odd
 layers, Q4_K on even), then the output projection on 32 gathered canvas rows
 (126,464 x 4096 Q6_K).  Q, K and V read the same quantized input, so their
@@ -23,6 +25,7 @@ stream), and the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -40,6 +43,7 @@ METRIC = "K-quant×int8 GEMM TOPS + HBM GB/s (% roofline) at LLaDA-8B step shape
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
 L, K, F, V, LAYERS, ROWS = 160, 4096, 12288, 126464, 32, 32
+EPS = 1e-5  # RMSNorm epsilon
 Q4_K, Q6_K = 12, 14
 BLOCK = {Q4_K: 144, Q6_K: 210}
 COPY_MIB = 512
@@ -75,6 +79,14 @@ def gemm_bytes(type_, M, N, K_):
 
 def quant_bytes(M, K_):
     return M * K_ * 4 + M * K_ + M * (K_ // 256) * 4 + M * (K_ // 32) * 4
+
+
+def norm_quant_bytes(M, K_):  # the row, the norm weights, the quantized record
+    return quant_bytes(M, K_) + K_ * 4
+
+
+def swiglu_quant_bytes(M, F_):  # gate and up rows in, the quantized record out
+    return quant_bytes(M, F_) + M * F_ * 4
 
 
 def source_hash():
@@ -120,9 +132,14 @@ def main():
     # ---------------------------------------------------------------- inputs
     t0 = time.perf_counter()
     act_rng = np.random.default_rng(synth.seed(2, 0, 9))
+    # the residual stream in front of attention and of the FFN, and attention's
+    # output (attention is not part of this path); the down projection's input is
+    # made by the step itself from the gate/up GEMM's output
     acts = {"qkv": up(synth.activations(act_rng, L, K)), "o": up(synth.activations(act_rng, L, K)),
-            "ffn": up(synth.activations(act_rng, L, K)),
-            "down": up(synth.activations(act_rng, L, F))}
+            "ffn": up(synth.activations(act_rng, L, K))}
+    norm_rng = np.random.default_rng(synth.seed(2, 0, 8))
+    gammas = [{n: up((1.0 + 0.1 * norm_rng.standard_normal(K)).astype(np.float32))
+               for n in ("qkv", "ffn")} for _ in range(LAYERS)]
     qbuf = {kk: torch.empty(dq.act_size(L, kk), dtype=torch.uint8, device=dev) for kk in (K, F)}
     outs = {name: torch.empty((L, N), dtype=torch.float32, device=dev)
             for name, N in (("qkv", 3 * K), ("o", K), ("gateup", 2 * F), ("down", K))}
@@ -166,6 +183,22 @@ def main():
                       "quantize", 0, quant_bytes(L, kk)))
         return buf
 
+    def norm_quant(li, name):
+        x = acts[name]
+        buf = qbuf[K]
+        calls.append((lib.dq_rmsnorm_quantize_act,
+                      (L, K, x.data_ptr(), K, gammas[li][name].data_ptr(), ctypes.c_float(EPS),
+                       buf.data_ptr()),
+                      "rmsnorm_quantize", 0, norm_quant_bytes(L, K)))
+        return buf
+
+    def swiglu_quant():
+        gu = outs["gateup"]
+        buf = qbuf[F]
+        calls.append((lib.dq_swiglu_quantize_act, (L, F, gu.data_ptr(), 2 * F, buf.data_ptr()),
+                      "swiglu_quantize", 0, swiglu_quant_bytes(L, F)))
+        return buf
+
     def gemm(lp, name, buf):
         t, N, kk, pk = lp[name]
         y = outs[name]
@@ -174,11 +207,11 @@ def main():
         calls.append((lib.dq_qgemm, (t, L, N, kk, buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N),
                       kind, 2 * L * N * kk, gemm_bytes(t, L, N, kk)))
 
-    for lp in packed:
-        gemm(lp, "qkv", quant("qkv"))
+    for li, lp in enumerate(packed):
+        gemm(lp, "qkv", norm_quant(li, "qkv"))
         gemm(lp, "o", quant("o"))
-        gemm(lp, "gateup", quant("ffn"))
-        gemm(lp, "down", quant("down"))
+        gemm(lp, "gateup", norm_quant(li, "ffn"))
+        gemm(lp, "down", swiglu_quant())
     # gathered f32 rows and the index list stand in for pre-quantized activations
     rows_bytes = V * (K // 256) * BLOCK[Q6_K] + ROWS * K * 4 + ROWS * 4 + ROWS * V * 4
     calls.append((lib.dq_qgemm_rows,
@@ -303,7 +336,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "LLaDA-8B denoising step at canvas L=160: 32 layers x (4 int8 "
-                               "activation quantizations + Q/K/V/O 4096x4096, gate/up "
+                               "activation quantizations, two fused with RMSNorm and one with "
+                               "SwiGLU on the gate/up output + Q/K/V/O 4096x4096, gate/up "
                                "12288x4096, down 4096x12288 K-quant GEMMs; down Q6_K on odd "
                                "layers, Q4_K on even) + output projection on 32 of 160 "
                                "gathered rows, 126464x4096 Q6_K",
@@ -325,11 +359,12 @@ def main():
 
     # ------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts)
+        result["cpu_baseline"] = cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts,
+                                                gammas)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
+def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):
     """The oracle, as it stands, on the first layers of the step plus 1/4 of the vocab rows."""
     import oracle
 
@@ -338,16 +373,23 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
     ops = 0
     t0 = time.perf_counter()
     for layer in range(args.cpu_layers):
-        quantized = {}
+        g = {n: gammas[layer][n].cpu().numpy() for n in ("qkv", "ffn")}
+        y_gu = None
         for name in ("qkv", "o", "gateup", "down"):
             W = host_keep[(layer, name)]
             t = Q6_K if W.shape[-1] == 210 else Q4_K
             N, KK = W.shape[0], W.shape[1] * 256
-            src = {"qkv": "qkv", "o": "o", "gateup": "ffn", "down": "down"}[name]
-            if src not in quantized:
-                quantized[src] = oracle.quantize_act(xs[src])
-            q, d, b = quantized[src]
-            oracle.qgemm_f32(t, q, d, b, W, N, threads=th)
+            if name == "qkv":
+                q, d, b = oracle.rmsnorm_quantize_act(xs["qkv"], g["qkv"], EPS)
+            elif name == "o":
+                q, d, b = oracle.quantize_act(xs["o"])
+            elif name == "gateup":
+                q, d, b = oracle.rmsnorm_quantize_act(xs["ffn"], g["ffn"], EPS)
+            else:
+                q, d, b = oracle.swiglu_quantize_act(y_gu, F)
+            y = oracle.qgemm_f32(t, q, d, b, W, N, threads=th)
+            if name == "gateup":
+                y_gu = y
             ops += 2 * L * N * KK
     nv = V // 4
     gq, gd, gb = oracle.qgemm_rows_inputs(canvas_np, idx_np)
@@ -355,7 +397,8 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts):
     ops += 2 * ROWS * nv * K
     dt = time.perf_counter() - t0
     return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": th, "kind": "oracle",
-            "sample": f"oracle quantize + integer-decomposition GEMM on {args.cpu_layers} of 32 "
+            "sample": f"oracle RMSNorm/SwiGLU/plain quantize + integer-decomposition GEMM on "
+                      f"{args.cpu_layers} of 32 "
                       f"layers (all projections, L=160) and 1/4 of the 126464 vocab rows at "
                       f"M=32: {ops / 1e9:.1f} GOP in {dt:.1f} s"}
 

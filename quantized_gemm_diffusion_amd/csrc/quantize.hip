@@ -217,20 +217,21 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(int64_t M, int64_t
   quantize_lane(v, rec, r, lane);
 }
 
-// RMSNorm then quantize: one workgroup of 4 waves per (padded) row.  The sum
-// of squares is formed in the order the producer defines: thread j keeps a
-// partial over the 4-value groups j, j + 256, ... in increasing order (one
-// square and one addition at a time), then a halving tree in LDS, at h = 128,
-// 64, ..., 1: partial[j] += partial[j + h].  mean = ss / K, rinv =
+// RMSNorm then quantize: one workgroup of 16 waves per (padded) row.  The
+// sum of squares is formed in the order the producer defines: thread j < 256
+// keeps a partial over the 4-value groups j, j + 256, ... in increasing order
+// (one square and one addition at a time), then a halving tree in LDS, at
+// h = 128, 64, ..., 1: partial[j] += partial[j + h].  mean = ss / K, rinv =
 // 1 / sqrt(mean + eps), y = (x * rinv) * gamma; wave w then quantizes blocks
-// w, w + 4, ... of y.
-constexpr int NORM_THREADS = 256;
+// w, w + 16, ... of y (one block per wave at K = 4096).
+constexpr int NORM_PARTS = 256;    // partial sums of the defined order
+constexpr int NORM_THREADS = 1024;
 
 template <bool VEC>
 __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
     int64_t M, int64_t Mpad, int nb, const float *__restrict__ x, int64_t ldx,
     const float *__restrict__ gamma, float eps, uint8_t *__restrict__ qa) {
-  __shared__ float part[NORM_THREADS];
+  __shared__ float part[NORM_PARTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m = blockIdx.x;
   const int64_t mb = m / ACT_ROWS;
@@ -241,25 +242,27 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
 
   float rinv = 0.0f;
   if (valid) {
-    float acc = 0.0f;
-    for (int64_t g = tid; 4 * g < K; g += NORM_THREADS) {
-      float v[4];
-      if (VEC) {
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(xr + 4 * g);
-        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
-      } else {
+    if (tid < NORM_PARTS) {
+      float acc = 0.0f;
+      for (int64_t g = tid; 4 * g < K; g += NORM_PARTS) {
+        float v[4];
+        if (VEC) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(xr + 4 * g);
+          v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = xr[4 * g + i];
-      }
+          for (int i = 0; i < 4; ++i) v[i] = xr[4 * g + i];
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sq = v[i] * v[i];
-        acc = acc + sq;
+        for (int i = 0; i < 4; ++i) {
+          const float sq = v[i] * v[i];
+          acc = acc + sq;
+        }
       }
+      part[tid] = acc;
     }
-    part[tid] = acc;
     __syncthreads();
-    for (int h = NORM_THREADS / 2; h >= 1; h >>= 1) {
+    for (int h = NORM_PARTS / 2; h >= 1; h >>= 1) {
       if (tid < h) part[tid] = part[tid] + part[tid + h];
       __syncthreads();
     }
