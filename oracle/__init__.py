@@ -77,10 +77,11 @@ def _load():
                                                  vp, vp]
             lib.dqo_qgemm_f32.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, i64,
                                           i64, vp, i64]
+            lib.dqo_logits_stats.argtypes = [i64, i64, vp, i64, ctypes.c_float, vp, vp]
             for name in ("dqo_dequant_row", "dqo_quantize_act", "dqo_swiglu_quantize_act",
                          "dqo_rmsnorm_quantize_act", "dqo_subdots",
                          "dqo_superblock_sums", "dqo_qgemm_ref", "dqo_qgemm_ref_points",
-                         "dqo_qgemm_f32"):
+                         "dqo_qgemm_f32", "dqo_logits_stats"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -306,3 +307,34 @@ def qgemm_rows_inputs(canvas: np.ndarray, idx: np.ndarray):
     """
     rows = np.ascontiguousarray(np.asarray(canvas, np.float32)[np.asarray(idx, np.int64)])
     return quantize_act(rows)
+
+
+def logits_stats(y: np.ndarray, beta: float = 1.0):
+    """Sampler statistics of each row of a logits matrix (dqo_logits_stats).
+
+    heatdrop.ai card, "The interesting bit", and the aiboss88 news page's
+    capability list: the samplers read the requested rows' logits (LLaDA ranks
+    by the confidence of its greedy prediction, Dream by entropy).  With
+    z = beta * y (binary32): returns (token int32[M], stats float64[M, 4]) where
+    stats[m] = (max z, log sum exp z, entropy of softmax z, softmax probability
+    of the token) and token is the first index of the maximum.
+    """
+    y = np.ascontiguousarray(np.atleast_2d(np.asarray(y, np.float64)))
+    M, N = y.shape
+    token = np.zeros(M, np.int32)
+    stats = np.zeros((M, 4), np.float64)
+    _check(_load().dqo_logits_stats(M, N, _p(y), N, ctypes.c_float(beta), _p(token), _p(stats)))
+    return token, stats
+
+
+def qgemm_rows_sample_ref(type_: int, canvas: np.ndarray, idx: np.ndarray, W, N: int,
+                          beta: float = 1.0, threads=None):
+    """Gathered-row projection followed by the sampler statistics of its rows.
+
+    Returns (token, stats, y, T): the statistics of the plain-definition logits
+    y (f64, M x N) of the rows canvas[idx], and the tolerance scale T of y.
+    """
+    q, d, _ = qgemm_rows_inputs(canvas, idx)
+    y, T = qgemm_ref(type_, q, d, W, N, threads)
+    token, stats = logits_stats(y, beta)
+    return token, stats, y, T

@@ -493,3 +493,53 @@ int dqo_qgemm_f32(int type, int64_t M, int64_t N, int64_t K, const int8_t *qx,
   free(dm);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* What the samplers read from the logits of one requested row (heatdrop.ai  */
+/* card, "The interesting bit": logits exist only for the positions the      */
+/* sampler can commit; aiboss88 news page, capability list: LLaDA remasks    */
+/* the lowest-confidence predictions, Dream orders positions by entropy).    */
+/* With z[n] = beta * y[n], a binary32 product of the binary32 logit (the    */
+/* inverse temperature beta scales the logits before the softmax):           */
+/*   token   = the smallest n with z[n] = max z (greedy prediction);         */
+/*   zmax    = z[token];                                                     */
+/*   lse     = log sum_n exp(z[n])                  (log of the partition);  */
+/*   entropy = -sum_n p[n] log p[n],  p[n] = exp(z[n] - lse), where          */
+/*             log p[n] = z[n] - lse (so an underflowed p[n] adds nothing);  */
+/*   p_top   = exp(zmax - lse)   (the softmax probability of the token: the  */
+/*             confidence low-confidence remasking ranks by).                */
+/* Everything after the product is binary64, summed in increasing n, with    */
+/* the maximum taken out of the exponentials.  y is M rows, leading          */
+/* dimension ldy; stats is M x 4 {zmax, lse, entropy, p_top}.                */
+/* ------------------------------------------------------------------------ */
+int dqo_logits_stats(int64_t M, int64_t N, const double *y, int64_t ldy, float beta,
+                     int32_t *token, double *stats) {
+  if (N <= 0 || ldy < N) return -1;
+  double *z = (double *)malloc(sizeof(double) * (size_t)N);
+  if (!z) return -2;
+  for (int64_t m = 0; m < M; ++m) {
+    const double *yr = y + m * ldy;
+    int64_t best = 0;
+    for (int64_t n = 0; n < N; ++n) {
+      const float zf = beta * (float)yr[n];
+      z[n] = (double)zf;
+      if (z[n] > z[best]) best = n;
+    }
+    const double zmax = z[best];
+    double part = 0.0;
+    for (int64_t n = 0; n < N; ++n) part += exp(z[n] - zmax);
+    const double lse = zmax + log(part);
+    double h = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double logp = z[n] - lse;
+      h -= exp(logp) * logp;
+    }
+    token[m] = (int32_t)best;
+    stats[4 * m + 0] = zmax;
+    stats[4 * m + 1] = lse;
+    stats[4 * m + 2] = h;
+    stats[4 * m + 3] = exp(zmax - lse);
+  }
+  free(z);
+  return 0;
+}

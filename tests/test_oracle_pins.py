@@ -16,6 +16,11 @@
   RMSNorm closed forms (exact codes for integer inputs), exact power-of-two
   scaling invariance, and RMSNorm against the float64 formula within the
   quantizer's rounding.
+* Sampler statistics of the logits: closed forms (uniform and two-level
+  rows), scipy's logsumexp and entropy on random rows, the first index on
+  ties, the binary32 product deciding the token, exact power-of-two
+  temperature and integer shift invariance, and no overflow at large
+  magnitudes.
 """
 import os
 
@@ -405,3 +410,73 @@ def test_rmsnorm_quantize_closed_forms_and_scaling():
     y = x64 / np.sqrt(np.mean(x64 * x64, axis=1, keepdims=True) + eps) * g2.astype(np.float64)
     deq = q3.astype(np.float64) * np.repeat(d3.astype(np.float64), 256, axis=1)
     assert np.all(np.abs(deq - y) <= np.repeat(d3.astype(np.float64), 256, axis=1) * 0.5001 + 1e-6)
+
+
+# --- sampler statistics of the logits ---------------------------------------
+
+def test_logits_stats_uniform_and_two_level_closed_forms():
+    N = 1000
+    tok, st = oracle.logits_stats(np.full((1, N), 2.5), 1.0)
+    assert tok[0] == 0
+    np.testing.assert_allclose(st[0], [2.5, 2.5 + np.log(N), np.log(N), 1.0 / N], rtol=1e-13)
+    # k entries at a, N - k at b
+    k, a, b = 7, 3.0, -1.0
+    y = np.full(N, b)
+    pos = np.random.default_rng(3).choice(N, k, replace=False)
+    y[pos] = a
+    tok, st = oracle.logits_stats(y[None, :], 1.0)
+    zsum = k * np.exp(a) + (N - k) * np.exp(b)
+    pa, pb = np.exp(a) / zsum, np.exp(b) / zsum
+    assert tok[0] == pos.min()
+    np.testing.assert_allclose(st[0], [a, np.log(zsum), -k * pa * np.log(pa) - (N - k) * pb * np.log(pb), pa],
+                               rtol=1e-12)
+
+
+def test_logits_stats_against_scipy():
+    from scipy.special import logsumexp, softmax
+    from scipy.stats import entropy
+    rng = np.random.default_rng(11)
+    for scale, beta in ((1.0, 1.0), (30.0, 0.05), (0.01, 8.0)):
+        y = (rng.standard_normal((5, 4099)) * scale).astype(np.float32).astype(np.float64)
+        tok, st = oracle.logits_stats(y, beta)
+        z = (np.float32(beta) * y.astype(np.float32)).astype(np.float64)
+        np.testing.assert_array_equal(tok, np.argmax(z, axis=1))
+        np.testing.assert_array_equal(st[:, 0], z.max(axis=1))
+        np.testing.assert_allclose(st[:, 1], logsumexp(z, axis=1), rtol=1e-13)
+        np.testing.assert_allclose(st[:, 2], entropy(softmax(z, axis=1), axis=1), rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(st[:, 3], softmax(z, axis=1).max(axis=1), rtol=1e-12)
+
+
+def test_logits_stats_token_is_first_maximum_of_the_binary32_product():
+    tok, _ = oracle.logits_stats(np.array([[0.0, 5.0, 2.0, 5.0, -1.0]]), 1.0)
+    assert tok[0] == 1
+    # 1 + 2^-30 rounds to 1.0f: a tie in binary32, so the first index wins
+    tok, st = oracle.logits_stats(np.array([[1.0, 1.0 + 2.0 ** -30]]), 1.0)
+    assert tok[0] == 0 and st[0, 0] == 1.0
+    # 3 * 0.1f and 3 * 0.1 differ: the binary32 product is the one reported
+    _, st = oracle.logits_stats(np.array([[3.0]]), 0.1)
+    assert st[0, 0] == float(np.float32(3.0) * np.float32(0.1))
+
+
+def test_logits_stats_temperature_and_shift_invariance():
+    rng = np.random.default_rng(5)
+    y = rng.integers(-200, 200, size=(4, 777)).astype(np.float64)
+    t1, s1 = oracle.logits_stats(y, 0.25)
+    t2, s2 = oracle.logits_stats(0.25 * y, 1.0)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(s1, s2)
+    t3, s3 = oracle.logits_stats(y + 1000.0, 1.0)
+    t4, s4 = oracle.logits_stats(y, 1.0)
+    np.testing.assert_array_equal(t3, t4)
+    np.testing.assert_allclose(s3[:, :2] - 1000.0, s4[:, :2], rtol=0, atol=1e-9)
+    np.testing.assert_allclose(s3[:, 2:], s4[:, 2:], rtol=1e-9, atol=1e-15)
+
+
+def test_logits_stats_large_magnitudes_do_not_overflow():
+    tok, st = oracle.logits_stats(np.array([[1e4, 0.0, -1e4, 9990.0]]), 1.0)
+    assert tok[0] == 0
+    assert np.all(np.isfinite(st))
+    np.testing.assert_allclose(st[0, 1], 1e4 + np.log1p(np.exp(-10.0)), rtol=1e-14)
+    p = 1.0 / (1.0 + np.exp(-10.0))
+    np.testing.assert_allclose(st[0, 2], -p * np.log(p) - (1 - p) * np.log(1 - p), rtol=1e-9)
+    np.testing.assert_allclose(st[0, 3], p, rtol=1e-11)  # exp of a difference of ~1e4-sized values
