@@ -235,6 +235,57 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * Sampler statistics of requested rows of logits.
+ *
+ * Source: heatdrop.ai card, "The interesting bit" (the output projection
+ * computes logits only for the positions the sampler can commit) and the
+ * aiboss88 news page's capability list (each model's own sampler: LLaDA's
+ * low-confidence remasking, Dream's entropy ordering).  What the samplers
+ * read from a row is reduced on the device, so the M x N logits need not be
+ * kept.  With z[n] = beta * y[n] (binary32; beta is the inverse temperature):
+ *   token[i]        = the smallest n with z[n] = max z   (greedy prediction)
+ *   stats[4*i + 0]  = max z
+ *   stats[4*i + 1]  = log sum_n exp z[n]                 (log-partition)
+ *   stats[4*i + 2]  = -sum_n p[n] log p[n], p = softmax(z)  (entropy)
+ *   stats[4*i + 3]  = p[token[i]]                        (its confidence)
+ * token and max are exact functions of z; the three sums are binary32 with a
+ * relative error of a few 1e-6.  Logits must be finite and |z| < 3e38 (out
+ * of that domain the results are unspecified).
+ *
+ * dq_logits_stats_workspace / dq_logits_stats -- the statistics of the M rows
+ * of an f32 logits matrix y (row stride ldy >= N floats).
+ *   beta  : finite, > 0.
+ *   token : device int32 [M];  stats : device f32 [M x 4], 4-byte aligned.
+ *   ws    : device workspace of at least dq_logits_stats_workspace(M, N)
+ *           bytes, 16-byte aligned; its contents are overwritten.
+ * Errors: DQ_EINVAL (M < 0, N < 1, ldy < N, beta, NULL, alignment, too many
+ *         rows for one launch), DQ_EWORKSPACE, DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_logits_stats_workspace(int64_t M, int64_t N, size_t *bytes);
+int dq_logits_stats(int64_t M, int64_t N, const float *y, int64_t ldy, float beta,
+                    int32_t *token, float *stats, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_qgemm_rows_sample_workspace / dq_qgemm_rows_sample -- the output
+ * projection on the requested canvas rows (as dq_qgemm_rows) with the sampler
+ * statistics above computed in the GEMM's epilogue: the logits are reduced
+ * where they are formed and never written to memory.  The logits reduced are
+ * bit-identical to the y that dq_qgemm_rows writes for the same arguments.
+ *   canvas, ldc, idx, packed : as for dq_qgemm_rows (idx flags likewise in the
+ *           first 4*M bytes of ws).
+ *   beta, token, stats       : as for dq_logits_stats.
+ *   ws    : at least dq_qgemm_rows_sample_workspace(M, N, K) bytes, 256-byte
+ *           aligned; its contents are overwritten.
+ * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (shape, beta, NULL, alignment),
+ *         DQ_EWORKSPACE, DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_qgemm_rows_sample_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes);
+int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
+                         const float *canvas, int64_t ldc, const int32_t *idx, const void *packed,
+                         float beta, int32_t *token, float *stats, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * dq_debug_superblock_sums -- test hook.  Runs the dq_qgemm kernel with its
  * fold replaced by stores of the exact per-super-block integers, so that the
  * integer part of the production code path can be compared bit for bit:

@@ -32,7 +32,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdq.so")
 
 EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_weights",
            "dq_act_size", "dq_quantize_act", "dq_swiglu_quantize_act", "dq_rmsnorm_quantize_act",
-           "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_debug_superblock_sums")
+           "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_logits_stats_workspace",
+           "dq_logits_stats", "dq_qgemm_rows_sample_workspace", "dq_qgemm_rows_sample",
+           "dq_debug_superblock_sums")
 ACT_RECORD = 5120  # bytes per (super-block, 16-row block) record
 
 
@@ -78,6 +80,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
             "dq_qgemm_rows_workspace": [i64, i64, psz],
             "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
+            "dq_logits_stats_workspace": [i64, i64, psz],
+            "dq_logits_stats": [i64, i64, vp, i64, ctypes.c_float, vp, vp, vp, sz, vp],
+            "dq_qgemm_rows_sample_workspace": [i64, i64, i64, psz],
+            "dq_qgemm_rows_sample": [i32, i64, i64, i64, i64, vp, i64, vp, vp, ctypes.c_float, vp,
+                                     vp, vp, sz, vp],
             "dq_debug_superblock_sums": [i32, i64, i64, i64, vp, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
@@ -261,6 +268,85 @@ def qgemm_rows(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packed: torc
                              y.stride(0) if M > 1 else N, _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(canvas)), "dq_qgemm_rows")
     return y, ws
+
+
+def _stats_out(M: int, token, stats, dev):
+    if token is None:
+        token = torch.empty(M, dtype=torch.int32, device=dev)
+    if stats is None:
+        stats = torch.empty((M, 4), dtype=torch.float32, device=dev)
+    _need(token, torch.int32, "token")
+    _need(stats, torch.float32, "stats")
+    if token.numel() < M or not token.is_contiguous():
+        raise ValueError("token must be a contiguous int32 tensor of at least M entries")
+    if stats.numel() < 4 * M or not stats.is_contiguous():
+        raise ValueError("stats must be a contiguous f32 tensor of at least 4 M entries")
+    return token, stats
+
+
+def _ws(nbytes: int, ws, dev):
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(ws, torch.uint8, "ws")
+    return ws
+
+
+def logits_stats_workspace(M: int, N: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_logits_stats_workspace(M, N, ctypes.byref(out)), "dq_logits_stats_workspace")
+    return out.value
+
+
+def logits_stats(y: torch.Tensor, beta: float = 1.0, token=None, stats=None, ws=None):
+    """Sampler statistics of each row of f32 logits y [M, N]: (token int32 [M],
+    stats f32 [M, 4] = max, log-partition, entropy, top probability of
+    softmax(beta * y)), ws."""
+    lib = load_library()
+    _need(y, torch.float32, "y")
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be 2-D with unit column stride")
+    M, N = y.shape
+    token, stats = _stats_out(M, token, stats, y.device)
+    ws = _ws(logits_stats_workspace(M, N), ws, y.device)
+    _check(lib.dq_logits_stats(M, N, _ptr(y), y.stride(0) if M > 1 else N, beta, _ptr(token),
+                               _ptr(stats), _ptr(ws), ws.numel(), _stream(y)), "dq_logits_stats")
+    return token, stats, ws
+
+
+def qgemm_rows_sample_workspace(M: int, N: int, K: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_qgemm_rows_sample_workspace(M, N, K, ctypes.byref(out)),
+           "dq_qgemm_rows_sample_workspace")
+    return out.value
+
+
+def qgemm_rows_sample(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packed: torch.Tensor,
+                      N: int, beta: float = 1.0, token=None, stats=None, ws=None):
+    """The output projection on canvas rows idx with the sampler statistics
+    formed in its epilogue (no logits are stored): (token, stats, ws) as for
+    logits_stats."""
+    lib = load_library()
+    _need(canvas, torch.float32, "canvas")
+    _need(idx, torch.int32, "idx")
+    if canvas.dim() != 2 or canvas.stride(1) != 1:
+        raise ValueError("canvas must be 2-D with unit column stride")
+    L, K = canvas.shape
+    M = idx.numel()
+    if not idx.is_contiguous():
+        raise ValueError("idx must be contiguous")
+    _need(packed, torch.uint8, "packed")
+    if packed.numel() < packed_size(type_, N, K) or not packed.is_contiguous():
+        raise ValueError("packed is smaller than packed_size(type, N, K)")
+    dev = canvas.device
+    token, stats = _stats_out(M, token, stats, dev)
+    ws = _ws(qgemm_rows_sample_workspace(M, N, K), ws, dev)
+    _check(lib.dq_qgemm_rows_sample(type_, L, M, N, K, _ptr(canvas),
+                                    canvas.stride(0) if L > 1 else K, _ptr(idx), _ptr(packed),
+                                    beta, _ptr(token), _ptr(stats), _ptr(ws), ws.numel(),
+                                    _stream(canvas)), "dq_qgemm_rows_sample")
+    return token, stats, ws
 
 
 def debug_superblock_sums(type_: int, act: Act, packed: torch.Tensor, N: int):

@@ -9,6 +9,7 @@
 
 #include "dq.h"
 #include "dq_internal.h"
+#include "row_stats.h"
 
 namespace {
 
@@ -235,6 +236,97 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
   return launched(dq::launch_qgemm(type, 1, M, N, K, qa, static_cast<const uint8_t *>(packed), y,
                                    ldy, nullptr, nullptr, stream),
                   "dq_qgemm_rows (gemm)");
+}
+
+static int check_beta(float beta) {
+  if (!(beta > 0.0f) || !isfinite(beta)) return fail(DQ_EINVAL, "beta must be finite and > 0");
+  return DQ_OK;
+}
+
+static size_t stats_part_bytes(int64_t M, int64_t npart) {
+  return (size_t)M * (size_t)npart * sizeof(float4);
+}
+
+int dq_logits_stats_workspace(int64_t M, int64_t N, size_t *bytes) {
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (N < 1 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
+  *bytes = stats_part_bytes(M, dq::logits_stats_parts(N));
+  return ok();
+}
+
+int dq_logits_stats(int64_t M, int64_t N, const float *y, int64_t ldy, float beta,
+                    int32_t *token, float *stats, void *ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  if (int s = dq_logits_stats_workspace(M, N, &need)) return s;
+  if (ldy < N) return fail(DQ_EINVAL, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
+  if (int s = check_beta(beta)) return s;
+  const int npart = dq::logits_stats_parts(N);
+  // one workgroup of 256 work-items per (row, partial), numbered in 32 bits
+  if (M * npart * 256 > (int64_t)UINT32_MAX) return fail(DQ_EINVAL, "too many rows for one launch");
+  if (M == 0) return ok();
+  if (!y || !token || !stats) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(y, 4) || !aligned(token, 4) || !aligned(stats, 4))
+    return fail(DQ_EINVAL, "y, token and stats must be 4-byte aligned");
+  if (!ws || ws_bytes < need)
+    return fail(DQ_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned(ws, 16)) return fail(DQ_EINVAL, "workspace must be 16-byte aligned");
+  float4 *part = static_cast<float4 *>(ws);
+  hipError_t e = dq::launch_logits_stats_partial(M, N, y, ldy, beta, npart, part, stream);
+  if (e != hipSuccess) return launched(e, "dq_logits_stats (partials)");
+  return launched(dq::launch_row_stats_finish(M, npart, part, token, stats, stream),
+                  "dq_logits_stats (finish)");
+}
+
+// Workspace: [flags | quantized-activation records | partial states], the
+// first two as for dq_qgemm_rows, the states 16-byte aligned after them.
+int dq_qgemm_rows_sample_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes) {
+  size_t rows = 0;
+  if (N < 1 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if (int s = dq_qgemm_rows_workspace(M, K, &rows)) return s;
+  *bytes = rows + stats_part_bytes(M, dq::qgemm_stats_parts(M, N, K));
+  return ok();
+}
+
+int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
+                         const float *canvas, int64_t ldc, const int32_t *idx, const void *packed,
+                         float beta, int32_t *token, float *stats, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (int s = check_type(type)) return s;
+  if (int s = check_k(K)) return s;
+  if (L < 0 || L > kMaxRows) return fail(DQ_EINVAL, "L = %lld out of range", (long long)L);
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (N < 1 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if (ldc < K) return fail(DQ_EINVAL, "ldc = %lld < K = %lld", (long long)ldc, (long long)K);
+  if (int s = check_beta(beta)) return s;
+  // the finish launch: one 256-wide workgroup per row
+  if (M * 256 > (int64_t)UINT32_MAX) return fail(DQ_EINVAL, "too many rows for one launch");
+  if (M == 0) return ok();
+  if (!canvas || !idx || !packed || !token || !stats)
+    return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(canvas, 4) || !aligned(idx, 4) || !aligned(token, 4) || !aligned(stats, 4) ||
+      !aligned(packed, 16))
+    return fail(DQ_EINVAL,
+                "canvas, idx, token, stats must be 4-byte aligned, packed 16-byte aligned");
+  size_t need = 0, rows = 0;
+  if (int s = dq_qgemm_rows_sample_workspace(M, N, K, &need)) return s;
+  if (int s = dq_qgemm_rows_workspace(M, K, &rows)) return s;
+  if (!ws || ws_bytes < need)
+    return fail(DQ_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned(ws, 256)) return fail(DQ_EINVAL, "workspace must be 256-byte aligned");
+  uint8_t *w = static_cast<uint8_t *>(ws);
+  uint8_t *qa = w + rows_ws_flags(M);
+  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
+  int32_t *flags = reinterpret_cast<int32_t *>(w);
+  float4 *part = reinterpret_cast<float4 *>(w + rows);
+  const int npart = dq::qgemm_stats_parts(M, N, K);
+  hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
+  if (e != hipSuccess) return launched(e, "dq_qgemm_rows_sample (gather-quantize)");
+  e = dq::launch_qgemm_stats(type, M, N, K, qa, static_cast<const uint8_t *>(packed), beta, part,
+                             npart, stream);
+  if (e != hipSuccess) return launched(e, "dq_qgemm_rows_sample (gemm)");
+  return launched(dq::launch_row_stats_finish(M, npart, part, token, stats, stream),
+                  "dq_qgemm_rows_sample (finish)");
 }
 
 int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const void *qa,

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "dq_internal.h"
+#include "row_stats.h"
 
 namespace dq {
 namespace {
@@ -396,7 +397,9 @@ __device__ inline void place(int id, int ncg, int nrg, int &cg, int &rg) {
 // for all NT tiles.  The WAVES f32 partial sums are added in LDS (pairwise
 // tree, fixed order) at the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its
 // own symbol so profiles tell the two workloads apart), 2 = debug stores of
-// S and Mn.
+// S and Mn, 3 = gathered-row GEMM whose output rows are folded into sampler
+// states (one per row per workgroup, at part[row * npart + column group])
+// instead of being stored.
 //
 // Load schedule of one wave (every load is a buffer-to-LDS load, and loads
 // complete in issue order, so a wait for one load also waits for every older
@@ -421,7 +424,10 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
                                                                    float *__restrict__ y, int64_t ldy,
                                                                    int y_vec,
                                                                    int32_t *__restrict__ dbg_S,
-                                                                   int32_t *__restrict__ dbg_Mn) {
+                                                                   int32_t *__restrict__ dbg_Mn,
+                                                                   float beta,
+                                                                   float4 *__restrict__ part,
+                                                                   int npart) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
   constexpr int MB = SH::MB, NT = SH::NT, R = SH::R, D = R - 1, WAVES = SH::WAVES;
@@ -564,6 +570,31 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
   __syncthreads();
   const int ri = lane >> 4, rq = (lane >> 2) & 3, c0 = 4 * (lane & 3);
   const int r = 4 * rq + ri;
+  if (MODE == 3) {
+    // wave w takes the m-blocks t = w, w + WAVES, ...: each lane folds its
+    // row's 4 columns of every n-tile, the 4 lanes of a row merge (lanes
+    // 4g .. 4g+3 share row r), and one of them stores the row's state
+    for (int t = wave; t < MB; t += WAVES) {
+      RowStat st = stat_empty();
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int p = t * NT + j;
+        const float *src = red + (p * 4 + ri) * 64 + 16 * rq + c0;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const f32x4 *>(src + w * (PER * 64));
+        const int64_t n0 = (nt0 + j) * TILE_N + c0;
+        const int64_t left = nt0 + j < ntiles ? N - n0 : 0;
+        const float z[4] = {beta * v[0], beta * v[1], beta * v[2], beta * v[3]};
+        stat_push4(st, z, (int)n0, left < 0 ? 0 : left > 4 ? 4 : (int)left);
+      }
+      st = stat_merge(st, stat_shfl_xor(st, 1));
+      st = stat_merge(st, stat_shfl_xor(st, 2));
+      const int row = (mb0 + t) * MBLK + r;
+      if ((lane & 3) == 0 && row < M) part[(int64_t)row * npart + cg] = stat_pack(st);
+    }
+    return;
+  }
   for (int p = wave; p < MB * NT; p += WAVES) {
     const int t = p / NT, j = p - t * NT;
     const int64_t n0 = (nt0 + j) * TILE_N + c0;
@@ -596,7 +627,10 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
 // tile has been read into registers, so S n-tiles are in flight while one is
 // being computed.  The waves'
 // partial sums of each tile meet in LDS (double buffered: one barrier per
-// tile) and waves 0 .. MB-1 add them in wave order and store.
+// tile) and waves 0 .. MB-1 add them in wave order and store.  With STATS the
+// storing lanes fold their outputs into a running sampler state instead (no
+// stores in the loop), and each row's state of the workgroup goes to
+// part[row * npart + blockIdx.x] at the end.
 constexpr int NW_WAVES = 8;  // most waves per narrow workgroup
 constexpr int NW_KB = 2;     // super-blocks per wave
 
@@ -620,16 +654,16 @@ constexpr int narrow_lds() {
   return 2 * NW_WAVES * MB * 4 * 64 * 4 + NW_WAVES * S * NW_KB * wslot_bytes<Q6>();
 }
 
-template <int TYPE, int MB, int S, bool VEC>
+template <int TYPE, int MB, int S, bool VEC, bool STATS>
 __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
     int M, int64_t N, int nb, const uint8_t *__restrict__ qa, const uint8_t *__restrict__ packed,
-    float *__restrict__ y, int64_t ldy) {
+    float *__restrict__ y, int64_t ldy, float beta, float4 *__restrict__ part, int npart) {
   constexpr bool Q6 = TYPE == 14;
   constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
   constexpr int WSLOT = wslot_bytes<Q6>();
   constexpr int SET = NW_KB * WSLOT;                      // one n-tile of one wave
   constexpr int DPS = NW_KB * dma_per_tile<Q6>();         // loads per set
-  constexpr int SC = VEC ? 1 : 4;                         // stores per tile (storing waves)
+  constexpr int SC = STATS ? 0 : VEC ? 1 : 4;            // stores per tile (storing waves)
   constexpr int PER = MB * 4 * 64;                        // partial sums per wave per tile
   static_assert(S >= 2 && (S - 1) * DPS + S * SC < 64, "pipeline shape");
   static_assert(narrow_lds<Q6, MB, S>() <= 160 * 1024, "LDS");
@@ -682,10 +716,11 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
   const bool storer = wave < MB;
   const int t_st = storer ? wave : 0;
   const int rows_st = M - MBLK * t_st < MBLK ? M - MBLK * t_st : MBLK;
-  const i32x4 dy = desc(y + (int64_t)t_st * MBLK * ldy,
-                        (uint32_t)(((int64_t)(rows_st - 1) * ldy + N) * 4));
+  const i32x4 dy = STATS ? i32x4{} : desc(y + (int64_t)t_st * MBLK * ldy,
+                                          (uint32_t)(((int64_t)(rows_st - 1) * ldy + N) * 4));
   const int ri = lane >> 4, rq = (lane >> 2) & 3, c0 = 4 * (lane & 3);
   const int r_st = 4 * rq + ri;  // this lane's row and first column in the tile
+  RowStat st = stat_empty();      // STATS: this lane's row over its columns so far
 
 #pragma unroll
   for (int p = 0; p < S; ++p) issue(p, p);
@@ -697,7 +732,7 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
     // younger than this tile's loads: the next S - 1 sets, and the stores of
     // the last S tiles (fewer in the first tiles: then the wait only waits
     // longer)
-    if (storer && k >= S)
+    if (SC > 0 && storer && k >= S)
       wait_vm<(S - 1) * DPS + S * SC>();
     else
       wait_vm<(S - 1) * DPS>();
@@ -741,7 +776,11 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
       const int64_t n0 = nt * TILE_N + c0;
       const uint32_t off = (uint32_t)(((int64_t)r_st * ldy + n0) * 4);
       const bool row_ok = r_st < rows_st;
-      if (VEC) {
+      if (STATS) {
+        const int64_t left = row_ok ? N - n0 : 0;
+        const float z[4] = {beta * v[0], beta * v[1], beta * v[2], beta * v[3]};
+        stat_push4(st, z, (int)n0, left < 0 ? 0 : left > 4 ? 4 : (int)left);
+      } else if (VEC) {
         bstore4(dy, row_ok && n0 < N ? off : NW_DROP, v);
       } else {
 #pragma unroll
@@ -750,26 +789,42 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
     }
   }
   wait_vm<0>();  // no LDS write may land after the workgroup ends
+  if (STATS && storer) {
+    st = stat_merge(st, stat_shfl_xor(st, 1));
+    st = stat_merge(st, stat_shfl_xor(st, 2));
+    if ((lane & 3) == 0 && r_st < rows_st)
+      part[(int64_t)(t_st * MBLK + r_st) * npart + blockIdx.x] = stat_pack(st);
+  }
 }
 
 // Narrow launches: one workgroup per CU (fewer if there are fewer tiles).
 constexpr int NW_CUS = 256;
 
+inline int64_t narrow_grid(int64_t N) {
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  return ntiles < NW_CUS ? ntiles : NW_CUS;
+}
+
+// part == nullptr: store y; otherwise fold the rows into part (npart =
+// narrow_grid(N) states per row).
 template <int TYPE, int MB>
 hipError_t launch_narrow(int64_t M, int64_t N, int nb, const uint8_t *qa, const uint8_t *packed,
-                         float *y, int64_t ldy, hipStream_t stream) {
-  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
-  dim3 grid((unsigned)(ntiles < NW_CUS ? ntiles : NW_CUS)), block(64 * (nb / NW_KB));
+                         float *y, int64_t ldy, float beta, float4 *part, hipStream_t stream) {
+  dim3 grid((unsigned)narrow_grid(N)), block(64 * (nb / NW_KB));
+  const int npart = (int)grid.x;
   const bool vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0) && (N % 4 == 0);
   // Q6_K tiles are larger: two slots per wave fit beside the sums, Q4_K three
   constexpr int S = TYPE == 14 ? 2 : 3;
   const int m = (int)M;
-  if (vec)
-    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, true>), grid, block, 0, stream, m, N, nb,
-                       qa, packed, y, ldy);
+  if (part)
+    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, true, true>), grid, block, 0, stream, m,
+                       N, nb, qa, packed, nullptr, (int64_t)0, beta, part, npart);
+  else if (vec)
+    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, true, false>), grid, block, 0, stream, m,
+                       N, nb, qa, packed, y, ldy, 0.0f, nullptr, 0);
   else
-    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, false>), grid, block, 0, stream, m, N,
-                       nb, qa, packed, y, ldy);
+    hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, false, false>), grid, block, 0, stream, m,
+                       N, nb, qa, packed, y, ldy, 0.0f, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -784,9 +839,16 @@ inline bool use_narrow(int mode, int64_t M, int64_t N, int nb, int64_t ldy) {
          nb <= NW_WAVES * NW_KB && ntiles >= 4 * NW_CUS && ldy <= (int64_t(1) << 25);
 }
 
+struct Extra {  // arguments of the debug and sampler-state modes
+  int32_t *dbg_S = nullptr, *dbg_Mn = nullptr;
+  float beta = 0.0f;
+  float4 *part = nullptr;
+  int npart = 0;
+};
+
 template <int TYPE, class SH>
 hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
-                   const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S, int32_t *dbg_Mn,
+                   const uint8_t *packed, float *y, int64_t ldy, const Extra &x,
                    hipStream_t stream) {
   const int64_t nmb = (M + MBLK - 1) / MBLK;
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
@@ -796,15 +858,16 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
   const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
   // rows of y can take 16-byte stores
   const int y_vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);
-  if (mode == 2)
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 2>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
-                       packed, y, ldy, y_vec, dbg_S, dbg_Mn);
-  else if (mode == 1)
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 1>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
-                       packed, y, ldy, y_vec, dbg_S, dbg_Mn);
-  else
-    hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, 0>), grid, block, 0, stream, m, N, nb, qa, qa_bytes,
-                       packed, y, ldy, y_vec, dbg_S, dbg_Mn);
+#define DQ_LAUNCH(MODE)                                                                        \
+  hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, MODE>), grid, block, 0, stream, m, N, nb, qa,        \
+                     qa_bytes, packed, y, ldy, y_vec, x.dbg_S, x.dbg_Mn, x.beta, x.part, x.npart)
+  switch (mode) {
+    case 1: DQ_LAUNCH(1); break;
+    case 2: DQ_LAUNCH(2); break;
+    case 3: DQ_LAUNCH(3); break;
+    default: DQ_LAUNCH(0); break;
+  }
+#undef DQ_LAUNCH
   return hipGetLastError();
 }
 
@@ -864,16 +927,16 @@ inline Pick pick_shape(int64_t M, int64_t N, int64_t nb) {
 
 template <int TYPE>
 hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
-                       const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
-                       int32_t *dbg_Mn, hipStream_t stream) {
+                       const uint8_t *packed, float *y, int64_t ldy, const Extra &x,
+                       hipStream_t stream) {
   const Pick pk = pick_shape(M, N, nb);
 #define DQ_MB(X)                                                                               \
   case X:                                                                                      \
     if (pk.waves == 8)                                                                         \
       return launch2<TYPE, typename ShapeOf<TYPE, X, 8>::type>(mode, M, N, nb, qa, packed, y,  \
-                                                               ldy, dbg_S, dbg_Mn, stream);    \
+                                                               ldy, x, stream);                \
     return launch2<TYPE, typename ShapeOf<TYPE, X, 4>::type>(mode, M, N, nb, qa, packed, y,    \
-                                                             ldy, dbg_S, dbg_Mn, stream)
+                                                             ldy, x, stream)
   switch (pk.mb) {
     DQ_MB(8);
     DQ_MB(5);
@@ -885,9 +948,9 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
 #undef DQ_MB
   if (pk.waves == 8)
     return launch2<TYPE, typename ShapeOf<TYPE, 1, 8>::type>(mode, M, N, nb, qa, packed, y, ldy,
-                                                             dbg_S, dbg_Mn, stream);
-  return launch2<TYPE, typename ShapeOf<TYPE, 1, 4>::type>(mode, M, N, nb, qa, packed, y, ldy,
-                                                           dbg_S, dbg_Mn, stream);
+                                                             x, stream);
+  return launch2<TYPE, typename ShapeOf<TYPE, 1, 4>::type>(mode, M, N, nb, qa, packed, y, ldy, x,
+                                                           stream);
 }
 
 }  // namespace
@@ -899,14 +962,46 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
   if (use_narrow(mode, M, N, nb, ldy)) {
     const bool two = M > MBLK;
     if (type == 12)
-      return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, y, ldy, stream)
-                 : launch_narrow<12, 1>(M, N, nb, qa, packed, y, ldy, stream);
-    return two ? launch_narrow<14, 2>(M, N, nb, qa, packed, y, ldy, stream)
-               : launch_narrow<14, 1>(M, N, nb, qa, packed, y, ldy, stream);
+      return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
+                 : launch_narrow<12, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
+    return two ? launch_narrow<14, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
+               : launch_narrow<14, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
   }
-  if (type == 12)
-    return launch_type<12>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
-  return launch_type<14>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+  Extra x;
+  x.dbg_S = dbg_S;
+  x.dbg_Mn = dbg_Mn;
+  if (type == 12) return launch_type<12>(mode, M, N, nb, qa, packed, y, ldy, x, stream);
+  return launch_type<14>(mode, M, N, nb, qa, packed, y, ldy, x, stream);
+}
+
+// The sampler-state GEMM takes the narrow kernel where the plain one would
+// (its row-stride condition does not apply: nothing is stored per column),
+// else the canvas kernel with one state per row per column group.
+int qgemm_stats_parts(int64_t M, int64_t N, int64_t K) {
+  const int nb = (int)(K / QK);
+  if (use_narrow(3, M, N, nb, 0)) return (int)narrow_grid(N);
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  return (int)((ntiles + NT_ALL - 1) / NT_ALL);
+}
+
+hipError_t launch_qgemm_stats(int type, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
+                              const uint8_t *packed, float beta, float4 *part, int npart,
+                              hipStream_t stream) {
+  const int nb = (int)(K / QK);
+  if (use_narrow(3, M, N, nb, 0)) {
+    const bool two = M > MBLK;
+    if (type == 12)
+      return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream)
+                 : launch_narrow<12, 1>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream);
+    return two ? launch_narrow<14, 2>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream)
+               : launch_narrow<14, 1>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream);
+  }
+  Extra x;
+  x.beta = beta;
+  x.part = part;
+  x.npart = npart;
+  if (type == 12) return launch_type<12>(3, M, N, nb, qa, packed, nullptr, 0, x, stream);
+  return launch_type<14>(3, M, N, nb, qa, packed, nullptr, 0, x, stream);
 }
 
 }  // namespace dq

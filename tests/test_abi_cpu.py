@@ -112,3 +112,42 @@ def test_rows_workspace(lib):
                            None, need, None)
     assert st == dq.DQ_EWORKSPACE
     assert lib.dq_qgemm_rows_workspace(4, 100, None) == dq.DQ_EINVAL
+
+
+def test_sampler_workspaces_and_host_checks(lib):
+    # standalone: one 16-byte state per 4096 columns per row
+    assert dq.logits_stats_workspace(32, 126464) == 32 * 31 * 16
+    assert dq.logits_stats_workspace(3, 1) == 3 * 16
+    # fused: the narrow kernel (M <= 32, K/256 even in [8, 16], >= 1024 n-tiles) keeps one
+    # state per row per workgroup (256), the canvas kernel one per 32-column group
+    rows = dq.qgemm_rows_workspace(32, 4096)
+    assert dq.qgemm_rows_sample_workspace(32, 126464, 4096) == rows + 32 * 256 * 16
+    assert dq.qgemm_rows_sample_workspace(64, 152064, 3584) == \
+        dq.qgemm_rows_workspace(64, 3584) + 64 * 4752 * 16
+    assert dq.qgemm_rows_sample_workspace(8, 4096, 4096) == \
+        dq.qgemm_rows_workspace(8, 4096) + 8 * 128 * 16
+    out = ctypes.c_size_t()
+    assert lib.dq_logits_stats_workspace(4, 0, ctypes.byref(out)) == dq.DQ_EINVAL
+    assert lib.dq_qgemm_rows_sample_workspace(4, 0, 256, ctypes.byref(out)) == dq.DQ_EINVAL
+    assert lib.dq_qgemm_rows_sample_workspace(4, 256, 100, ctypes.byref(out)) == dq.DQ_EINVAL
+    need = dq.logits_stats_workspace(4, 1000)
+    for beta in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.dq_logits_stats(4, 1000, 16, 1000, beta, 16, 16, 256, need, None) == dq.DQ_EINVAL
+        assert lib.dq_qgemm_rows_sample(dq.Q6_K, 160, 4, 4096, 4096, 256, 4096, 256, 256, beta,
+                                        16, 16, 256, 1 << 30, None) == dq.DQ_EINVAL
+    assert lib.dq_logits_stats(4, 1000, 16, 999, 1.0, 16, 16, 256, need, None) == dq.DQ_EINVAL
+    assert lib.dq_logits_stats(4, 1000, None, 1000, 1.0, 16, 16, 256, need, None) == dq.DQ_EINVAL
+    assert lib.dq_logits_stats(4, 1000, 16, 1000, 1.0, 16, 16, 256, need - 1, None) == \
+        dq.DQ_EWORKSPACE
+    assert lib.dq_logits_stats(4, 1000, 16, 1000, 1.0, 16, 16, 8, need, None) == dq.DQ_EINVAL
+    ws = dq.qgemm_rows_sample_workspace(32, 126464, 4096)
+    assert lib.dq_qgemm_rows_sample(dq.Q6_K, 160, 32, 126464, 4096, 256, 4096, 256, 256, 1.0,
+                                    16, 16, 256, ws - 1, None) == dq.DQ_EWORKSPACE
+    assert lib.dq_qgemm_rows_sample(dq.Q6_K, 160, 32, 126464, 4096, 256, 4096, 256, 256, 1.0,
+                                    16, None, 256, ws, None) == dq.DQ_EINVAL
+    assert lib.dq_qgemm_rows_sample(7, 160, 32, 126464, 4096, 256, 4096, 256, 256, 1.0,
+                                    16, 16, 256, ws, None) == dq.DQ_EUNSUPPORTED
+    # empty row lists are valid no-ops
+    assert lib.dq_logits_stats(0, 1000, None, 1000, 1.0, None, None, None, 0, None) == dq.DQ_OK
+    assert lib.dq_qgemm_rows_sample(dq.Q6_K, 160, 0, 4096, 4096, None, 4096, None, None, 1.0,
+                                    None, None, None, 0, None) == dq.DQ_OK
