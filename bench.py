@@ -243,6 +243,7 @@ def main():
     torch.cuda.synchronize()
     if args.counters:
         run_calls(sp)
+        sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws, reps=0)
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -271,6 +272,8 @@ def main():
                    "GB_s": round(v[3] / (v[1] * 1e-3) / 1e9, 1)}
                for k, v in per_kind.items()}
     log("per-kind (isolated launches):", json.dumps(kernels))
+    sampler = sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws)
+    log("output projection feeding the samplers:", json.dumps(sampler))
 
     # ------------------------------------------ the step as one HIP graph
     # The step's launches are captured once and replayed: the host then
@@ -353,6 +356,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(dom_bytes),
                      "ops_per_launch": int(dom_ops), "launches": dom_launches},
         "kernels_isolated": kernels,
+        "sampler_output_projection": sampler,
         "step_timing": f"HIP graph replay of the step's {len(calls)} launches",
         "device": torch.cuda.get_device_properties(dev).name,
     }
@@ -362,6 +366,69 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts,
                                                 gammas)
     print(json.dumps(result), flush=True)
+
+
+def sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws, reps=20):
+    # reps = 0: one call of each, untimed (the counter runs)
+    """The step's output projection as the samplers consume it (not part of the
+    timed step, whose projection stores the logits): per requested row the greedy
+    token, maximum, log-partition, entropy and top probability of the logits,
+    (a) formed in the GEMM's epilogue (dq_qgemm_rows_sample: no logits stored)
+    and (b) by storing the logits and reducing them (dq_qgemm_rows, then
+    dq_logits_stats).  HIP events around `reps` back-to-back calls of each on
+    the step's stream; both read the 425 MB weight matrix from HBM every call
+    (it is larger than the last-level cache)."""
+    dev = canvas.device
+    beta = ctypes.c_float(1.0 / 64)
+    token = torch.empty(ROWS, dtype=torch.int32, device=dev)
+    stats = torch.empty((ROWS, 4), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(dq.qgemm_rows_sample_workspace(ROWS, V, K), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(dq.logits_stats_workspace(ROWS, V), dtype=torch.uint8, device=dev)
+
+    def fused():
+        return lib.dq_qgemm_rows_sample(Q6_K, L, ROWS, V, K, canvas.data_ptr(), K, idx.data_ptr(),
+                                        out_packed.data_ptr(), beta, token.data_ptr(),
+                                        stats.data_ptr(), ws_f.data_ptr(), ws_f.numel(), sp)
+
+    def unfused():
+        return (lib.dq_qgemm_rows(Q6_K, L, ROWS, V, K, canvas.data_ptr(), K, idx.data_ptr(),
+                                  out_packed.data_ptr(), logits.data_ptr(), V, ws.data_ptr(),
+                                  ws.numel(), sp)
+                or lib.dq_logits_stats(ROWS, V, logits.data_ptr(), V, beta, token.data_ptr(),
+                                       stats.data_ptr(), ws_s.data_ptr(), ws_s.numel(), sp))
+
+    weights = V * (K // 256) * BLOCK[Q6_K]
+    rows_in = ROWS * K * 4 + ROWS * 4           # gathered f32 rows and their indices
+    stats_out = ROWS * (4 + 16)                 # token and 4 statistics per row
+    out = {"rows": ROWS, "vocab": V, "K": K, "beta": 1.0 / 64}
+    for name, fn, nbytes in (("fused", fused, weights + rows_in + stats_out),
+                             ("unfused", unfused, weights + rows_in + stats_out
+                              + 2 * ROWS * V * 4)):  # logits written, then read back
+        for _ in range(3 if reps else 1):
+            if fn():
+                raise RuntimeError(lib.dq_last_error().decode())
+        torch.cuda.synchronize()
+        if not reps:
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        out[f"{name}_us"] = round(us, 2)
+        out[f"{name}_algorithmic_MB"] = round(nbytes / 1e6, 2)
+        out[f"{name}_GB_s"] = round(nbytes / us / 1e3, 1)
+    if not reps:
+        return out
+    # the fused result is the unfused one's, bit for bit in token and maximum
+    tok_u, st_u = token.clone(), stats.clone()
+    fused()
+    torch.cuda.synchronize()
+    if not (torch.equal(token, tok_u) and torch.equal(stats[:, 0], st_u[:, 0])):
+        raise RuntimeError("fused and unfused sampler statistics differ")
+    return out
 
 
 def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):

@@ -30,8 +30,11 @@ __device__ inline RowStat block_merge(RowStat st, float4 *lds) {
 }
 
 // Workgroup r * npart + c computes partial c of row r, over the columns
-// c * RS_CHUNK .. min(N, (c + 1) * RS_CHUNK) - 1; thread t takes the groups of
-// 4 columns that start 4 * (t + 256 i) columns into the chunk.
+// c * RS_CHUNK .. min(N, (c + 1) * RS_CHUNK) - 1; thread t takes the RS_G groups
+// of 4 columns that start 4 * (t + 256 g) columns into the chunk, all loaded
+// before any is folded (RS_G loads in flight per thread).
+constexpr int RS_G = RS_CHUNK / (4 * RS_THREADS);
+
 template <bool VEC>
 __global__ __launch_bounds__(RS_THREADS) void logits_stats_partial_kernel(
     int64_t N, const float *__restrict__ y, int64_t ldy, float beta, int npart,
@@ -42,22 +45,28 @@ __global__ __launch_bounds__(RS_THREADS) void logits_stats_partial_kernel(
   const float *yr = y + r * ldy;
   const int64_t lo = (int64_t)c * RS_CHUNK;
   const int64_t hi = lo + RS_CHUNK < N ? lo + RS_CHUNK : N;
-  RowStat st = stat_empty();
-  for (int64_t n0 = lo + 4 * threadIdx.x; n0 < hi; n0 += 4 * RS_THREADS) {
+  float v[RS_G][4];
+  int cnt[RS_G];
+#pragma unroll
+  for (int g = 0; g < RS_G; ++g) {
+    const int64_t n0 = lo + 4 * (threadIdx.x + RS_THREADS * g);
     const int64_t left = hi - n0;
-    const int cnt = left > 4 ? 4 : (int)left;
-    float v[4];
-    if (VEC && cnt == 4) {
+    cnt[g] = left <= 0 ? 0 : left > 4 ? 4 : (int)left;
+    if (VEC && cnt[g] == 4) {
       const float4 q = *reinterpret_cast<const float4 *>(yr + n0);
-      v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+      v[g][0] = q.x, v[g][1] = q.y, v[g][2] = q.z, v[g][3] = q.w;
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = i < cnt ? yr[n0 + i] : 0.0f;
+      for (int i = 0; i < 4; ++i) v[g][i] = i < cnt[g] ? yr[n0 + i] : 0.0f;
     }
+  }
+  RowStat st = stat_empty();
+#pragma unroll
+  for (int g = 0; g < RS_G; ++g) {
     float z[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = beta * v[i];
-    stat_push4(st, z, (int)n0, cnt);
+    for (int i = 0; i < 4; ++i) z[i] = beta * v[g][i];
+    stat_push4(st, z, (int)(lo + 4 * (threadIdx.x + RS_THREADS * g)), cnt[g]);
   }
   st = block_merge(st, lds);
   if (threadIdx.x == 0) part[r * npart + c] = stat_pack(st);
