@@ -78,10 +78,17 @@ def _load():
             lib.dqo_qgemm_f32.argtypes = [ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, i64,
                                           i64, vp, i64]
             lib.dqo_logits_stats.argtypes = [i64, i64, vp, i64, ctypes.c_float, vp, vp]
+            lib.dqo_f32_to_fp16.restype = ctypes.c_uint16
+            lib.dqo_f32_to_fp16.argtypes = [ctypes.c_float]
+            lib.dqo_f32_to_fp16_n.argtypes = [vp, vp, i64]
+            lib.dqo_rope_pair.argtypes = [ctypes.c_float] * 4 + [vp, vp]
+            lib.dqo_rope_rows.argtypes = [i64, i64, i64, vp, i64, vp, ctypes.c_int]
+            lib.dqo_attention.argtypes = [i64, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp, i64,
+                                          vp]
             for name in ("dqo_dequant_row", "dqo_quantize_act", "dqo_swiglu_quantize_act",
                          "dqo_rmsnorm_quantize_act", "dqo_subdots",
                          "dqo_superblock_sums", "dqo_qgemm_ref", "dqo_qgemm_ref_points",
-                         "dqo_qgemm_f32", "dqo_logits_stats"):
+                         "dqo_qgemm_f32", "dqo_logits_stats", "dqo_attention", "dqo_rope_rows"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -338,3 +345,53 @@ def qgemm_rows_sample_ref(type_: int, canvas: np.ndarray, idx: np.ndarray, W, N:
     y, T = qgemm_ref(type_, q, d, W, N, threads)
     token, stats = logits_stats(y, beta)
     return token, stats, y, T
+
+
+# --- attention over the canvas ------------------------------------------------
+
+ROPE_NONE, ROPE_NORM, ROPE_NEOX = 0, 1, 2
+
+
+def f32_to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """IEEE binary32 -> binary16 (round to nearest even), as uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    h = np.zeros(x.shape, np.uint16)
+    _load().dqo_f32_to_fp16_n(_p(x), _p(h), x.size)
+    return h
+
+
+def rope_pair(a: float, b: float, c: float, s: float):
+    """One RoPE rotation of the pair (a, b) by (cos, sin) = (c, s), in binary32."""
+    ra, rb = ctypes.c_float(), ctypes.c_float()
+    _load().dqo_rope_pair(a, b, c, s, ctypes.byref(ra), ctypes.byref(rb))
+    return ra.value, rb.value
+
+
+def rope_rows(x: np.ndarray, n_heads: int, D: int, rope: np.ndarray, mode: int) -> np.ndarray:
+    """RoPE of the n_heads head vectors of each row (row l at position l): a copy."""
+    x = np.array(x, dtype=np.float32, order="C", copy=True)
+    rope = np.ascontiguousarray(rope, dtype=np.float32)
+    _check(_load().dqo_rope_rows(x.shape[0], n_heads, D, _p(x), x.shape[1], _p(rope), mode))
+    return x
+
+
+def attention(qkv: np.ndarray, H: int, Hkv: int, D: int, rope=None, mode: int = ROPE_NONE):
+    """Bidirectional attention of every canvas position over all L positions.
+
+    Architecture page, "A forward pass", step 2 (RoPE on Q and K, attention over
+    all L positions, no mask) and "Source map" (NORM and NEOX RoPE); aiboss88 news
+    page, capability list (attention on f16 tensor cores).  qkv: L x ((H + 2 Hkv) D)
+    f32 rows [Q | K | V]; rope: L x D/2 x 2 (cos, sin) f32 or None.  Q and K are
+    rotated in binary32, Q, K and V rounded to binary16, the rest is binary64.
+    Returns (out [L, H D], tol [L, H D]) with tol = sum_j p_j |v_j| / sum_j p_j.
+    """
+    qkv = np.ascontiguousarray(qkv, dtype=np.float32)
+    L = qkv.shape[0]
+    if rope is not None:
+        rope = np.ascontiguousarray(rope, dtype=np.float32)
+    out = np.zeros((L, H * D), np.float64)
+    tol = np.zeros((L, H * D), np.float64)
+    _check(_load().dqo_attention(L, H, Hkv, D, _p(qkv), qkv.shape[1],
+                                 _p(rope) if rope is not None else None, mode, _p(out), H * D,
+                                 _p(tol)))
+    return out, tol

@@ -543,3 +543,156 @@ int dqo_logits_stats(int64_t M, int64_t N, const double *y, int64_t ldy, float b
   free(z);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention over the canvas (Architecture page, "A forward pass", step 2:  */
+/* RoPE rotates Q and K, then attention runs over all L positions with no    */
+/* mask; "Source map": NORM and NEOX RoPE, bidirectional attention; aiboss88 */
+/* news page, capability list: attention runs on f16 tensor cores).          */
+/* ------------------------------------------------------------------------ */
+
+/* binary32 -> binary16, round to nearest even (the IEEE conversion), as the */
+/* 16-bit pattern.  Overflow gives Inf; NaN stays NaN.                       */
+uint16_t dqo_f32_to_fp16(float f) {
+  uint32_t x;
+  memcpy(&x, &f, sizeof x);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x200u : 0u));
+  const int e = (int)(ax >> 23) - 127; /* unbiased exponent */
+  if (e > 15) return (uint16_t)(sign | 0x7c00u);
+  uint32_t mant = (ax & 0x7fffffu) | 0x800000u; /* 24-bit significand (normal inputs) */
+  int shift;                                    /* bits dropped from the significand */
+  uint32_t hexp;
+  if (e >= -14) { /* normal half: keep 11 bits */
+    shift = 13;
+    hexp = (uint32_t)(e + 15);
+  } else { /* subnormal half: value = m * 2^-24 */
+    if (ax < 0x33000000u) return (uint16_t)sign; /* below half the smallest subnormal */
+    if ((ax >> 23) == 0) return (uint16_t)sign;  /* f32 subnormal: far below */
+    shift = 13 + (-14 - e);
+    hexp = 0;
+  }
+  uint32_t kept = mant >> shift;
+  const uint32_t rem = mant & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (kept & 1u))) kept += 1u;
+  /* kept holds the significand with its leading one (normal) or the       */
+  /* subnormal count; a carry out of the significand bumps the exponent    */
+  uint32_t h;
+  if (hexp == 0)
+    h = kept; /* kept == 0x400 becomes the smallest normal, as it should */
+  else
+    h = ((hexp << 10) + (kept - 0x400u)); /* kept in [0x400, 0x800] */
+  if (h >= 0x7c00u) h = 0x7c00u;
+  return (uint16_t)(sign | h);
+}
+
+static double f16r(float f) { return (double)dqo_fp16_to_f32(dqo_f32_to_fp16(f)); }
+
+/* Rotation of one pair (a, b) by the table's (c, s) = (cos, sin) of the     */
+/* position's angle, in binary32 with a fixed operation order:               */
+/*   a' = fma(a, c, -(b*s)),  b' = fma(b, c, a*s).                           */
+void dqo_rope_pair(float a, float b, float c, float s, float *ra, float *rb) {
+  const float bs = b * s;
+  const float as = a * s;
+  *ra = fmaf(a, c, -bs);
+  *rb = fmaf(b, c, as);
+}
+
+/* Rotate one head vector x[0..D) at position pos.  mode 1 (NORM) pairs    */
+/* (2i, 2i+1), mode 2 (NEOX) pairs (i, i + D/2), i < D/2; mode 0 leaves x.   */
+/* rope holds, per position, D/2 pairs (cos, sin) of the angles pos*f_i.     */
+static void rope_vec(float *x, int64_t D, int mode, const float *rope, int64_t pos) {
+  if (mode == 0) return;
+  const int64_t P = D / 2;
+  for (int64_t i = 0; i < P; ++i) {
+    const float c = rope[(pos * P + i) * 2], s = rope[(pos * P + i) * 2 + 1];
+    const int64_t ia = mode == 1 ? 2 * i : i, ib = mode == 1 ? 2 * i + 1 : i + P;
+    float ra, rb;
+    dqo_rope_pair(x[ia], x[ib], c, s, &ra, &rb);
+    x[ia] = ra;
+    x[ib] = rb;
+  }
+}
+
+/* out[l][h*D + d] = sum_j p_j v_j[d] / sum_j p_j with p_j = exp(q.k_j / sqrt(D) */
+/* - max), over all L keys j of the kv head h / (H / Hkv) (no mask).  q, k:    */
+/* rotated (binary32, rope_vec), then rounded to binary16; v rounded to        */
+/* binary16; everything after in binary64.  Row l of qkv holds               */
+/* [Q (H*D) | K (Hkv*D) | V (Hkv*D)].  tol (optional, same shape as out)     */
+/* receives sum_j p_j |v_j[d]| / sum_j p_j, the scale of the tolerance.      */
+int dqo_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv, int64_t ldqkv,
+                  const float *rope, int mode, double *out, int64_t ldo, double *tol) {
+  if (L <= 0 || H <= 0 || Hkv <= 0 || H % Hkv || D <= 0 || D % 2 || mode < 0 || mode > 2 ||
+      ldqkv < (H + 2 * Hkv) * D || ldo < H * D || (mode && !rope))
+    return -1;
+  double *kh = (double *)malloc(sizeof(double) * (size_t)(L * Hkv * D));
+  double *vh = (double *)malloc(sizeof(double) * (size_t)(L * Hkv * D));
+  double *qh = (double *)malloc(sizeof(double) * (size_t)D);
+  double *sc = (double *)malloc(sizeof(double) * (size_t)L);
+  float *tmp = (float *)malloc(sizeof(float) * (size_t)D);
+  if (!kh || !vh || !qh || !sc || !tmp) {
+    free(kh), free(vh), free(qh), free(sc), free(tmp);
+    return -2;
+  }
+  for (int64_t l = 0; l < L; ++l)
+    for (int64_t g = 0; g < Hkv; ++g) {
+      const float *kr = qkv + l * ldqkv + (H + g) * D;
+      const float *vr = qkv + l * ldqkv + (H + Hkv + g) * D;
+      for (int64_t d = 0; d < D; ++d) tmp[d] = kr[d];
+      rope_vec(tmp, D, mode, rope, l);
+      for (int64_t d = 0; d < D; ++d) {
+        kh[(l * Hkv + g) * D + d] = f16r(tmp[d]);
+        vh[(l * Hkv + g) * D + d] = f16r(vr[d]);
+      }
+    }
+  const double inv = 1.0 / sqrt((double)D);
+  for (int64_t l = 0; l < L; ++l)
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / (H / Hkv);
+      const float *qr = qkv + l * ldqkv + h * D;
+      for (int64_t d = 0; d < D; ++d) tmp[d] = qr[d];
+      rope_vec(tmp, D, mode, rope, l);
+      for (int64_t d = 0; d < D; ++d) qh[d] = f16r(tmp[d]);
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < L; ++j) {
+        double s = 0.0;
+        for (int64_t d = 0; d < D; ++d) s += qh[d] * kh[(j * Hkv + g) * D + d];
+        sc[j] = s * inv;
+        if (sc[j] > mx) mx = sc[j];
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j < L; ++j) {
+        sc[j] = exp(sc[j] - mx);
+        den += sc[j];
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double num = 0.0, ab = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+          const double v = vh[(j * Hkv + g) * D + d];
+          num += sc[j] * v;
+          ab += sc[j] * fabs(v);
+        }
+        out[l * ldo + h * D + d] = num / den;
+        if (tol) tol[l * ldo + h * D + d] = ab / den;
+      }
+    }
+  free(kh), free(vh), free(qh), free(sc), free(tmp);
+  return 0;
+}
+
+/* Elementwise dqo_f32_to_fp16 over n values (for the exhaustive pin). */
+void dqo_f32_to_fp16_n(const float *x, uint16_t *h, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) h[i] = dqo_f32_to_fp16(x[i]);
+}
+
+/* Rotate in place the n_heads head vectors (D values each, consecutive)    */
+/* of each of L rows of x (row stride ldx), row l at position l.             */
+int dqo_rope_rows(int64_t L, int64_t n_heads, int64_t D, float *x, int64_t ldx, const float *rope,
+                  int mode) {
+  if (D <= 0 || D % 2 || mode < 0 || mode > 2 || ldx < n_heads * D || (mode && !rope)) return -1;
+  for (int64_t l = 0; l < L; ++l)
+    for (int64_t h = 0; h < n_heads; ++h) rope_vec(x + l * ldx + h * D, D, mode, rope, l);
+  return 0;
+}

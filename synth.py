@@ -83,8 +83,10 @@ def row_index(rng: np.random.Generator, L: int, M: int) -> np.ndarray:
 # --------------------------------------------------------------------------- #
 # Workloads (shapes of the five configurations; seeds 1000*config+10*layer+p)  #
 # --------------------------------------------------------------------------- #
-LLADA = dict(L=160, K=4096, ffn=12288, vocab=126464, layers=32)
-DREAM = dict(L=512, K=3584, ffn=18944, kv=512, vocab=152064)
+LLADA = dict(L=160, K=4096, ffn=12288, vocab=126464, layers=32, heads=32, kv_heads=32,
+             head_dim=128, rope_theta=500000.0, rope="norm")
+DREAM = dict(L=512, K=3584, ffn=18944, kv=512, vocab=152064, heads=28, kv_heads=4,
+             head_dim=128, rope_theta=1000000.0, rope="neox")
 
 
 def llada_layer(layer: int):
@@ -106,3 +108,20 @@ def dream_layer():
 
 def seed(config: int, layer: int, proj: int) -> int:
     return 1000 * config + 10 * layer + proj
+
+
+def rope_table(L: int, D: int, theta: float) -> np.ndarray:
+    """L x D/2 x 2 float32 (cos, sin) of the angles pos * theta**(-2i/D), i < D/2.
+
+    A model constant (precomputed once for the longest canvas); attention takes
+    it as an input, like the RMSNorm weights.
+    """
+    inv = theta ** (-np.arange(0, D, 2, dtype=np.float64) / D)
+    ang = np.arange(L, dtype=np.float64)[:, None] * inv[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+def qkv_rows(rng: np.random.Generator, L: int, H: int, Hkv: int, D: int,
+             scale: float = 1.0) -> np.ndarray:
+    """L x (H + 2 Hkv) D float32 rows [Q | K | V] ~ N(0, scale^2)."""
+    return (rng.standard_normal((L, (H + 2 * Hkv) * D)) * scale).astype(np.float32)

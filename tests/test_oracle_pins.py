@@ -21,6 +21,11 @@
   ties, the binary32 product deciding the token, exact power-of-two
   temperature and integer shift invariance, and no overflow at large
   magnitudes.
+* Attention: binary32 -> binary16 rounding against numpy's float16 at every
+  rounding boundary of every exponent (and random patterns); RoPE against complex multiplication in float64 for both pairings
+  (and exact special angles); attention closed forms (one position, equal
+  keys, constant values, two keys), permutation equivariance, shared kv heads,
+  and rotation invariance of the scores (RoPE depends on relative position).
 """
 import os
 
@@ -480,3 +485,157 @@ def test_logits_stats_large_magnitudes_do_not_overflow():
     p = 1.0 / (1.0 + np.exp(-10.0))
     np.testing.assert_allclose(st[0, 2], -p * np.log(p) - (1 - p) * np.log(1 - p), rtol=1e-9)
     np.testing.assert_allclose(st[0, 3], p, rtol=1e-11)  # exp of a difference of ~1e4-sized values
+
+
+# --- attention ----------------------------------------------------------------
+
+import synth  # noqa: E402
+
+
+def _fp16_cases():
+    """Every rounding boundary of binary32 -> binary16: for each sign and binary32
+    exponent, every pattern of the significand bits that survive, with the dropped
+    bits at 0, 1, just below, at and just above the half-way point, and all ones;
+    plus 4M random bit patterns."""
+    out = [np.random.default_rng(61).integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)]
+    for e in range(256):
+        ue = e - 127
+        shift = 13 if ue >= -14 else min(24, -1 - ue)
+        shift = min(shift, 23)
+        half = 1 << (shift - 1)
+        lows = np.array(sorted({0, 1, half - 1, half, half + 1, (1 << shift) - 1}), np.uint32)
+        highs = np.arange(1 << (23 - shift), dtype=np.uint32) << np.uint32(shift)
+        mant = (highs[:, None] | lows[None, :]).ravel()
+        for sign in (0, 1):
+            out.append((np.uint32(sign << 31) | np.uint32(e << 23) | mant).astype(np.uint32))
+    return np.concatenate(out)
+
+
+def test_f32_to_fp16_rounding_boundaries_against_numpy():
+    bits = _fp16_cases()
+    x = bits.view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = oracle.f32_to_fp16_bits(x)
+    nan = np.isnan(x)
+    bad = np.nonzero(got[~nan] != ref[~nan])[0]
+    assert bad.size == 0, [hex(int(v)) for v in bits[~nan][bad[:5]]]
+    assert np.all((got[nan] & 0x7c00) == 0x7c00) and np.all(got[nan] & 0x3ff)
+
+
+def test_rope_pair_special_angles_and_complex_rotation():
+    assert oracle.rope_pair(1.5, -2.25, 1.0, 0.0) == (1.5, -2.25)        # angle 0
+    assert oracle.rope_pair(1.5, -2.25, 0.0, 1.0) == (2.25, 1.5)         # a quarter turn
+    assert oracle.rope_pair(1.5, -2.25, -1.0, 0.0) == (-1.5, 2.25)       # a half turn
+    rng = np.random.default_rng(21)
+    for mode, pair in ((oracle.ROPE_NORM, lambda i: (2 * i, 2 * i + 1)),
+                       (oracle.ROPE_NEOX, lambda i: (i, i + 64))):
+        L, D, nh = 37, 128, 3
+        tab = synth.rope_table(L, D, 10000.0)
+        x = rng.standard_normal((L, nh * D)).astype(np.float32)
+        y = oracle.rope_rows(x, nh, D, tab, mode)
+        for h in range(nh):
+            for i in range(D // 2):
+                a, b = pair(i)
+                z = (x[:, h * D + a].astype(np.float64) + 1j * x[:, h * D + b]) * \
+                    (tab[:, i, 0].astype(np.float64) + 1j * tab[:, i, 1])
+                mag = np.abs(z) + 1e-30
+                assert np.all(np.abs(y[:, h * D + a] - z.real) <= 4e-7 * mag)
+                assert np.all(np.abs(y[:, h * D + b] - z.imag) <= 4e-7 * mag)
+
+
+def _f16(x):
+    return np.asarray(x, np.float32).astype(np.float16).astype(np.float64)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(31)
+    H, Hkv, D = 4, 2, 128
+    # one position: the output is its own value vector
+    qkv = synth.qkv_rows(rng, 1, H, Hkv, D)
+    out, _ = oracle.attention(qkv, H, Hkv, D)
+    v = _f16(qkv[0, (H + Hkv) * D:])
+    for h in range(H):
+        assert np.array_equal(out[0, h * D:(h + 1) * D], v[(h // 2) * D:(h // 2 + 1) * D])
+    # equal keys: uniform weights, the mean of the values
+    L = 9
+    qkv = synth.qkv_rows(rng, L, H, Hkv, D)
+    qkv[:, H * D:(H + Hkv) * D] = qkv[0, H * D:(H + Hkv) * D]
+    out, tol = oracle.attention(qkv, H, Hkv, D)
+    vmean = _f16(qkv[:, (H + Hkv) * D:]).mean(axis=0)
+    for h in range(H):
+        g = h // 2
+        np.testing.assert_allclose(out[:, h * D:(h + 1) * D],
+                                   np.broadcast_to(vmean[g * D:(g + 1) * D], (L, D)),
+                                   rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(tol[:, :D], np.broadcast_to(np.abs(_f16(qkv[:, (H + Hkv) * D:
+                                                                       (H + Hkv) * D + D])).mean(0), (L, D)),
+                               rtol=1e-12)
+    # constant values: the output is that constant, whatever the weights
+    qkv = synth.qkv_rows(rng, L, H, Hkv, D, scale=2.0)
+    qkv[:, (H + Hkv) * D:] = qkv[3, (H + Hkv) * D:]
+    out, _ = oracle.attention(qkv, H, Hkv, D)
+    v = _f16(qkv[3, (H + Hkv) * D:])
+    for h in range(H):
+        np.testing.assert_allclose(out[:, h * D:(h + 1) * D],
+                                   np.broadcast_to(v[(h // 2) * D:(h // 2 + 1) * D], (L, D)),
+                                   rtol=1e-13)
+
+
+def test_attention_two_keys():
+    # one head, D = 2: q = (1, 0); keys (a, 0) and (b, 0); values (1, 0) and (0, 1):
+    # the output is (p, 1 - p) with p = 1 / (1 + exp((b - a) / sqrt(2)))
+    H, Hkv, D = 1, 1, 2
+    a, b = 3.0, 1.0
+    qkv = np.array([[1, 0, a, 0, 1, 0],
+                    [0.5, 0.25, b, 0, 0, 1]], np.float32)
+    out, _ = oracle.attention(qkv, H, Hkv, D)
+    p = 1.0 / (1.0 + np.exp((b - a) / np.sqrt(2.0)))
+    np.testing.assert_allclose(out[0], [p, 1 - p], rtol=1e-14)
+    # position 1's query (0.5, 0.25): scores 0.5 a and 0.5 b
+    p1 = 1.0 / (1.0 + np.exp(0.5 * (b - a) / np.sqrt(2.0)))
+    np.testing.assert_allclose(out[1], [p1, 1 - p1], rtol=1e-14)
+
+
+def test_attention_permutation_and_shared_kv_heads():
+    rng = np.random.default_rng(41)
+    L, H, Hkv, D = 23, 6, 2, 128
+    qkv = synth.qkv_rows(rng, L, H, Hkv, D, scale=1.5)
+    out, _ = oracle.attention(qkv, H, Hkv, D)
+    perm = rng.permutation(L)
+    outp, _ = oracle.attention(qkv[perm], H, Hkv, D)
+    np.testing.assert_allclose(outp, out[perm], rtol=1e-12, atol=1e-14)
+    # heads 0 and 2 share kv head 0 (groups of 3): equal queries give equal outputs
+    qkv2 = qkv.copy()
+    qkv2[:, 2 * D:3 * D] = qkv2[:, 0:D]
+    out2, _ = oracle.attention(qkv2, H, Hkv, D)
+    assert np.array_equal(out2[:, 0:D], out2[:, 2 * D:3 * D])
+    assert not np.array_equal(out2[:, 0:D], out2[:, 3 * D:4 * D])  # head 3 reads kv head 1
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_attention_rope_scores_depend_on_relative_position(mode):
+    # every position's q and k equal: with RoPE, position i's scores over the keys j
+    # depend on i - j only, so position i attends to a shifted copy of the pattern of
+    # position 0 (checked on the weights, through one-hot values)
+    rng = np.random.default_rng(51)
+    L, D = 8, 128
+    qk = rng.standard_normal(D).astype(np.float32)
+    tab = synth.rope_table(L, D, 10000.0)
+    qkv = np.zeros((L, 3 * D + 0), np.float32)
+    # values: position j carries the unit vector e_j in its first L dims
+    qkv[:, 0:D] = qk
+    qkv[:, D:2 * D] = qk
+    qkv[np.arange(L), 2 * D + np.arange(L)] = 1.0
+    out, _ = oracle.attention(qkv, 1, 1, D, tab, mode)
+    w = out[:, :L]  # w[i, j] = attention weight of position i on key j
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-12)
+    # scores s(i, j) = f(i - j): w[i, j] / w[i, j'] = w[0, j - i] / w[0, j' - i] where in range
+    for i in range(1, L):
+        for j in range(i, L):
+            r1 = np.log(w[i, j]) - np.log(w[i, i])
+            r0 = np.log(w[0, j - i]) - np.log(w[0, 0])
+            assert abs(r1 - r0) < 0.05, (i, j, r1, r0)  # binary16 rounding of rotated vectors
+    # without RoPE every score is the same: uniform weights
+    out0, _ = oracle.attention(qkv, 1, 1, D)
+    np.testing.assert_allclose(out0[:, :L], 1.0 / L, rtol=1e-12)
