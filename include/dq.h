@@ -286,6 +286,41 @@ int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * dq_attention -- bidirectional attention of every canvas position over all
+ * L positions.
+ *
+ * Source: Architecture page, "A forward pass", step 2 (RoPE rotates Q and K;
+ * attention runs over all L positions with no mask) and "Source map" (NORM
+ * and NEOX RoPE, bidirectional attention); aiboss88 news page, capability
+ * list (attention on f16 tensor cores, 16 queries per warp, keys streamed
+ * through shared memory with an online softmax).  For position l and head h
+ * (kv head g = h / (H / Hkv)):
+ *   q = RoPE(Q[l, h]), k_j = RoPE(K[j, g]) at positions l and j, rounded to
+ *   binary16; v_j = V[j, g] rounded to binary16;
+ *   out[l][h*D + d] = sum_j p_j v_j[d] / sum_j p_j,
+ *   p_j = exp(q . k_j / sqrt(D) - max_j q . k_j / sqrt(D)),  j = 0 .. L-1.
+ * RoPE of the pair (a, b) by (c, s) = rope[pos][i] is a' = fma(a, c, -(b*s)),
+ * b' = fma(b, c, a*s) in binary32; pairs are (2i, 2i+1) for rope_mode 1
+ * (NORM) and (i, i + D/2) for rope_mode 2 (NEOX); rope_mode 0 rotates nothing.
+ * Products accumulate in binary32 and the probabilities enter the second
+ * product as binary16, so |out - exact| stays below about 1e-3 of
+ * sum_j p_j |v_j[d]| / sum_j p_j.
+ *
+ *   D     : head dimension; only 128 is built (else DQ_EUNSUPPORTED).
+ *   qkv   : device f32, L rows [Q (H*D) | K (Hkv*D) | V (Hkv*D)], row stride
+ *           ldqkv >= (H + 2 Hkv) D floats, a multiple of 4; 16-byte aligned
+ *           (the Q/K/V projection's output as dq_qgemm writes it).
+ *   rope  : device f32 [L][D/2][2] (cos, sin) of each position's angles,
+ *           8-byte aligned; ignored (may be NULL) for rope_mode 0.
+ *   out   : device f32, L rows of H*D, row stride ldo >= H D; only those
+ *           columns are written.
+ * Errors: DQ_EUNSUPPORTED (D), DQ_EINVAL (shapes, H % Hkv, rope_mode, strides,
+ *         NULL, alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv, int64_t ldqkv,
+                 const float *rope, int rope_mode, float *out, int64_t ldo, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * dq_debug_superblock_sums -- test hook.  Runs the dq_qgemm kernel with its
  * fold replaced by stores of the exact per-super-block integers, so that the
  * integer part of the production code path can be compared bit for bit:

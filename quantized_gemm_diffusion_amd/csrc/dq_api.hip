@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "dq.h"
+#include "attention.h"
 #include "dq_internal.h"
 #include "row_stats.h"
 
@@ -327,6 +328,29 @@ int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
   if (e != hipSuccess) return launched(e, "dq_qgemm_rows_sample (gemm)");
   return launched(dq::launch_row_stats_finish(M, npart, part, token, stats, stream),
                   "dq_qgemm_rows_sample (finish)");
+}
+
+int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv, int64_t ldqkv,
+                 const float *rope, int rope_mode, float *out, int64_t ldo, hipStream_t stream) {
+  if (D != dq::ATTN_HEAD_DIM)
+    return fail(DQ_EUNSUPPORTED, "head dimension %lld (only 128 is built)", (long long)D);
+  if (L < 0 || L > ((int64_t)1 << 24)) return fail(DQ_EINVAL, "L = %lld out of range", (long long)L);
+  if (H <= 0 || Hkv <= 0 || H % Hkv || H > 4096)
+    return fail(DQ_EINVAL, "H = %lld, Hkv = %lld: need 0 < Hkv, Hkv divides H <= 4096",
+                (long long)H, (long long)Hkv);
+  if (rope_mode < 0 || rope_mode > 2) return fail(DQ_EINVAL, "rope_mode %d not 0, 1 or 2", rope_mode);
+  if (ldqkv < (H + 2 * Hkv) * D || ldqkv % 4)
+    return fail(DQ_EINVAL, "ldqkv = %lld: need >= (H + 2 Hkv) D and a multiple of 4",
+                (long long)ldqkv);
+  if (ldo < H * D) return fail(DQ_EINVAL, "ldo = %lld < H D", (long long)ldo);
+  // one workgroup per (head, 32 or 64 queries), numbered in 32 bits
+  if (H * ((L + 31) / 32) > (int64_t)INT32_MAX) return fail(DQ_EINVAL, "L x H too large");
+  if (L == 0) return ok();
+  if (!qkv || !out || (rope_mode && !rope)) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(qkv, 16) || !aligned(out, 4) || (rope_mode && !aligned(rope, 8)))
+    return fail(DQ_EINVAL, "qkv must be 16-byte aligned, out 4-byte, rope 8-byte");
+  return launched(dq::launch_attention(L, H, Hkv, qkv, ldqkv, rope, rope_mode, out, ldo, stream),
+                  "dq_attention");
 }
 
 int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const void *qa,

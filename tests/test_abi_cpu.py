@@ -151,3 +151,26 @@ def test_sampler_workspaces_and_host_checks(lib):
     assert lib.dq_logits_stats(0, 1000, None, 1000, 1.0, None, None, None, 0, None) == dq.DQ_OK
     assert lib.dq_qgemm_rows_sample(dq.Q6_K, 160, 0, 4096, 4096, None, 4096, None, None, 1.0,
                                     None, None, None, 0, None) == dq.DQ_OK
+
+
+def test_attention_host_checks(lib):
+    ld = (32 + 2 * 32) * 128
+    ok_args = dict(L=160, H=32, Hkv=32, D=128, qkv=256, ldqkv=ld, rope=256, mode=1, out=256,
+                   ldo=4096)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.dq_attention(a["L"], a["H"], a["Hkv"], a["D"], a["qkv"], a["ldqkv"], a["rope"],
+                                a["mode"], a["out"], a["ldo"], None)
+    assert call(D=64) == dq.DQ_EUNSUPPORTED
+    assert call(Hkv=5) == dq.DQ_EINVAL              # does not divide H
+    assert call(Hkv=0) == dq.DQ_EINVAL
+    assert call(mode=3) == dq.DQ_EINVAL
+    assert call(ldqkv=ld - 4) == dq.DQ_EINVAL        # shorter than the three blocks
+    assert call(ldqkv=ld + 2) == dq.DQ_EINVAL        # not a multiple of 4
+    assert call(ldo=4095) == dq.DQ_EINVAL
+    assert call(qkv=None) == dq.DQ_EINVAL
+    assert call(rope=None) == dq.DQ_EINVAL           # NORM needs the table
+    assert call(qkv=264) == dq.DQ_EINVAL             # qkv not 16-byte aligned
+    assert call(rope=260) == dq.DQ_EINVAL            # rope not 8-byte aligned
+    assert call(L=0) == dq.DQ_OK                     # empty canvas: nothing to do
