@@ -244,6 +244,7 @@ def main():
     if args.counters:
         run_calls(sp)
         sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws, reps=0)
+        attention_shapes(lib, dq, torch, stream, sp, up, reps=0)
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -274,6 +275,8 @@ def main():
     log("per-kind (isolated launches):", json.dumps(kernels))
     sampler = sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws)
     log("output projection feeding the samplers:", json.dumps(sampler))
+    attn = attention_shapes(lib, dq, torch, stream, sp, up)
+    log("canvas attention:", json.dumps(attn))
 
     # ------------------------------------------ the step as one HIP graph
     # The step's launches are captured once and replayed: the host then
@@ -357,6 +360,7 @@ def main():
                      "ops_per_launch": int(dom_ops), "launches": dom_launches},
         "kernels_isolated": kernels,
         "sampler_output_projection": sampler,
+        "attention": attn,
         "step_timing": f"HIP graph replay of the step's {len(calls)} launches",
         "device": torch.cuda.get_device_properties(dev).name,
     }
@@ -429,6 +433,46 @@ def sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits
     if not (torch.equal(token, tok_u) and torch.equal(stats[:, 0], st_u[:, 0])):
         raise RuntimeError("fused and unfused sampler statistics differ")
     return out
+
+
+def attention_shapes(lib, dq, torch, stream, sp, up, reps=20):
+    """Bidirectional attention over the LLaDA-8B (L = 160, 32 heads, NORM RoPE) and
+    Dream-7B (L = 512, 28 query heads over 4 kv heads, NEOX RoPE) canvases, on
+    seeded Q/K/V rows: not part of the timed step (whose O projection reads a
+    seeded input).  HIP events around `reps` back-to-back calls on the step's
+    stream; algorithmic bytes are the f32 Q/K/V rows and RoPE table read and the
+    f32 output written, operations 4 L^2 H D (two products)."""
+    res = {}
+    for name, cfg, mode in (("llada", synth.LLADA, 1), ("dream", synth.DREAM, 2)):
+        Ln, H, Hkv, D = cfg["L"], cfg["heads"], cfg["kv_heads"], cfg["head_dim"]
+        rng = np.random.default_rng(synth.seed(6, 0, mode))
+        qkv = up(synth.qkv_rows(rng, Ln, H, Hkv, D))
+        tab = up(synth.rope_table(Ln, D, cfg["rope_theta"]))
+        out = torch.empty((Ln, H * D), dtype=torch.float32, device=qkv.device)
+        wsa = torch.empty(dq.attention_workspace(Ln, H, Hkv, D), dtype=torch.uint8,
+                          device=qkv.device)
+        args = (Ln, H, Hkv, D, qkv.data_ptr(), qkv.shape[1], tab.data_ptr(), mode,
+                out.data_ptr(), H * D, wsa.data_ptr(), wsa.numel(), sp)
+        for _ in range(3 if reps else 1):
+            if lib.dq_attention(*args):
+                raise RuntimeError(lib.dq_last_error().decode())
+        torch.cuda.synchronize()
+        if not reps:
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            lib.dq_attention(*args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        nbytes = qkv.numel() * 4 + tab.numel() * 4 + out.numel() * 4
+        flops = 4 * Ln * Ln * H * D
+        res[name] = {"L": Ln, "heads": H, "kv_heads": Hkv, "us": round(us, 2),
+                     "algorithmic_MB": round(nbytes / 1e6, 2), "GB_s": round(nbytes / us / 1e3, 1),
+                     "TFLOPs": round(flops / us / 1e6, 2),
+                     "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):

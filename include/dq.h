@@ -286,8 +286,8 @@ int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream);
 
 /* --------------------------------------------------------------------------
- * dq_attention -- bidirectional attention of every canvas position over all
- * L positions.
+ * dq_attention_workspace / dq_attention -- bidirectional attention of every
+ * canvas position over all L positions.
  *
  * Source: Architecture page, "A forward pass", step 2 (RoPE rotates Q and K;
  * attention runs over all L positions with no mask) and "Source map" (NORM
@@ -314,11 +314,17 @@ int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
  *           8-byte aligned; ignored (may be NULL) for rope_mode 0.
  *   out   : device f32, L rows of H*D, row stride ldo >= H D; only those
  *           columns are written.
+ *   ws    : device workspace of at least dq_attention_workspace(L, H, Hkv, D)
+ *           bytes (Hkv * ceil(L/32) * 20 KB: each kv head's keys and values,
+ *           rotated and rounded to binary16, in blocks of 32 keys), 16-byte
+ *           aligned; its contents are overwritten.
  * Errors: DQ_EUNSUPPORTED (D), DQ_EINVAL (shapes, H % Hkv, rope_mode, strides,
- *         NULL, alignment), DQ_EHIP.
+ *         NULL, alignment), DQ_EWORKSPACE, DQ_EHIP.
  * ------------------------------------------------------------------------ */
+int dq_attention_workspace(int64_t L, int64_t H, int64_t Hkv, int64_t D, size_t *bytes);
 int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv, int64_t ldqkv,
-                 const float *rope, int rope_mode, float *out, int64_t ldo, hipStream_t stream);
+                 const float *rope, int rope_mode, float *out, int64_t ldo, void *ws,
+                 size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
  * dq_debug_superblock_sums -- test hook.  Runs the dq_qgemm kernel with its

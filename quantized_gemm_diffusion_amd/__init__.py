@@ -34,7 +34,7 @@ EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_wei
            "dq_act_size", "dq_quantize_act", "dq_swiglu_quantize_act", "dq_rmsnorm_quantize_act",
            "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_logits_stats_workspace",
            "dq_logits_stats", "dq_qgemm_rows_sample_workspace", "dq_qgemm_rows_sample",
-           "dq_attention", "dq_debug_superblock_sums")
+           "dq_attention_workspace", "dq_attention", "dq_debug_superblock_sums")
 ACT_RECORD = 5120  # bytes per (super-block, 16-row block) record
 
 
@@ -85,7 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dq_qgemm_rows_sample_workspace": [i64, i64, i64, psz],
             "dq_qgemm_rows_sample": [i32, i64, i64, i64, i64, vp, i64, vp, vp, ctypes.c_float, vp,
                                      vp, vp, sz, vp],
-            "dq_attention": [i64, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp],
+            "dq_attention_workspace": [i64, i64, i64, i64, psz],
+            "dq_attention": [i64, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, sz, vp],
             "dq_debug_superblock_sums": [i32, i64, i64, i64, vp, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
@@ -367,11 +368,20 @@ def debug_superblock_sums(type_: int, act: Act, packed: torch.Tensor, N: int):
 ROPE_NONE, ROPE_NORM, ROPE_NEOX = 0, 1, 2
 
 
+def attention_workspace(L: int, H: int, Hkv: int, D: int = 128) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_attention_workspace(L, H, Hkv, D, ctypes.byref(out)), "dq_attention_workspace")
+    return out.value
+
+
 def attention(qkv: torch.Tensor, H: int, Hkv: int, D: int = 128, rope: torch.Tensor | None = None,
-              rope_mode: int = ROPE_NONE, out: torch.Tensor | None = None) -> torch.Tensor:
+              rope_mode: int = ROPE_NONE, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None) -> torch.Tensor:
     """Bidirectional attention over the canvas: qkv f32 [L, >= (H + 2 Hkv) D] rows
     [Q | K | V]; rope f32 [L, D/2, 2] (cos, sin) for rope_mode NORM or NEOX;
-    returns out f32 [L, H D]."""
+    ws: uint8 workspace of attention_workspace(L, H, Hkv, D) bytes (allocated
+    when None); returns out f32 [L, H D]."""
     lib = load_library()
     _need(qkv, torch.float32, "qkv")
     if qkv.dim() != 2 or qkv.stride(1) != 1:
@@ -390,8 +400,9 @@ def attention(qkv: torch.Tensor, H: int, Hkv: int, D: int = 128, rope: torch.Ten
     _need(out, torch.float32, "out")
     if out.dim() != 2 or out.shape[0] != L or out.shape[1] < H * D or out.stride(1) != 1:
         raise ValueError("out must be [L, >= H D] with unit column stride")
+    ws = _ws(attention_workspace(L, H, Hkv, D), ws, qkv.device)
     _check(lib.dq_attention(L, H, Hkv, D, _ptr(qkv), qkv.stride(0) if L > 1 else qkv.shape[1],
                             _ptr(rope) if rope is not None else None, rope_mode, _ptr(out),
-                            out.stride(0) if L > 1 else out.shape[1], _stream(qkv)),
-           "dq_attention")
+                            out.stride(0) if L > 1 else out.shape[1], _ptr(ws), ws.numel(),
+                            _stream(qkv)), "dq_attention")
     return out

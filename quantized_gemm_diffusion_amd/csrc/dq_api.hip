@@ -330,26 +330,45 @@ int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
                   "dq_qgemm_rows_sample (finish)");
 }
 
-int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv, int64_t ldqkv,
-                 const float *rope, int rope_mode, float *out, int64_t ldo, hipStream_t stream) {
+static int check_attention_shape(int64_t L, int64_t H, int64_t Hkv, int64_t D) {
   if (D != dq::ATTN_HEAD_DIM)
     return fail(DQ_EUNSUPPORTED, "head dimension %lld (only 128 is built)", (long long)D);
-  if (L < 0 || L > ((int64_t)1 << 24)) return fail(DQ_EINVAL, "L = %lld out of range", (long long)L);
+  if (L < 0 || L > ((int64_t)1 << 20)) return fail(DQ_EINVAL, "L = %lld out of range", (long long)L);
   if (H <= 0 || Hkv <= 0 || H % Hkv || H > 4096)
     return fail(DQ_EINVAL, "H = %lld, Hkv = %lld: need 0 < Hkv, Hkv divides H <= 4096",
                 (long long)H, (long long)Hkv);
+  // one kv head's key blocks are addressed with 32-bit offsets
+  if (dq::attention_workspace_bytes(L, 1) > (int64_t)INT32_MAX)
+    return fail(DQ_EINVAL, "L = %lld too long", (long long)L);
+  return DQ_OK;
+}
+
+int dq_attention_workspace(int64_t L, int64_t H, int64_t Hkv, int64_t D, size_t *bytes) {
+  if (int s = check_attention_shape(L, H, Hkv, D)) return s;
+  if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
+  *bytes = (size_t)dq::attention_workspace_bytes(L, Hkv);
+  return ok();
+}
+
+int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv, int64_t ldqkv,
+                 const float *rope, int rope_mode, float *out, int64_t ldo, void *ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  if (int s = check_attention_shape(L, H, Hkv, D)) return s;
   if (rope_mode < 0 || rope_mode > 2) return fail(DQ_EINVAL, "rope_mode %d not 0, 1 or 2", rope_mode);
   if (ldqkv < (H + 2 * Hkv) * D || ldqkv % 4)
     return fail(DQ_EINVAL, "ldqkv = %lld: need >= (H + 2 Hkv) D and a multiple of 4",
                 (long long)ldqkv);
   if (ldo < H * D) return fail(DQ_EINVAL, "ldo = %lld < H D", (long long)ldo);
-  // one workgroup per (head, 32 or 64 queries), numbered in 32 bits
-  if (H * ((L + 31) / 32) > (int64_t)INT32_MAX) return fail(DQ_EINVAL, "L x H too large");
   if (L == 0) return ok();
   if (!qkv || !out || (rope_mode && !rope)) return fail(DQ_EINVAL, "NULL pointer argument");
   if (!aligned(qkv, 16) || !aligned(out, 4) || (rope_mode && !aligned(rope, 8)))
     return fail(DQ_EINVAL, "qkv must be 16-byte aligned, out 4-byte, rope 8-byte");
-  return launched(dq::launch_attention(L, H, Hkv, qkv, ldqkv, rope, rope_mode, out, ldo, stream),
+  const size_t need = (size_t)dq::attention_workspace_bytes(L, Hkv);
+  if (!ws || ws_bytes < need)
+    return fail(DQ_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned(ws, 16)) return fail(DQ_EINVAL, "workspace must be 16-byte aligned");
+  return launched(dq::launch_attention(L, H, Hkv, qkv, ldqkv, rope, rope_mode,
+                                       static_cast<uint8_t *>(ws), out, ldo, stream),
                   "dq_attention");
 }
 

@@ -155,13 +155,16 @@ def test_sampler_workspaces_and_host_checks(lib):
 
 def test_attention_host_checks(lib):
     ld = (32 + 2 * 32) * 128
+    need = dq.attention_workspace(160, 32, 32)
+    assert need == 32 * 5 * 20480                    # per kv head and 32 keys, one 20 KB image
+    assert dq.attention_workspace(512, 28, 4) == 4 * 16 * 20480
     ok_args = dict(L=160, H=32, Hkv=32, D=128, qkv=256, ldqkv=ld, rope=256, mode=1, out=256,
-                   ldo=4096)
+                   ldo=4096, ws=256, wsb=need)
 
     def call(**kw):
         a = dict(ok_args, **kw)
         return lib.dq_attention(a["L"], a["H"], a["Hkv"], a["D"], a["qkv"], a["ldqkv"], a["rope"],
-                                a["mode"], a["out"], a["ldo"], None)
+                                a["mode"], a["out"], a["ldo"], a["ws"], a["wsb"], None)
     assert call(D=64) == dq.DQ_EUNSUPPORTED
     assert call(Hkv=5) == dq.DQ_EINVAL              # does not divide H
     assert call(Hkv=0) == dq.DQ_EINVAL
@@ -173,4 +176,7 @@ def test_attention_host_checks(lib):
     assert call(rope=None) == dq.DQ_EINVAL           # NORM needs the table
     assert call(qkv=264) == dq.DQ_EINVAL             # qkv not 16-byte aligned
     assert call(rope=260) == dq.DQ_EINVAL            # rope not 8-byte aligned
+    assert call(wsb=need - 1) == dq.DQ_EWORKSPACE
+    assert call(ws=None) == dq.DQ_EWORKSPACE
+    assert call(ws=264) == dq.DQ_EINVAL              # workspace not 16-byte aligned
     assert call(L=0) == dq.DQ_OK                     # empty canvas: nothing to do

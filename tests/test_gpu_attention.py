@@ -13,8 +13,8 @@ ATT_TOL = 1e-3 leaves a factor 2 over their sum.
 Shapes: LLaDA-8B (L = 160, 32 heads, NORM RoPE, theta 5e5) and Dream-7B
 (L = 512, 28 query heads over 4 kv heads, NEOX RoPE, theta 1e6) canvases; a
 single position; a block and one key; ragged L with strided input and output
-rows, no RoPE; an unaligned output (element stores); peaked scores; the
-4-wave workgroup shape.
+rows, no RoPE; an unaligned output (element stores); peaked scores; every
+workgroup shape (groups of 1, 3, 8, 16 and 32 query heads per kv head).
 """
 import numpy as np
 import pytest
@@ -67,7 +67,9 @@ def _run(dq, L, H, Hkv, mode, theta=10000.0, scale=1.0, seed=0, pad_in=0, pad_ou
         assert np.isnan(got[:, H * D:]).all(), "padding columns written"
     tail = out_buf[out_offset + L * ldo:].cpu().numpy()
     assert np.isnan(tail).all(), "wrote past the output"
-    return np.max(err / np.maximum(tol, 1e-300))
+    worst = np.max(err / np.maximum(tol, 1e-300))
+    print(f"attention L={L} H={H} Hkv={Hkv} mode={mode}: worst err/tol {worst:.3g}")
+    return worst
 
 
 def test_attention_llada_canvas(dq):
@@ -95,9 +97,15 @@ def test_attention_peaked_scores(dq):
     _run(dq, 96, 8, 2, oracle.ROPE_NORM, scale=4.0, seed=5)
 
 
-def test_attention_four_wave_workgroups(dq):
-    # H * ceil(L / 64) >= 256 selects 64 queries per workgroup
-    _run(dq, 300, 64, 8, oracle.ROPE_NEOX, seed=6)
+@pytest.mark.parametrize("L,H,Hkv", [
+    (300, 64, 8),    # groups of 8 heads: 8 heads x 2 query tiles per workgroup
+    (70, 6, 2),      # groups of 3: the 4-head shape with one idle head
+    (40, 32, 2),     # groups of 16: 16 heads x 1 query tile
+    (45, 64, 2),     # groups of 32: two workgroups per group
+    (60, 8, 8),      # no sharing, 4 query tiles: the 4-tile shape
+])
+def test_attention_workgroup_shapes(dq, L, H, Hkv):
+    _run(dq, L, H, Hkv, oracle.ROPE_NEOX, seed=6 + H)
 
 
 def test_attention_deterministic(dq):
