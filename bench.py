@@ -133,8 +133,9 @@ def main():
     t0 = time.perf_counter()
     act_rng = np.random.default_rng(synth.seed(2, 0, 9))
     # the residual stream in front of attention and of the FFN, and attention's
-    # output (attention is not part of this path); the down projection's input is
-    # made by the step itself from the gate/up GEMM's output
+    # output (attention is timed on its own, below, not inside the GEMM step); the
+    # down projection's input is made by the step itself from the gate/up GEMM's
+    # output
     acts = {"qkv": up(synth.activations(act_rng, L, K)), "o": up(synth.activations(act_rng, L, K)),
             "ffn": up(synth.activations(act_rng, L, K))}
     norm_rng = np.random.default_rng(synth.seed(2, 0, 8))
