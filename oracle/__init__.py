@@ -24,8 +24,7 @@ import threading
 
 import numpy as np
 
-Q4_K = 12
-Q6_K = 14
+F32, F16, Q8_0, Q4_K, Q5_K, Q6_K, BF16 = 0, 1, 8, 12, 13, 14, 30  # GGUF type ids
 QK = 256
 BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
 SUBBLOCKS = {Q4_K: 8, Q6_K: 16}
@@ -83,12 +82,19 @@ def _load():
             lib.dqo_f32_to_fp16_n.argtypes = [vp, vp, i64]
             lib.dqo_rope_pair.argtypes = [ctypes.c_float] * 4 + [vp, vp]
             lib.dqo_rope_rows.argtypes = [i64, i64, i64, vp, i64, vp, ctypes.c_int]
+            lib.dqo_decode_q8_0.argtypes = [vp, vp, vp]
+            lib.dqo_decode_q5k.argtypes = [vp] * 6
+            lib.dqo_row_bytes.restype = i64
+            lib.dqo_row_bytes.argtypes = [ctypes.c_int, i64]
+            lib.dqo_decode_row.argtypes = [ctypes.c_int, vp, i64, vp]
+            lib.dqo_embed_rows.argtypes = [ctypes.c_int, i64, i64, vp, vp, i64, vp, i64, vp]
             lib.dqo_attention.argtypes = [i64, i64, i64, i64, vp, i64, vp, ctypes.c_int, vp, i64,
                                           vp]
             for name in ("dqo_dequant_row", "dqo_quantize_act", "dqo_swiglu_quantize_act",
                          "dqo_rmsnorm_quantize_act", "dqo_subdots",
                          "dqo_superblock_sums", "dqo_qgemm_ref", "dqo_qgemm_ref_points",
-                         "dqo_qgemm_f32", "dqo_logits_stats", "dqo_attention", "dqo_rope_rows"):
+                         "dqo_qgemm_f32", "dqo_logits_stats", "dqo_attention", "dqo_rope_rows",
+                         "dqo_decode_row", "dqo_embed_rows"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -395,3 +401,51 @@ def attention(qkv: np.ndarray, H: int, Hkv: int, D: int, rope=None, mode: int = 
                                  _p(rope) if rope is not None else None, mode, _p(out), H * D,
                                  _p(tol)))
     return out, tol
+
+
+# --- the decoder's other block types and embedding rows ----------------------
+
+def row_bytes(type_: int, K: int) -> int:
+    """Bytes of one row of K values of a GGUF type (0: unknown type or bad K)."""
+    return int(_load().dqo_row_bytes(type_, K))
+
+
+def decode_q8_0(block: np.ndarray):
+    """34-byte Q8_0 block -> (d, q[32] int8)."""
+    block = np.ascontiguousarray(block, dtype=np.uint8)
+    d = ctypes.c_float()
+    q = np.zeros(32, np.int8)
+    _load().dqo_decode_q8_0(_p(block), ctypes.byref(d), _p(q))
+    return d.value, q
+
+
+def decode_q5k(block: np.ndarray):
+    """176-byte Q5_K block -> (d, dmin, sc[8], mn[8], q[256] in [0, 31])."""
+    block = np.ascontiguousarray(block, dtype=np.uint8)
+    d, dm = ctypes.c_float(), ctypes.c_float()
+    sc, mn, q = np.zeros(8, np.uint8), np.zeros(8, np.uint8), np.zeros(256, np.uint8)
+    _load().dqo_decode_q5k(_p(block), ctypes.byref(d), ctypes.byref(dm), _p(sc), _p(mn), _p(q))
+    return d.value, dm.value, sc, mn, q
+
+
+def decode_row(type_: int, row: np.ndarray, K: int) -> np.ndarray:
+    """One row of any supported GGUF type -> K float64 values (exact)."""
+    row = np.ascontiguousarray(row, dtype=np.uint8).reshape(-1)
+    w = np.zeros(K, np.float64)
+    _check(_load().dqo_decode_row(type_, _p(row), K, _p(w)))
+    return w
+
+
+def embed_rows(type_: int, table: np.ndarray, K: int, ids: np.ndarray):
+    """Rows ids of an N x K table in GGUF bytes (N rows of row_bytes(type, K)),
+    decoded to float32 (Architecture page, "A forward pass", step 1).  Returns
+    (out [M, K] float32, flag [M] int32: 1 where the id is outside [0, N))."""
+    rb = row_bytes(type_, K)
+    table = np.ascontiguousarray(table, dtype=np.uint8).reshape(-1)
+    N = table.size // rb if rb else 0
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    M = ids.size
+    out = np.zeros((M, K), np.float32)
+    flag = np.zeros(M, np.int32)
+    _check(_load().dqo_embed_rows(type_, N, K, _p(table), _p(ids), M, _p(out), K, _p(flag)))
+    return out, flag

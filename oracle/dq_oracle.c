@@ -696,3 +696,129 @@ int dqo_rope_rows(int64_t L, int64_t n_heads, int64_t D, float *x, int64_t ldx, 
     for (int64_t h = 0; h < n_heads; ++h) rope_vec(x + l * ldx + h * D, D, mode, rope, l);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* The decoder's other block types (Architecture page, "Source map": scalar  */
+/* F32 / F16 / BF16 / Q8_0 / Q4_K / Q5_K / Q6_K decoders, the test oracle and */
+/* the embedding rows; "A forward pass", step 1: embedding rows are decoded  */
+/* from the memory-mapped Q4_K table, one row per token).  Byte layouts are  */
+/* the public GGUF/ggml block definitions (GGUF type ids in parentheses):    */
+/*   F32 (0): 4 bytes per value;  F16 (1): IEEE binary16;                    */
+/*   BF16 (30): the top 16 bits of a binary32;                               */
+/*   Q8_0 (8): 34 bytes per 32 values: d (fp16), q[32] (int8); w = d * q;    */
+/*   Q5_K (13): 176 bytes per 256: d, dmin (fp16), scales[12] (the Q4_K       */
+/*     6-bit packing), qh[32], qs[128]; chunk c = 0..3 of 64 weights: weight  */
+/*     64c + l takes the low nibble of qs[32c + l] and bit 2c of qh[l] as its */
+/*     fifth bit, weight 64c + 32 + l the high nibble and bit 2c + 1;         */
+/*     w = d * sc_j * q - dmin * m_j with j = i / 32.                        */
+/* ------------------------------------------------------------------------ */
+#define TYPE_F32 0
+#define TYPE_F16 1
+#define TYPE_Q8_0 8
+#define TYPE_Q5K 13
+#define TYPE_BF16 30
+#define Q8_0_BYTES 34
+#define Q5K_BYTES 176
+
+void dqo_decode_q8_0(const uint8_t *blk, float *d, int8_t q[32]) {
+  *d = dqo_fp16_to_f32(rd16(blk));
+  for (int i = 0; i < 32; ++i) q[i] = (int8_t)blk[2 + i];
+}
+
+void dqo_decode_q5k(const uint8_t *blk, float *d, float *dmin, uint8_t sc[8], uint8_t mn[8],
+                    uint8_t q[256]) {
+  const uint8_t *s = blk + 4;
+  const uint8_t *qh = blk + 16;
+  const uint8_t *qs = blk + 48;
+  *d = dqo_fp16_to_f32(rd16(blk));
+  *dmin = dqo_fp16_to_f32(rd16(blk + 2));
+  for (int j = 0; j < 8; ++j) {
+    if (j < 4) {
+      sc[j] = s[j] & 63;
+      mn[j] = s[j + 4] & 63;
+    } else {
+      sc[j] = (uint8_t)((s[j + 4] & 15) | ((s[j - 4] >> 6) << 4));
+      mn[j] = (uint8_t)((s[j + 4] >> 4) | ((s[j] >> 6) << 4));
+    }
+  }
+  for (int c = 0; c < 4; ++c)
+    for (int l = 0; l < 32; ++l) {
+      q[64 * c + l] = (uint8_t)((qs[32 * c + l] & 15) | (((qh[l] >> (2 * c)) & 1) << 4));
+      q[64 * c + 32 + l] = (uint8_t)((qs[32 * c + l] >> 4) | (((qh[l] >> (2 * c + 1)) & 1) << 4));
+    }
+}
+
+/* Bytes of one row of K values of the type (0 if unknown or K does not fit */
+/* its blocks).                                                              */
+int64_t dqo_row_bytes(int type, int64_t K) {
+  switch (type) {
+    case TYPE_F32: return 4 * K;
+    case TYPE_F16:
+    case TYPE_BF16: return 2 * K;
+    case TYPE_Q8_0: return K % 32 ? 0 : K / 32 * Q8_0_BYTES;
+    case TYPE_Q4K: return K % QK ? 0 : K / QK * Q4K_BYTES;
+    case TYPE_Q5K: return K % QK ? 0 : K / QK * Q5K_BYTES;
+    case TYPE_Q6K: return K % QK ? 0 : K / QK * Q6K_BYTES;
+    default: return 0;
+  }
+}
+
+/* One row of any of the types to binary64 values (every one exact).        */
+int dqo_decode_row(int type, const uint8_t *row, int64_t K, double *w) {
+  if (!dqo_row_bytes(type, K)) return -1;
+  if (type == TYPE_Q4K || type == TYPE_Q6K) return dqo_dequant_row(type, row, K, w);
+  for (int64_t i = 0; i < K; ++i) {
+    if (type == TYPE_F32) {
+      float f;
+      memcpy(&f, row + 4 * i, 4);
+      w[i] = f;
+    } else if (type == TYPE_F16) {
+      w[i] = dqo_fp16_to_f32(rd16(row + 2 * i));
+    } else if (type == TYPE_BF16) {
+      const uint32_t bits = (uint32_t)rd16(row + 2 * i) << 16;
+      float f;
+      memcpy(&f, &bits, 4);
+      w[i] = f;
+    }
+  }
+  if (type == TYPE_Q8_0) {
+    for (int64_t b = 0; b < K / 32; ++b) {
+      float d;
+      int8_t q[32];
+      dqo_decode_q8_0(row + b * Q8_0_BYTES, &d, q);
+      for (int i = 0; i < 32; ++i) w[32 * b + i] = (double)d * q[i];
+    }
+  } else if (type == TYPE_Q5K) {
+    for (int64_t b = 0; b < K / QK; ++b) {
+      float d, dmin;
+      uint8_t sc[8], mn[8], q[256];
+      dqo_decode_q5k(row + b * Q5K_BYTES, &d, &dmin, sc, mn, q);
+      for (int i = 0; i < QK; ++i)
+        w[QK * b + i] = (double)d * sc[i / 32] * q[i] - (double)dmin * mn[i / 32];
+    }
+  }
+  return 0;
+}
+
+/* Embedding rows: out[i][k] = row ids[i] of the N x K table, decoded and   */
+/* rounded once to binary32 (out row stride ldo); an id outside [0, N) gives */
+/* a row of zeros and flag[i] = 1 (else 0).                                  */
+int dqo_embed_rows(int type, int64_t N, int64_t K, const uint8_t *table, const int32_t *ids,
+                   int64_t M, float *out, int64_t ldo, int32_t *flag) {
+  const int64_t rb = dqo_row_bytes(type, K);
+  if (!rb || ldo < K) return -1;
+  double *w = (double *)malloc(sizeof(double) * (size_t)K);
+  if (!w) return -2;
+  for (int64_t i = 0; i < M; ++i) {
+    const int64_t id = ids[i];
+    flag[i] = id < 0 || id >= N;
+    if (flag[i]) {
+      for (int64_t k = 0; k < K; ++k) out[i * ldo + k] = 0.0f;
+      continue;
+    }
+    dqo_decode_row(type, table + id * rb, K, w);
+    for (int64_t k = 0; k < K; ++k) out[i * ldo + k] = (float)w[k];
+  }
+  free(w);
+  return 0;
+}

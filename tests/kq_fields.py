@@ -126,3 +126,85 @@ def dequant_q6k_fields(f) -> np.ndarray:
     d = f["d"].astype(np.float64)[:, :, None]
     sc = np.repeat(f["sc"], 16, axis=2).astype(np.float64)
     return (d * sc * (f["q"] - 32)).reshape(N, nb * 256)
+
+
+# --- Q5_K and Q8_0 (the decoder's other block types) --------------------------
+
+def q5k_position(i: int):
+    """(qs byte, qs shift, qh byte, qh bit) of the 5-bit code of weight i."""
+    c, r = divmod(i, 64)
+    l = r % 32
+    upper = r >= 32
+    return 32 * c + l, (4 if upper else 0), l, 2 * c + (1 if upper else 0)
+
+
+def enc_q5k(d: float, dmin: float, sc, mn, q) -> np.ndarray:
+    """Fields -> one 176-byte Q5_K block.  sc, mn in [0,63] (Q4_K packing); q in [0,31]."""
+    blk = np.zeros(176, np.uint8)
+    blk[0:2] = np.array([d], np.float16).view(np.uint8)
+    blk[2:4] = np.array([dmin], np.float16).view(np.uint8)
+    s = np.zeros(12, np.int64)
+    for j in range(8):
+        sp, mp = q4k_scale_bits(j)
+        for (byte, shift, width, vshift) in sp:
+            s[byte] |= ((int(sc[j]) >> vshift) & ((1 << width) - 1)) << shift
+        for (byte, shift, width, vshift) in mp:
+            s[byte] |= ((int(mn[j]) >> vshift) & ((1 << width) - 1)) << shift
+    blk[4:16] = s.astype(np.uint8)
+    qh = np.zeros(32, np.int64)
+    qs = np.zeros(128, np.int64)
+    for i in range(256):
+        qb, qsft, hb, hbit = q5k_position(i)
+        qs[qb] |= (int(q[i]) & 15) << qsft
+        qh[hb] |= ((int(q[i]) >> 4) & 1) << hbit
+    blk[16:48] = qh.astype(np.uint8)
+    blk[48:176] = qs.astype(np.uint8)
+    return blk
+
+
+def enc_q8_0(d: float, q) -> np.ndarray:
+    """Fields -> one 34-byte Q8_0 block: d as fp16, q int8 [32]."""
+    blk = np.zeros(34, np.uint8)
+    blk[0:2] = np.array([d], np.float16).view(np.uint8)
+    blk[2:34] = np.asarray(q, np.int8).view(np.uint8)
+    return blk
+
+
+def random_q5k_fields(rng, N, nb):
+    f = random_q4k_fields(rng, N, nb)
+    f["q"] = rng.integers(0, 32, (N, nb, 256))
+    return f
+
+
+def random_q8_0_fields(rng, N, nblk32):
+    d = (np.abs(rng.standard_normal((N, nblk32))) * 2e-2).astype(np.float16)
+    q = rng.integers(-128, 128, (N, nblk32, 32))
+    return dict(d=d, q=q)
+
+
+def encode_q5k_matrix(f) -> np.ndarray:
+    N, nb = f["d"].shape
+    out = np.zeros((N, nb, 176), np.uint8)
+    for n in range(N):
+        for b in range(nb):
+            out[n, b] = enc_q5k(f["d"][n, b], f["dmin"][n, b], f["sc"][n, b], f["mn"][n, b],
+                                f["q"][n, b])
+    return out
+
+
+def encode_q8_0_matrix(f) -> np.ndarray:
+    N, nb = f["d"].shape
+    out = np.zeros((N, nb, 34), np.uint8)
+    for n in range(N):
+        for b in range(nb):
+            out[n, b] = enc_q8_0(f["d"][n, b], f["q"][n, b])
+    return out
+
+
+def dequant_q5k_fields(f) -> np.ndarray:
+    return dequant_q4k_fields(f)  # same formula, 5-bit codes
+
+
+def dequant_q8_0_fields(f) -> np.ndarray:
+    N, nb = f["d"].shape
+    return (f["d"].astype(np.float64)[:, :, None] * f["q"]).reshape(N, nb * 32)

@@ -26,6 +26,11 @@
   (and exact special angles); attention closed forms (one position, equal
   keys, constant values, two keys), permutation equivariance, shared kv heads,
   and rotation invariance of the scores (RoPE depends on relative position).
+* The decoder's other types: binary16 exhaustively against numpy; bfloat16 on
+  exact constants and on every binary32 whose low half is zero; Q8_0 and Q5_K
+  on hand-built blocks with closed-form values (every code, the fifth bit in
+  every chunk) and on random fields through the per-weight encoder; embedding
+  rows equal to the decoded rows they select, out-of-range ids flagged.
 """
 import os
 
@@ -639,3 +644,74 @@ def test_attention_rope_scores_depend_on_relative_position(mode):
     # without RoPE every score is the same: uniform weights
     out0, _ = oracle.attention(qkv, 1, 1, D)
     np.testing.assert_allclose(out0[:, :L], 1.0 / L, rtol=1e-12)
+
+
+# --- the decoder's other block types --------------------------------------------
+
+from kq_fields import (dequant_q5k_fields, dequant_q8_0_fields, enc_q5k, enc_q8_0,  # noqa: E402
+                       encode_q5k_matrix, encode_q8_0_matrix, random_q5k_fields,
+                       random_q8_0_fields)
+
+
+def test_f16_and_bf16_rows():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    w = oracle.decode_row(oracle.F16, bits.view(np.uint8), 1 << 16)
+    ref = bits.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(w[fin], ref[fin])
+    assert np.all(np.isinf(w[np.isinf(ref)])) and np.all(np.isnan(w[np.isnan(ref)]))
+    consts = {0x3F80: 1.0, 0xC000: -2.0, 0x3E20: 0.15625, 0x4049: 3.140625, 0x0000: 0.0,
+              0x0001: 2.0 ** -133, 0x7F7F: 3.3895313892515355e38}
+    keys = np.array(list(consts), np.uint16)
+    w = oracle.decode_row(oracle.BF16, keys.view(np.uint8), len(keys))
+    assert np.array_equal(w, np.array(list(consts.values())))
+    # every binary32 with a zero low half is its own top half
+    x = (np.random.default_rng(71).integers(0, 1 << 16, 4096).astype(np.uint32) << 16)
+    x = x[np.isfinite(x.view(np.float32))]
+    w = oracle.decode_row(oracle.BF16, (x >> 16).astype(np.uint16).view(np.uint8), x.size)
+    assert np.array_equal(w, x.view(np.float32).astype(np.float64))
+    f = np.random.default_rng(72).standard_normal(300).astype(np.float32)
+    assert np.array_equal(oracle.decode_row(oracle.F32, f.view(np.uint8), 300), f.astype(np.float64))
+
+
+def test_q8_0_closed_form_and_round_trip():
+    q = np.arange(-128, 128, dtype=np.int64).reshape(8, 32)
+    row = np.concatenate([enc_q8_0(0.5, q[b]) for b in range(8)])
+    d, qq = oracle.decode_q8_0(row[:34])
+    assert d == 0.5 and np.array_equal(qq, q[0])
+    assert np.array_equal(oracle.decode_row(oracle.Q8_0, row, 256), np.arange(-128, 128) / 2.0)
+    f = random_q8_0_fields(np.random.default_rng(73), 5, 6)
+    W = encode_q8_0_matrix(f).reshape(5, -1)
+    for n in range(5):
+        assert np.array_equal(oracle.decode_row(oracle.Q8_0, W[n], 192), dequant_q8_0_fields(f)[n])
+
+
+def test_q5k_closed_form_and_round_trip():
+    # d = 1, dmin = 0.5, sc_j = j + 1 (the high-bit scales need j >= 4 slots up to 63),
+    # m_j = 2j, q_i = i mod 32 (the fifth bit set in half of each chunk)
+    sc = [1, 2, 3, 4, 61, 62, 63, 40]
+    mn = [0, 2, 4, 6, 8, 63, 12, 14]
+    q = np.arange(256) % 32
+    blk = enc_q5k(1.0, 0.5, sc, mn, q)
+    d, dm, s2, m2, q2 = oracle.decode_q5k(blk)
+    assert (d, dm) == (1.0, 0.5)
+    assert list(s2) == sc and list(m2) == mn and np.array_equal(q2, q)
+    ref = np.array([sc[i // 32] * q[i] - 0.5 * mn[i // 32] for i in range(256)], np.float64)
+    assert np.array_equal(oracle.decode_row(oracle.Q5_K, blk, 256), ref)
+    f = random_q5k_fields(np.random.default_rng(74), 4, 3)
+    W = encode_q5k_matrix(f).reshape(4, -1)
+    for n in range(4):
+        assert np.array_equal(oracle.decode_row(oracle.Q5_K, W[n], 768), dequant_q5k_fields(f)[n])
+
+
+def test_embed_rows_select_and_flag():
+    rng = np.random.default_rng(75)
+    N, K = 7, 512
+    f = random_q5k_fields(rng, N, K // 256)
+    table = encode_q5k_matrix(f).reshape(N, -1)
+    ids = np.array([3, 0, 6, 3, -1, 7], np.int32)
+    out, flag = oracle.embed_rows(oracle.Q5_K, table, K, ids)
+    ref = dequant_q5k_fields(f).astype(np.float32)
+    assert np.array_equal(flag, [0, 0, 0, 0, 1, 1])
+    assert np.array_equal(out[:4], ref[ids[:4]]) and not out[4:].any()
+    assert oracle.row_bytes(oracle.Q8_0, 100) == 0 and oracle.row_bytes(99, 256) == 0
