@@ -140,7 +140,9 @@ int dqo_dequant_row(int type, const uint8_t *row, int64_t K, double *w) {
       int8_t sc[16];
       uint8_t q[256];
       dqo_decode_q6k(blk, &d, sc, q);
-      for (int i = 0; i < QK; ++i) o[i] = (double)d * sc[i / 16] * ((int)q[i] - 32);
+      /* the integer sc * (q - 32) first: the same exact value, with the sign */
+      /* of a zero product taken from d alone                                 */
+      for (int i = 0; i < QK; ++i) o[i] = (double)d * (double)(sc[i / 16] * ((int)q[i] - 32));
     }
   }
   return 0;
