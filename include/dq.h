@@ -327,6 +327,33 @@ int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv,
                  size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * dq_row_bytes / dq_embed_rows -- embedding rows: the rows of a GGUF table
+ * selected by token id, decoded to f32.
+ *
+ * Source: Architecture page, "A forward pass", step 1 (embedding rows are
+ * decoded from the memory-mapped Q4_K table, one row per token) and "Source
+ * map" (scalar F32 / F16 / BF16 / Q8_0 / Q4_K / Q5_K / Q6_K decoders).  The
+ * table is N rows of dq_row_bytes(type, K) bytes in the public GGUF block
+ * layouts, as stored in the file (not repacked).  Types (GGUF ids): F32 0,
+ * F16 1, Q8_0 8 (34-byte blocks of 32: fp16 d, int8 q; w = d q), Q4_K 12,
+ * Q5_K 13 (176-byte blocks: d, dmin, the Q4_K 6-bit scales, qh[32] fifth
+ * bits, qs[128] nibbles; w = d sc q - dmin m), Q6_K 14, BF16 30.  Every value
+ * is the correctly rounded binary32 of its definition (exact for all but Q4_K
+ * and Q5_K, whose d sc q - dmin m is rounded once).
+ *
+ *   K     : values per row, a positive multiple of 256.
+ *   table : device bytes, 16-byte aligned; read only.
+ *   ids   : device int32 [M]; ids outside [0, N) give a row of zeros and,
+ *           when flags is not NULL, flags[i] = 1 (0 for valid ids).
+ *   out   : device f32, M rows of K, row stride ldo >= K.
+ * Errors: DQ_EUNSUPPORTED (type), DQ_EINVAL (K, shapes, ldo, NULL,
+ *         alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_row_bytes(int type, int64_t K, size_t *bytes);
+int dq_embed_rows(int type, int64_t N, int64_t K, const void *table, const int32_t *ids,
+                  int64_t M, float *out, int64_t ldo, int32_t *flags, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * dq_debug_superblock_sums -- test hook.  Runs the dq_qgemm kernel with its
  * fold replaced by stores of the exact per-super-block integers, so that the
  * integer part of the production code path can be compared bit for bit:

@@ -34,7 +34,8 @@ EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_wei
            "dq_act_size", "dq_quantize_act", "dq_swiglu_quantize_act", "dq_rmsnorm_quantize_act",
            "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_logits_stats_workspace",
            "dq_logits_stats", "dq_qgemm_rows_sample_workspace", "dq_qgemm_rows_sample",
-           "dq_attention_workspace", "dq_attention", "dq_debug_superblock_sums")
+           "dq_attention_workspace", "dq_attention", "dq_row_bytes", "dq_embed_rows",
+           "dq_debug_superblock_sums")
 ACT_RECORD = 5120  # bytes per (super-block, 16-row block) record
 
 
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      vp, vp, sz, vp],
             "dq_attention_workspace": [i64, i64, i64, i64, psz],
             "dq_attention": [i64, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, sz, vp],
+            "dq_row_bytes": [i32, i64, psz],
+            "dq_embed_rows": [i32, i64, i64, vp, vp, i64, vp, i64, vp, vp],
             "dq_debug_superblock_sums": [i32, i64, i64, i64, vp, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
@@ -406,3 +409,40 @@ def attention(qkv: torch.Tensor, H: int, Hkv: int, D: int = 128, rope: torch.Ten
                             out.stride(0) if L > 1 else out.shape[1], _ptr(ws), ws.numel(),
                             _stream(qkv)), "dq_attention")
     return out
+
+
+F32, F16, Q8_0, Q5_K, BF16 = 0, 1, 8, 13, 30  # the decoder's other GGUF types
+
+
+def row_bytes(type_: int, K: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t()
+    _check(lib.dq_row_bytes(type_, K, ctypes.byref(out)), "dq_row_bytes")
+    return out.value
+
+
+def embed_rows(type_: int, table: torch.Tensor, K: int, ids: torch.Tensor,
+               out: torch.Tensor | None = None, flags: torch.Tensor | None = None):
+    """Rows ids of a GGUF table (uint8, N rows of row_bytes(type, K)) decoded to
+    f32: returns (out [M, K], flags int32 [M], 1 where an id is out of range)."""
+    lib = load_library()
+    _need(table, torch.uint8, "table")
+    _need(ids, torch.int32, "ids")
+    if not table.is_contiguous() or not ids.is_contiguous():
+        raise ValueError("table and ids must be contiguous")
+    rb = row_bytes(type_, K)
+    N = table.numel() // rb
+    M = ids.numel()
+    dev = table.device
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=dev)
+    if flags is None:
+        flags = torch.empty(M, dtype=torch.int32, device=dev)
+    _need(out, torch.float32, "out")
+    _need(flags, torch.int32, "flags")
+    if out.dim() != 2 or out.shape[0] != M or out.shape[1] < K or out.stride(1) != 1:
+        raise ValueError("out must be [M, >= K] with unit column stride")
+    _check(lib.dq_embed_rows(type_, N, K, _ptr(table), _ptr(ids), M, _ptr(out),
+                             out.stride(0) if M > 1 else out.shape[1], _ptr(flags),
+                             _stream(table)), "dq_embed_rows")
+    return out, flags

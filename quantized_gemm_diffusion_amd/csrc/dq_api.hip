@@ -10,6 +10,7 @@
 #include "dq.h"
 #include "attention.h"
 #include "dq_internal.h"
+#include "embed.h"
 #include "row_stats.h"
 
 namespace {
@@ -370,6 +371,36 @@ int dq_attention(int64_t L, int64_t H, int64_t Hkv, int64_t D, const float *qkv,
   return launched(dq::launch_attention(L, H, Hkv, qkv, ldqkv, rope, rope_mode,
                                        static_cast<uint8_t *>(ws), out, ldo, stream),
                   "dq_attention");
+}
+
+int dq_row_bytes(int type, int64_t K, size_t *bytes) {
+  if (type != 0 && type != 1 && type != 8 && type != 12 && type != 13 && type != 14 &&
+      type != 30)
+    return fail(DQ_EUNSUPPORTED, "GGUF type %d is not decoded (0, 1, 8, 12, 13, 14, 30 are)",
+                type);
+  if (K <= 0 || K % 256 || K > ((int64_t)1 << 24))
+    return fail(DQ_EINVAL, "K = %lld must be a positive multiple of 256", (long long)K);
+  if (!bytes) return fail(DQ_EINVAL, "bytes is NULL");
+  *bytes = (size_t)dq::embed_row_bytes(type, K);
+  return ok();
+}
+
+int dq_embed_rows(int type, int64_t N, int64_t K, const void *table, const int32_t *ids,
+                  int64_t M, float *out, int64_t ldo, int32_t *flags, hipStream_t stream) {
+  size_t rb = 0;
+  if (int s = dq_row_bytes(type, K, &rb)) return s;
+  if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
+  if (M < 0 || M > kMaxRows) return fail(DQ_EINVAL, "M = %lld out of range", (long long)M);
+  if (ldo < K) return fail(DQ_EINVAL, "ldo = %lld < K = %lld", (long long)ldo, (long long)K);
+  // one wave per (row, 256 values), four to a workgroup, numbered in 32 bits
+  if (M * (K / 256) / 4 >= (int64_t)UINT32_MAX) return fail(DQ_EINVAL, "M x K too large");
+  if (M == 0) return ok();
+  if (!table || !ids || !out) return fail(DQ_EINVAL, "NULL pointer argument");
+  if (!aligned(table, 16) || !aligned(ids, 4) || !aligned(out, 4) || (flags && !aligned(flags, 4)))
+    return fail(DQ_EINVAL, "table must be 16-byte aligned, ids, out and flags 4-byte");
+  return launched(dq::launch_embed_rows(type, N, K, static_cast<const uint8_t *>(table), ids, M,
+                                        out, ldo, flags, stream),
+                  "dq_embed_rows");
 }
 
 int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const void *qa,

@@ -125,3 +125,49 @@ def qkv_rows(rng: np.random.Generator, L: int, H: int, Hkv: int, D: int,
              scale: float = 1.0) -> np.ndarray:
     """L x (H + 2 Hkv) D float32 rows [Q | K | V] ~ N(0, scale^2)."""
     return (rng.standard_normal((L, (H + 2 * Hkv) * D)) * scale).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# Tables of the decoder's other GGUF types (embedding rows), raw bytes        #
+# --------------------------------------------------------------------------- #
+F32, F16, Q8_0, Q5_K, BF16 = 0, 1, 8, 13, 30
+
+
+def q5k_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-3) -> np.ndarray:
+    """N x K as raw Q5_K blocks, uint8 [N, K/256, 176]: d, dmin as in Q4_K, then
+    the 12 scale bytes, 32 fifth-bit bytes and 128 nibble bytes uniform."""
+    nb = K // QK
+    out = np.empty((N, nb, 176), np.uint8)
+    out[..., 0:2] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 2:4] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 4:176] = _bytes(rng, (N, nb, 172))
+    return out
+
+
+def q8_0_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-2) -> np.ndarray:
+    """N x K as raw Q8_0 blocks, uint8 [N, K/32, 34]: d as fp16(|N(0,1)| d_scale),
+    then 32 uniform int8 codes."""
+    nb = K // 32
+    out = np.empty((N, nb, 34), np.uint8)
+    out[..., 0:2] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 2:34] = _bytes(rng, (N, nb, 32))
+    return out
+
+
+def float_table(rng: np.random.Generator, type_: int, N: int, K: int) -> np.ndarray:
+    """N x K N(0,1) values as raw F32, F16 or BF16 bytes (BF16: the top half of
+    each binary32 pattern), uint8 [N, bytes per row]."""
+    x = rng.standard_normal((N, K)).astype(np.float32)
+    if type_ == F32:
+        return x.view(np.uint8).reshape(N, 4 * K)
+    if type_ == F16:
+        return x.astype(np.float16).view(np.uint8).reshape(N, 2 * K)
+    return (x.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8).reshape(N, 2 * K)
+
+
+def table(rng: np.random.Generator, type_: int, N: int, K: int) -> np.ndarray:
+    """A random N x K table of any decoded GGUF type, as raw bytes [N, row bytes]."""
+    gen = {Q4_K: q4k_weights, Q6_K: q6k_weights, Q5_K: q5k_weights, Q8_0: q8_0_weights}
+    if type_ in gen:
+        return gen[type_](rng, N, K).reshape(N, -1)
+    return float_table(rng, type_, N, K)

@@ -180,3 +180,16 @@ def test_attention_host_checks(lib):
     assert call(ws=None) == dq.DQ_EWORKSPACE
     assert call(ws=264) == dq.DQ_EINVAL              # workspace not 16-byte aligned
     assert call(L=0) == dq.DQ_OK                     # empty canvas: nothing to do
+
+
+def test_embed_rows_host_checks(lib):
+    for t, K, b in ((0, 512, 2048), (1, 512, 1024), (30, 512, 1024), (8, 512, 544),
+                    (12, 4096, 2304), (13, 4096, 2816), (14, 4096, 3360)):
+        assert dq.row_bytes(t, K) == b
+    out = ctypes.c_size_t()
+    assert lib.dq_row_bytes(2, 256, ctypes.byref(out)) == dq.DQ_EUNSUPPORTED   # Q4_0: not decoded
+    assert lib.dq_row_bytes(8, 288, ctypes.byref(out)) == dq.DQ_EINVAL        # not 256-aligned
+    assert lib.dq_embed_rows(12, 10, 4096, 256, 256, 4, 256, 4095, None, None) == dq.DQ_EINVAL
+    assert lib.dq_embed_rows(12, 10, 4096, 264, 256, 4, 256, 4096, None, None) == dq.DQ_EINVAL
+    assert lib.dq_embed_rows(12, 10, 4096, None, 256, 4, 256, 4096, None, None) == dq.DQ_EINVAL
+    assert lib.dq_embed_rows(12, 10, 4096, None, None, 0, None, 4096, None, None) == dq.DQ_OK
