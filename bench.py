@@ -246,6 +246,7 @@ def main():
         run_calls(sp)
         sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws, reps=0)
         attention_shapes(lib, dq, torch, stream, sp, up, reps=0)
+        embedding_rows(lib, torch, stream, sp, up, reps=0)
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -278,6 +279,8 @@ def main():
     log("output projection feeding the samplers:", json.dumps(sampler))
     attn = attention_shapes(lib, dq, torch, stream, sp, up)
     log("canvas attention:", json.dumps(attn))
+    emb = embedding_rows(lib, torch, stream, sp, up)
+    log("embedding rows:", json.dumps(emb))
 
     # ------------------------------------------ the step as one HIP graph
     # The step's launches are captured once and replayed: the host then
@@ -362,6 +365,7 @@ def main():
         "kernels_isolated": kernels,
         "sampler_output_projection": sampler,
         "attention": attn,
+        "embedding_rows": emb,
         "step_timing": f"HIP graph replay of the step's {len(calls)} launches",
         "device": torch.cuda.get_device_properties(dev).name,
     }
@@ -474,6 +478,37 @@ def attention_shapes(lib, dq, torch, stream, sp, up, reps=20):
                      "TFLOPs": round(flops / us / 1e6, 2),
                      "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     return res
+
+
+def embedding_rows(lib, torch, stream, sp, up, reps=20):
+    """The canvas's embedding rows: 160 token ids into the LLaDA-8B token table
+    (126,464 x 4096 Q4_K, 291 MB, as stored in the GGUF file), decoded to f32 (not
+    part of the timed step).  HIP events around `reps` calls; algorithmic bytes are
+    the selected rows' blocks, the ids and the f32 output."""
+    rng = np.random.default_rng(synth.seed(5, 0, 0))
+    table = up(synth.q4k_weights(rng, V, K).reshape(-1))
+    ids = up(rng.integers(0, V, L).astype(np.int32))
+    out = torch.empty((L, K), dtype=torch.float32, device=table.device)
+    flags = torch.empty(L, dtype=torch.int32, device=table.device)
+    args = (Q4_K, V, K, table.data_ptr(), ids.data_ptr(), L, out.data_ptr(), K, flags.data_ptr(),
+            sp)
+    for _ in range(3 if reps else 1):
+        if lib.dq_embed_rows(*args):
+            raise RuntimeError(lib.dq_last_error().decode())
+    torch.cuda.synchronize()
+    if not reps:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        lib.dq_embed_rows(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / reps
+    nbytes = L * (K // 256) * BLOCK[Q4_K] + L * 4 + L * K * 4
+    return {"rows": L, "table": f"{V}x{K} Q4_K", "us": round(us, 2),
+            "algorithmic_MB": round(nbytes / 1e6, 3), "GB_s": round(nbytes / us / 1e3, 1),
+            "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):
