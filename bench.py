@@ -275,11 +275,12 @@ def main():
                    "GB_s": round(v[3] / (v[1] * 1e-3) / 1e9, 1)}
                for k, v in per_kind.items()}
     log("per-kind (isolated launches):", json.dumps(kernels))
-    sampler = sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws)
+    sampler = sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws,
+                               cpu=not args.no_cpu_baseline)
     log("output projection feeding the samplers:", json.dumps(sampler))
-    attn = attention_shapes(lib, dq, torch, stream, sp, up)
+    attn = attention_shapes(lib, dq, torch, stream, sp, up, cpu=not args.no_cpu_baseline)
     log("canvas attention:", json.dumps(attn))
-    emb = embedding_rows(lib, torch, stream, sp, up)
+    emb = embedding_rows(lib, torch, stream, sp, up, cpu=not args.no_cpu_baseline)
     log("embedding rows:", json.dumps(emb))
 
     # ------------------------------------------ the step as one HIP graph
@@ -377,7 +378,15 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws, reps=20):
+def _oracle_seconds(fn):
+    """Wall time of one call of an oracle function (its C code runs single-threaded)."""
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits, ws, reps=20,
+                     cpu=False):
     # reps = 0: one call of each, untimed (the counter runs)
     """The step's output projection as the samplers consume it (not part of the
     timed step, whose projection stores the logits): per requested row the greedy
@@ -437,10 +446,18 @@ def sampler_variants(lib, dq, torch, stream, sp, out_packed, canvas, idx, logits
     torch.cuda.synchronize()
     if not (torch.equal(token, tok_u) and torch.equal(stats[:, 0], st_u[:, 0])):
         raise RuntimeError("fused and unfused sampler statistics differ")
+    if cpu:
+        # the oracle's statistics step on seeded logits of the same shape (its
+        # projection is timed in cpu_baseline)
+        import oracle
+        y = np.random.default_rng(7).standard_normal((ROWS, V)) * 64.0
+        out["cpu_oracle_stats_us"] = round(1e6 * _oracle_seconds(
+            lambda: oracle.logits_stats(y, 1.0 / 64)), 1)
+        out["cpu_oracle_cores"] = 1
     return out
 
 
-def attention_shapes(lib, dq, torch, stream, sp, up, reps=20):
+def attention_shapes(lib, dq, torch, stream, sp, up, reps=20, cpu=False):
     """Bidirectional attention over the LLaDA-8B (L = 160, 32 heads, NORM RoPE) and
     Dream-7B (L = 512, 28 query heads over 4 kv heads, NEOX RoPE) canvases, on
     seeded Q/K/V rows: not part of the timed step (whose O projection reads a
@@ -477,17 +494,30 @@ def attention_shapes(lib, dq, torch, stream, sp, up, reps=20):
                      "algorithmic_MB": round(nbytes / 1e6, 2), "GB_s": round(nbytes / us / 1e3, 1),
                      "TFLOPs": round(flops / us / 1e6, 2),
                      "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        if cpu:
+            # the oracle on one kv head and its query heads, scaled to all of them
+            import oracle
+            G = H // Hkv
+            q_np = synth.qkv_rows(np.random.default_rng(synth.seed(6, 0, mode)), Ln, H, Hkv, D)
+            sub = np.concatenate([q_np[:, :G * D], q_np[:, H * D:(H + 1) * D],
+                                  q_np[:, (H + Hkv) * D:(H + Hkv + 1) * D]], axis=1)
+            tab_np = synth.rope_table(Ln, D, cfg["rope_theta"])
+            sec = _oracle_seconds(lambda: oracle.attention(sub, G, 1, D, tab_np, mode))
+            res[name]["cpu_oracle_us"] = round(1e6 * sec * Hkv, 1)
+            res[name]["cpu_oracle_sample"] = f"1 of {Hkv} kv heads ({G} query heads), x{Hkv}"
+            res[name]["cpu_oracle_cores"] = 1
     return res
 
 
-def embedding_rows(lib, torch, stream, sp, up, reps=20):
+def embedding_rows(lib, torch, stream, sp, up, reps=20, cpu=False):
     """The canvas's embedding rows: 160 token ids into the LLaDA-8B token table
     (126,464 x 4096 Q4_K, 291 MB, as stored in the GGUF file), decoded to f32 (not
     part of the timed step).  HIP events around `reps` calls; algorithmic bytes are
     the selected rows' blocks, the ids and the f32 output."""
     rng = np.random.default_rng(synth.seed(5, 0, 0))
-    table = up(synth.q4k_weights(rng, V, K).reshape(-1))
-    ids = up(rng.integers(0, V, L).astype(np.int32))
+    table_np = synth.q4k_weights(rng, V, K).reshape(V, -1)
+    ids_np = rng.integers(0, V, L).astype(np.int32)
+    table, ids = up(table_np.reshape(-1)), up(ids_np)
     out = torch.empty((L, K), dtype=torch.float32, device=table.device)
     flags = torch.empty(L, dtype=torch.int32, device=table.device)
     args = (Q4_K, V, K, table.data_ptr(), ids.data_ptr(), L, out.data_ptr(), K, flags.data_ptr(),
@@ -506,9 +536,15 @@ def embedding_rows(lib, torch, stream, sp, up, reps=20):
     torch.cuda.synchronize()
     us = 1e3 * e0.elapsed_time(e1) / reps
     nbytes = L * (K // 256) * BLOCK[Q4_K] + L * 4 + L * K * 4
-    return {"rows": L, "table": f"{V}x{K} Q4_K", "us": round(us, 2),
-            "algorithmic_MB": round(nbytes / 1e6, 3), "GB_s": round(nbytes / us / 1e3, 1),
-            "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    res = {"rows": L, "table": f"{V}x{K} Q4_K", "us": round(us, 2),
+           "algorithmic_MB": round(nbytes / 1e6, 3), "GB_s": round(nbytes / us / 1e3, 1),
+           "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    if cpu:
+        import oracle
+        res["cpu_oracle_us"] = round(1e6 * _oracle_seconds(
+            lambda: oracle.embed_rows(Q4_K, table_np, K, ids_np)), 1)
+        res["cpu_oracle_cores"] = 1
+    return res
 
 
 def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):
