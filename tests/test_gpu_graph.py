@@ -64,3 +64,56 @@ def test_graph_replays_match_eager(dq):
         # eager work of the program's own between replays
         dq.qgemm(dq.Q4_K, dq.quantize_act(canvas), p4, N)
         torch.cuda.synchronize()
+
+
+def test_graph_replays_of_the_next_rows(dq):
+    """The fused producers, the sampler statistics, canvas attention and the
+    embedding rows captured together; every replay equals the eager result."""
+    L, K, F, V, M = 64, 512, 768, 20000, 6
+    H, Hkv, D = 4, 2, 128
+    rng = np.random.default_rng(31)
+    x = _t(synth.activations(rng, L, K))
+    gamma = _t((1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32))
+    gu = _t(synth.activations(rng, L, 2 * F))
+    idx = _t(np.array([3, 60, 3, 17, 0, 41], np.int32))
+    Wv = synth.q6k_weights(np.random.default_rng(32), V, K)
+    pv = dq.repack_weights(dq.Q6_K, V, K, _t(Wv.reshape(-1)))
+    qkv = _t(synth.qkv_rows(rng, L, H, Hkv, D))
+    tab = _t(synth.rope_table(L, D, 10000.0))
+    table = _t(synth.q5k_weights(np.random.default_rng(33), 50, K).reshape(-1))
+    ids = _t(np.array([7, 0, 49, 7], np.int32))
+
+    a1 = torch.empty(dq.act_size(L, K), dtype=torch.uint8, device=DEV)
+    a2 = torch.empty(dq.act_size(L, F), dtype=torch.uint8, device=DEV)
+    tok = torch.empty(M, dtype=torch.int32, device=DEV)
+    st = torch.empty((M, 4), device=DEV)
+    wss = torch.empty(dq.qgemm_rows_sample_workspace(M, V, K), dtype=torch.uint8, device=DEV)
+    att = torch.empty((L, H * D), device=DEV)
+    wsa = torch.empty(dq.attention_workspace(L, H, Hkv, D), dtype=torch.uint8, device=DEV)
+    emb = torch.empty((ids.numel(), K), device=DEV)
+    fl = torch.empty(ids.numel(), dtype=torch.int32, device=DEV)
+
+    def step():
+        dq.rmsnorm_quantize_act(x, gamma, 1e-5, out=a1)
+        dq.swiglu_quantize_act(gu, F, out=a2)
+        dq.qgemm_rows_sample(dq.Q6_K, x, idx, pv, V, 0.25, token=tok, stats=st, ws=wss)
+        dq.attention(qkv, H, Hkv, D, tab, dq.ROPE_NEOX, out=att, ws=wsa)
+        dq.embed_rows(dq.Q5_K, table, K, ids, out=emb, flags=fl)
+
+    outs = (a1, a2, tok, st, att, emb, fl)
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        for t in outs:
+            t.zero_() if t.dtype in (torch.uint8, torch.int32) else t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, eager):
+            assert torch.equal(got, want), f"replay {i} differs from the eager result"
+        dq.attention(qkv, H, Hkv, D, tab, dq.ROPE_NORM)  # the program's own eager work
+        torch.cuda.synchronize()
