@@ -61,9 +61,35 @@ __device__ inline void rope_pair(float a, float b, float c, float s, float &ra, 
 // slot 8g + 4t + i holds key 16t + 4g + i.
 __device__ inline int slot_key(int j) { return 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3); }
 
+// Workgroups are dealt to the 8 XCDs in turn, and each XCD has its own L2:
+// number the workgroups of one kv head 8 apart (while whole groups of 8 kv
+// heads remain) so that they run on one XCD and fetch that head's images into
+// one L2.
+// With fewer than 8 kv heads (dividing 8), each kv head's workgroups go to
+// 8 / nkv XCDs instead (all 8 stay busy).
+__device__ inline void place_kv(int id, int nkv, int per, int &kv, int &item) {
+  constexpr int XCDS = 8;
+  if (nkv < XCDS && XCDS % nkv == 0 && per % (XCDS / nkv) == 0) {
+    const int slot = id / XCDS, xcd = id - slot * XCDS;
+    kv = xcd % nkv;
+    item = slot * (XCDS / nkv) + xcd / nkv;
+    return;
+  }
+  const int full = nkv / XCDS * XCDS;
+  if (id < full * per) {
+    const int slot = id / XCDS, xcd = id - slot * XCDS;
+    kv = slot / per * XCDS + xcd;
+    item = slot % per;
+  } else {
+    const int t = id - full * per;
+    kv = full + t / per;
+    item = t % per;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Pack: image (hk, b) of kv head hk and block b is 1280 16-byte chunks, one per
-// thread of workgroups 5 (hk * nblk + b) .. + 4:
+// thread of the 5 workgroups of items 5b .. 5b + 4 of kv head hk:
 //   chunks 0 .. 543     K rows: row k = c / 17; chunk c % 17 of the row (16:
 //                       the pad) holds d = 8 (c % 17) .. + 7
 //   chunks 544 .. 1183  V^T rows: row d = c' / 5; chunk c' % 5 (4: the pad)
@@ -77,10 +103,12 @@ __global__ __launch_bounds__(256) void attention_pack_kernel(int L, int H, int H
                                                              const float *__restrict__ rope,
                                                              uint8_t *__restrict__ img) {
   const int nblk = (L + KB - 1) / KB;
-  const int im = blockIdx.x / 5;  // image hk * nblk + b
-  const int hk = im / nblk, b = im - hk * nblk;
+  int hk, item;  // the kv head's workgroups on the XCD its attention workgroups use
+  place_kv(blockIdx.x, Hkv, nblk * 5, hk, item);
+  const int b = item / 5;
+  const int im = hk * nblk + b;  // image hk * nblk + b
   const int kcol = (H + hk) * AD, vcol = (H + Hkv + hk) * AD;
-  const int c = threadIdx.x + 256 * (blockIdx.x - 5 * im);
+  const int c = threadIdx.x + 256 * (item - 5 * b);
   _Float16 hv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) hv[e] = (_Float16)0.0f;
@@ -221,9 +249,11 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(int L, int H, int Hk
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, g = lane >> 4;
   const int qblocks = (L + 16 * QW - 1) / (16 * QW);
-  const int h = blockIdx.x / qblocks;
-  const int q0 = (blockIdx.x - h * qblocks) * 16 * QW + 16 * wave;
-  const int hk = h / (H / Hkv);
+  const int G = H / Hkv;
+  int hk, item;  // kv head, and (query head in its group, query block)
+  place_kv(blockIdx.x, Hkv, G * qblocks, hk, item);
+  const int h = hk * G + item / qblocks;
+  const int q0 = (item % qblocks) * 16 * QW + 16 * wave;
   const int nblk = (L + KB - 1) / KB;
 
   // the kv head's images, block b at b * IMG_BYTES (blocks past the last
