@@ -49,17 +49,133 @@ static_assert(K_BYTES + VT_BYTES <= IMG_BYTES, "block image");
 constexpr int ring_slots(int) { return 4; }
 
 // RoPE of one pair (a, b) by (c, s): a' = fma(a, c, -(b*s)), b' = fma(b, c, a*s),
-// every step rounded in binary32 (no further contraction).
+// every step rounded in binary32.  The empty asm pins each result as a binary32
+// value in a register: otherwise the compiler may fuse an fma with the
+// following conversion to f16 (v_fma_mix*_f16), which rounds once, straight to
+// f16, instead of to binary32 and then to f16.
 __device__ inline void rope_pair(float a, float b, float c, float s, float &ra, float &rb) {
-  const float bs = __fmul_rn(b, s);
-  const float as = __fmul_rn(a, s);
-  ra = __fmaf_rn(a, c, -bs);
-  rb = __fmaf_rn(b, c, as);
+  float bs = __fmul_rn(b, s);
+  float as = __fmul_rn(a, s);
+  asm volatile("" : "+v"(bs), "+v"(as));
+  float x = __fmaf_rn(a, c, -bs);
+  float y = __fmaf_rn(b, c, as);
+  asm volatile("" : "+v"(x), "+v"(y));
+  ra = x;
+  rb = y;
 }
 
 // The key held at contraction slot j (0..31) of a block in the second product:
 // slot 8g + 4t + i holds key 16t + 4g + i.
 __device__ inline int slot_key(int j) { return 16 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3); }
+
+// This lane's Q^T operand (d = 32c + 8g + e, e = 0..7) of one query: the row
+// (128 f32) rotated in registers and rounded to f16; rrow is the query's
+// RoPE table row (64 x (cos, sin)).
+template <int MODE>
+__device__ inline void load_q(const float *__restrict__ row, const float *__restrict__ rrow, int g,
+                              f16x8 (&qf)[4]) {
+  float x[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 lo = *reinterpret_cast<const float4 *>(row + 32 * c + 8 * g);
+    const float4 hi = *reinterpret_cast<const float4 *>(row + 32 * c + 8 * g + 4);
+    x[c][0] = lo.x, x[c][1] = lo.y, x[c][2] = lo.z, x[c][3] = lo.w;
+    x[c][4] = hi.x, x[c][5] = hi.y, x[c][6] = hi.z, x[c][7] = hi.w;
+  }
+  if (MODE == 1) {  // NORM: pairs (2i, 2i+1), i = 16c + 4g + e/2
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int i = 16 * c + 4 * g + e / 2;
+        const float2 cs = *reinterpret_cast<const float2 *>(rrow + 2 * i);
+        rope_pair(x[c][e], x[c][e + 1], cs.x, cs.y, x[c][e], x[c][e + 1]);
+      }
+  } else if (MODE == 2) {  // NEOX: pairs (i, i + 64): chunk c with chunk c + 2
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 32 * c + 8 * g + e;
+        const float2 cs = *reinterpret_cast<const float2 *>(rrow + 2 * i);
+        rope_pair(x[c][e], x[c + 2][e], cs.x, cs.y, x[c][e], x[c + 2][e]);
+      }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[c][e] = (_Float16)x[c][e];
+}
+
+// One block of 32 keys (K image kl, V^T image vt; keys kb0 .. kb0 + 31, those
+// past L masked) into this wave's online softmax state (m, lsum) and O^T.
+__device__ inline void attend_block(const _Float16 *kl, const _Float16 *vt, const f16x8 (&qf)[4],
+                                    int kb0, int L, int col, int g, float &m, float &lsum,
+                                    f32x4 (&o)[8]) {
+  // log2(e) / sqrt(128): scores go straight to exp2
+  const float sc = 1.4426950408889634f * 0.08838834764831845f;
+  // S^T: lane holds query col, keys 16t + 4g + e
+  f32x4 s[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    s[t] = f32x4{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x8 ka = *reinterpret_cast<const f16x8 *>(kl + (16 * t + col) * K_LD + 32 * c + 8 * g);
+      s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[c], s[t], 0, 0, 0);
+    }
+  }
+  float bm = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = s[t][e] * sc;
+      if (kb0 + 16 * t + 4 * g + e >= L) v = -INFINITY;
+      s[t][e] = v;
+      bm = fmaxf(bm, v);
+    }
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float mn = fmaxf(m, bm);
+  const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block
+  m = mn;
+  f16x8 pf;
+  float ps = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __builtin_amdgcn_exp2f(s[t][e] - mn);
+      ps += p;
+      pf[4 * t + e] = (_Float16)p;
+    }
+  lsum = lsum * alpha + ps;
+  // O^T += V^T P^T
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    o[dt] *= alpha;
+    const f16x8 va = *reinterpret_cast<const f16x8 *>(vt + (16 * dt + col) * VT_LD + 8 * g);
+    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, o[dt], 0, 0, 0);
+  }
+}
+
+// The 4 lanes of a query hold partial sums over their keys; store O = O^T / lsum.
+__device__ inline void store_out(float lsum, const f32x4 (&o)[8], float *orow, int out_vec) {
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const f32x4 v = o[dt] * inv;
+    if (out_vec) {
+      *reinterpret_cast<f32x4 *>(orow + 16 * dt) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) orow[16 * dt + e] = v[e];
+    }
+  }
+}
 
 // Workgroups are dealt to the 8 XCDs in turn, and each XCD has its own L2:
 // number the workgroups of one kv head 8 apart (while whole groups of 8 kv
@@ -242,7 +358,8 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(int L, int H, int Hk
                                                             int out_vec) {
   constexpr int LPW = IMG_BYTES / 1024 / QW;  // loads per wave per block
   constexpr int RING = ring_slots(QW);
-  static_assert(RING * LPW < 64, "loads in flight");
+  // the first RING - 1 copies, then Q's 8 + 16 loads (rows and RoPE table)
+  static_assert((RING - 1) * LPW + 24 < 64, "loads in flight");
   static_assert(RING * IMG_BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[RING * IMG_BYTES];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -265,53 +382,21 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(int L, int H, int Hk
     dma_share<QW>(dimg, ring + slot * IMG_BYTES, blk * IMG_BYTES, wave, lane);
   };
 
+#pragma unroll
+  for (int s = 0; s < RING - 1; ++s) issue(s, s);
+
   // this lane's query (rows past L repeat the last one; they are not stored)
   const int q = q0 + col < L ? q0 + col : L - 1;
   // Q^T operand: d = 32c + 8g + e (e = 0..7), rotated in registers
   f16x8 qf[4];
-  {
-    const float *row = qkv + (int64_t)q * ldqkv + h * AD;
-    float x[4][8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 lo = *reinterpret_cast<const float4 *>(row + 32 * c + 8 * g);
-      const float4 hi = *reinterpret_cast<const float4 *>(row + 32 * c + 8 * g + 4);
-      x[c][0] = lo.x, x[c][1] = lo.y, x[c][2] = lo.z, x[c][3] = lo.w;
-      x[c][4] = hi.x, x[c][5] = hi.y, x[c][6] = hi.z, x[c][7] = hi.w;
-    }
-    if (MODE == 1) {  // NORM: pairs (2i, 2i+1), i = 16c + 4g + e/2
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int i = 16 * c + 4 * g + e / 2;
-          const float2 cs = *reinterpret_cast<const float2 *>(rope + ((int64_t)q * 64 + i) * 2);
-          rope_pair(x[c][e], x[c][e + 1], cs.x, cs.y, x[c][e], x[c][e + 1]);
-        }
-    } else if (MODE == 2) {  // NEOX: pairs (i, i + 64): chunk c with chunk c + 2
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 32 * c + 8 * g + e;
-          const float2 cs = *reinterpret_cast<const float2 *>(rope + ((int64_t)q * 64 + i) * 2);
-          rope_pair(x[c][e], x[c + 2][e], cs.x, cs.y, x[c][e], x[c + 2][e]);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][e] = (_Float16)x[c][e];
-  }
+  load_q<MODE>(qkv + (int64_t)q * ldqkv + h * AD, MODE ? rope + (int64_t)q * 128 : rope, g, qf);
 
-  // Q's loads are done before the block copies start, so that this wave never
-  // has more than RING * LPW loads in flight
+  // the last slot's copy once Q is in registers (the copies of the first
+  // RING - 1 blocks were issued before Q's loads, so both latencies overlap
+  // and at most (RING - 1) * LPW + 24 loads are ever in flight)
   wait_vm<0>();
-#pragma unroll
-  for (int s = 0; s < RING; ++s) issue(s, s);
+  issue(RING - 1, RING - 1);
 
-  // log2(e) / sqrt(128): scores go straight to exp2
-  const float sc = 1.4426950408889634f * 0.08838834764831845f;
   float m = -INFINITY, lsum = 0.0f;
   f32x4 o[8];
 #pragma unroll
@@ -327,71 +412,10 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(int L, int H, int Hk
     const uint8_t *buf = lds + (b % RING) * IMG_BYTES;
     const _Float16 *kl = reinterpret_cast<const _Float16 *>(buf);
     const _Float16 *vt = reinterpret_cast<const _Float16 *>(buf + K_BYTES);
-    // S^T: lane holds query col, keys 16t + 4g + i
-    f32x4 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x4{};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f16x8 ka = *reinterpret_cast<const f16x8 *>(kl + (16 * t + col) * K_LD + 32 * c + 8 * g);
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[c], s[t], 0, 0, 0);
-      }
-    }
-    // online softmax over the block
-    const int kb0 = b * KB;
-    float bm = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = s[t][e] * sc;
-        if (kb0 + 16 * t + 4 * g + e >= L) v = -INFINITY;
-        s[t][e] = v;
-        bm = fmaxf(bm, v);
-      }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block
-    m = mn;
-    f16x8 pf;
-    float ps = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[t][e] - mn);
-        ps += p;
-        pf[4 * t + e] = (_Float16)p;
-      }
-    lsum = lsum * alpha + ps;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt] *= alpha;
-      const f16x8 va = *reinterpret_cast<const f16x8 *>(vt + (16 * dt + col) * VT_LD + 8 * g);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pf, o[dt], 0, 0, 0);
-    }
+    attend_block(kl, vt, qf, b * KB, L, col, g, m, lsum, o);
   }
   wait_vm<0>();  // no LDS write may land after the workgroup ends
-
-  // the 4 lanes of a query hold partial sums over their keys
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (q0 + col >= L) return;
-  const float inv = 1.0f / lsum;
-  float *orow = out + (int64_t)(q0 + col) * ldo + h * AD + 4 * g;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const f32x4 v = o[dt] * inv;
-    if (out_vec) {
-      *reinterpret_cast<f32x4 *>(orow + 16 * dt) = v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) orow[16 * dt + e] = v[e];
-    }
-  }
+  if (q0 + col < L) store_out(lsum, o, out + (int64_t)(q0 + col) * ldo + h * AD + 4 * g, out_vec);
 }
 
 template <int MODE>

@@ -13,8 +13,10 @@ ATT_TOL = 1e-3 leaves a factor 2 over their sum.
 Shapes: LLaDA-8B (L = 160, 32 heads, NORM RoPE, theta 5e5) and Dream-7B
 (L = 512, 28 query heads over 4 kv heads, NEOX RoPE, theta 1e6) canvases; a
 single position; a block and one key; ragged L with strided input and output
-rows, no RoPE; an unaligned output (element stores); peaked scores; every
-workgroup shape (groups of 1, 3, 8, 16 and 32 query heads per kv head).
+rows, no RoPE; an unaligned output (element stores); peaked scores (where a
+binary16 rounding difference in a rotated element shows); every workgroup
+numbering (groups of 1, 3, 4, 8, 16 and 32 query heads per kv head, and 1, 2,
+3, 4, 8, 32, 64 kv heads).
 """
 import numpy as np
 import pytest
@@ -103,6 +105,9 @@ def test_attention_peaked_scores(dq):
     (40, 32, 2),     # groups of 16: 16 heads x 1 query tile
     (45, 64, 2),     # groups of 32: two workgroups per group
     (60, 8, 8),      # no sharing, 4 query tiles: the 4-tile shape
+    (200, 8, 4),     # groups of 2 over a longer canvas
+    (256, 4, 1),     # 8 whole key blocks, one kv head for all
+    (257, 4, 4),     # one key into a ninth block
 ])
 def test_attention_workgroup_shapes(dq, L, H, Hkv):
     _run(dq, L, H, Hkv, oracle.ROPE_NEOX, seed=6 + H)
