@@ -428,8 +428,10 @@ hipError_t launch_mode(int64_t L, int64_t H, int64_t Hkv, const float *qkv, int6
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_vec = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ldo % 4 == 0);
-  // 32 queries per workgroup; 64 once that still gives a workgroup per CU
-  if (H * ((L + 63) / 64) >= 256) {
+  // 32 queries per workgroup; 64 once that still gives a workgroup to half the
+  // CUs (measured: Dream-7B's 224 four-wave workgroups beat its 448 two-wave
+  // ones by 6%, LLaDA-8B's 96 would lose to its 160)
+  if (H * ((L + 63) / 64) >= 128) {
     hipLaunchKernelGGL((attention_kernel<MODE, 4>), dim3((unsigned)(H * ((L + 63) / 64))),
                        dim3(256), 0, stream, (int)L, (int)H, (int)Hkv, qkv, ldqkv, rope, img, out,
                        ldo, out_vec);
