@@ -872,31 +872,49 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
 }
 
 // Compiled variants, indexed by the number of 16-row m-blocks per workgroup:
-// two n-tiles per wave, and as many activation slabs (3 for Q4_K, 2 for the
-// larger Q6_K tiles) as keep the workgroups' LDS within the CU's 160 KB.
-// WAVES = 8 (one workgroup per CU) splits the reduction twice as finely as
-// WAVES = 4 (two workgroups per CU) over the same tile grid.
-template <int TYPE, int MB, int WAVES>
+// two n-tiles per wave, and as many activation slabs (3 for Q4_K at 4 waves,
+// else 2) as keep the workgroups' LDS within the CU's 160 KB; a third slab
+// measured no faster at 8 waves or for Q6_K.  WAVES = 8 (one workgroup per
+// CU) splits the reduction twice as finely as WAVES = 4 (two workgroups per
+// CU) over the same tile grid.  One Q4_K
+// variant takes three n-tiles per wave (five m-blocks, two slabs, four waves):
+// every activation fragment read then feeds three tiles, and its cross-wave
+// sums (60 KB) still leave room for two workgroups per CU.
+template <int TYPE, int MB, int WAVES, int NT = 2>
 struct ShapeOf {
-  using type = Shape<MB, 2, TYPE == 14 ? 2 : 3, WAVES, WAVES == 8 ? 1 : 2>;
+  using type = Shape<MB, NT, (TYPE == 14 || NT == 3 || WAVES == 8) ? 2 : 3, WAVES, WAVES == 8 ? 1 : 2>;
 };
 constexpr int MB_SET[] = {8, 5, 4, 3, 2, 1};
-constexpr int NT_ALL = 2;  // n-tiles per wave in every compiled shape
+constexpr int NT_STATS = 2;  // n-tiles per wave of the sampler-state launches (mode 3)
 
 struct Pick {
-  int mb, waves;
+  int mb, waves, nt;
 };
+
+constexpr int64_t CUS = 256;
+
+// Fraction of workgroup slots used over a launch of wgs workgroups with
+// per_cu workgroups resident per CU.
+inline double fill(int64_t wgs, int64_t per_cu) {
+  const int64_t slots = CUS * per_cu;
+  const int64_t rounds = (wgs + slots - 1) / slots;
+  return (double)wgs / (double)(rounds * slots);
+}
 
 // Prefer the largest MB (weight digits are built once per MB steps) with at
 // most one padded m-block per m-chunk that gives at least one wave per SIMD
-// (1024 waves at 4 waves per workgroup).  Use 8 waves per workgroup only for
-// long reductions (each wave still gets 6 or more super-blocks, so its
-// pipeline fill and the deeper cross-wave sum stay small) and when that fills
-// the CUs in whole rounds better than 4 (one 8-wave or two 4-wave workgroups
-// per CU).
-inline Pick pick_shape(int64_t M, int64_t N, int64_t nb) {
+// (1024 waves at 4 waves per workgroup).  For Q4_K with MB = 5, take three
+// n-tiles per wave when that fills the workgroup slots at least as well and
+// still makes a full round of two workgroups per CU (LLaDA-8B's stacked
+// Q/K/V and gate/up at L = 160: 512 and 1024 workgroups instead of 768 and
+// 1536; measured 8-11% faster on MI355X).  Use 8 waves per workgroup when
+// the reduction has at least 16 super-blocks (each wave still gets 2 or
+// more) and that fills the CUs in whole rounds better than 4 (one 8-wave or
+// two 4-wave workgroups per CU).
+inline Pick pick_shape(int type, int mode, int64_t M, int64_t N, int64_t nb) {
   const int64_t mblocks = (M + MBLK - 1) / MBLK;
-  const int64_t tiles = ((N + TILE_N - 1) / TILE_N + NT_ALL - 1) / NT_ALL;
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  const int64_t tiles = (ntiles + 1) / 2;
   int mb = 1;
   int64_t best_waves = -1;
   for (int cand : MB_SET) {
@@ -913,23 +931,24 @@ inline Pick pick_shape(int64_t M, int64_t N, int64_t nb) {
       mb = cand;
     }
   }
-  const int64_t wgs = tiles * ((mblocks + mb - 1) / mb);
-  constexpr int64_t CUS = 256;
-  // fraction of workgroup slots used over the whole launch, per wave count
-  auto fill = [&](int64_t per_cu) {
-    const int64_t slots = CUS * per_cu;
-    const int64_t rounds = (wgs + slots - 1) / slots;
-    return (double)wgs / (double)(rounds * slots);
-  };
-  const bool eight = nb >= 48 && fill(1) > fill(2) + 0.05;
-  return Pick{mb, eight ? 8 : 4};
+  const int64_t chunks = (mblocks + mb - 1) / mb;
+  const int64_t wgs = tiles * chunks;
+  if (type == 12 && mode != 3 && mb == 5) {
+    const int64_t wgs3 = (ntiles + 2) / 3 * chunks;
+    if (wgs3 >= 2 * CUS && fill(wgs3, 2) >= fill(wgs, 2)) return Pick{5, 4, 3};
+  }
+  const bool eight = nb >= 16 && fill(wgs, 1) > fill(wgs, 2) + 0.05;
+  return Pick{mb, eight ? 8 : 4, 2};
 }
 
 template <int TYPE>
 hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
                        const uint8_t *packed, float *y, int64_t ldy, const Extra &x,
                        hipStream_t stream) {
-  const Pick pk = pick_shape(M, N, nb);
+  const Pick pk = pick_shape(TYPE, mode, M, N, nb);
+  if (TYPE == 12 && pk.nt == 3)
+    return launch2<TYPE, typename ShapeOf<TYPE, 5, 4, 3>::type>(mode, M, N, nb, qa, packed, y,
+                                                                ldy, x, stream);
 #define DQ_MB(X)                                                                               \
   case X:                                                                                      \
     if (pk.waves == 8)                                                                         \
@@ -981,7 +1000,7 @@ int qgemm_stats_parts(int64_t M, int64_t N, int64_t K) {
   const int nb = (int)(K / QK);
   if (use_narrow(3, M, N, nb, 0)) return (int)narrow_grid(N);
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
-  return (int)((ntiles + NT_ALL - 1) / NT_ALL);
+  return (int)((ntiles + NT_STATS - 1) / NT_STATS);
 }
 
 hipError_t launch_qgemm_stats(int type, int64_t M, int64_t N, int64_t K, const uint8_t *qa,

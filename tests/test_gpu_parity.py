@@ -305,6 +305,8 @@ def test_abi_errors_on_gpu(dq):
     (oracle.Q4_K, 96, 8192, 1280),    # 5 super-blocks over 4 waves
     (oracle.Q6_K, 64, 8192, 256),     # a single super-block
     (oracle.Q4_K, 150, 8224, 768),    # a ragged last 16-row block
+    (oracle.Q4_K, 160, 12270, 512),   # three n-tiles per wave, ragged last column group
+    (oracle.Q4_K, 160, 4096, 4096),   # 8 waves over 16 super-blocks
 ])
 def test_qgemm_every_m_tiling(dq, type_, M, N, K):
     W = _weights(type_, N, K, 300 + M, full_scales=True)
@@ -317,9 +319,11 @@ def test_qgemm_every_m_tiling(dq, type_, M, N, K):
     _check_tol(y.cpu().numpy(), yr, T, f"type {type_} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("type_,M", [(oracle.Q4_K, 160), (oracle.Q6_K, 128), (oracle.Q4_K, 64)])
-def test_superblock_sums_bit_exact_multi_tile(dq, type_, M):
-    N, K = 8192, 512
+@pytest.mark.parametrize("type_,M,N", [(oracle.Q4_K, 160, 8192), (oracle.Q6_K, 128, 8192),
+                                       (oracle.Q4_K, 64, 8192),
+                                       (oracle.Q4_K, 160, 12270)])  # three n-tiles per wave
+def test_superblock_sums_bit_exact_multi_tile(dq, type_, M, N):
+    K = 512
     W = _weights(type_, N, K, 500 + M, full_scales=True)
     x = synth.activations(np.random.default_rng(600 + M), M, K)
     xq, xd, xb = oracle.quantize_act(x)
