@@ -253,6 +253,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"counters mode: one step, then a {COPY_MIB} MiB copy")
+        # the kind of each call of a step, in launch order (the rows call makes two
+        # launches: the gather-quantize, then the GEMM), so that per-dispatch
+        # counters can be attributed to the step's GEMM shapes
+        print(json.dumps({"counted_steps": args.warmup + 1,
+                          "step_call_kinds": [c[2] for c in calls]}), flush=True)
         return
     per_kind = {}
     evs = []

@@ -326,6 +326,10 @@ __device__ inline void step_mfma(const Frag &f, const Digits &D, StepOut &o) {
 template <bool Q6>
 __device__ inline void step_fold(const StepOut &o, const f32x4 &x4, float dw, float dmw,
                                  f32x4 &acc) {
+  // d and dmin enter as binary32 registers: folded back into mixed-precision
+  // FMAs (v_fma_mix_f32) they would cost a wait state before each
+  // accumulation that reads the result
+  asm("" : "+v"(dw), "+v"(dmw));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s_int = Q6 ? o.rl[i] + o.rh[i] * 256 : o.rl[i] + o.rh[i] * 8;
@@ -532,16 +536,20 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
         Frag f;
         read_frag<Q6>(ring + slot_use * SLAB, frag, col, kq, f);
         slot_use = slot_use + 1 == R ? 0 : slot_use + 1;
+        // tile j's MFMAs are issued before tile j - 1 is folded, so the fold
+        // reads results that are already complete while the matrix core
+        // works on the next tile
+        StepOut out[NT];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          StepOut cur;
-          step_mfma<Q6>(f, Dg[j], cur);
+          step_mfma<Q6>(f, Dg[j], out[j]);
           if (DEBUG)
-            step_debug<Q6>(cur, (int64_t)(mb0 + t) * MBLK, kq, (nt0 + j) * TILE_N + col, M,
+            step_debug<Q6>(out[j], (int64_t)(mb0 + t) * MBLK, kq, (nt0 + j) * TILE_N + col, M,
                            nt0 + j < ntiles ? N : 0, nb, b, dbg_S, dbg_Mn);
-          else
-            step_fold<Q6>(cur, f.x4, Dg[j].dw, Dg[j].dmw, acc[t][j]);
+          else if (j > 0)
+            step_fold<Q6>(out[j - 1], f.x4, Dg[j - 1].dw, Dg[j - 1].dmw, acc[t][j - 1]);
         }
+        if (!DEBUG) step_fold<Q6>(out[NT - 1], f.x4, Dg[NT - 1].dw, Dg[NT - 1].dmw, acc[t][NT - 1]);
       }
     }
     wait_vm<0>();  // no LDS write may land after this point
