@@ -220,12 +220,30 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(int64_t M, int64_t
 // RMSNorm then quantize: one workgroup of 16 waves per (padded) row.  The
 // sum of squares is formed in the order the producer defines: thread j < 256
 // keeps a partial over the 4-value groups j, j + 256, ... in increasing order
-// (one square and one addition at a time), then a halving tree in LDS, at
-// h = 128, 64, ..., 1: partial[j] += partial[j + h].  mean = ss / K, rinv =
-// 1 / sqrt(mean + eps), y = (x * rinv) * gamma; wave w then quantizes blocks
-// w, w + 16, ... of y (one block per wave at K = 4096).
+// (one square and one addition at a time), then a halving tree at h = 128,
+// 64, ..., 1: partial[j] += partial[j + h].  mean = ss / K, rinv = 1 /
+// sqrt(mean + eps), y = (x * rinv) * gamma; wave w then quantizes blocks w,
+// w + 16, ... of y (one block per wave at K = 4096).
+//
+// Latency: a thread's groups are loaded four at a time before any is added,
+// the tree's levels h <= 32 run inside wave 0 on lane shuffles (the same
+// additions of the same operands, without a workgroup barrier each), and
+// every wave loads its first block of x and gamma at the start, while the
+// sum of squares is still being formed.
 constexpr int NORM_PARTS = 256;    // partial sums of the defined order
 constexpr int NORM_THREADS = 1024;
+constexpr int NORM_WAVES = NORM_THREADS / 64;
+
+template <bool VEC>
+__device__ inline void load4(const float *p, float (&v)[4]) {
+  if (VEC) {
+    const f32x4 t = *reinterpret_cast<const f32x4 *>(p);
+    v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = p[i];
+  }
+}
 
 template <bool VEC>
 __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
@@ -240,45 +258,66 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
   const bool valid = m < M;  // uniform across the workgroup
   const float *xr = x + (valid ? m : 0) * ldx;
 
+  // this wave's first block (it does not depend on the norm)
+  float xv[4] = {0.f, 0.f, 0.f, 0.f}, gv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid && wave < nb) {
+    load4<VEC>(xr + (int64_t)wave * QK + 4 * lane, xv);
+    load4<VEC>(gamma + (int64_t)wave * QK + 4 * lane, gv);
+  }
+
   float rinv = 0.0f;
   if (valid) {
     if (tid < NORM_PARTS) {
       float acc = 0.0f;
-      for (int64_t g = tid; 4 * g < K; g += NORM_PARTS) {
-        float v[4];
-        if (VEC) {
-          const f32x4 t = *reinterpret_cast<const f32x4 *>(xr + 4 * g);
-          v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
-        } else {
+      for (int64_t g0 = tid; 4 * g0 < K; g0 += 4 * NORM_PARTS) {
+        float v[4][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = xr[4 * g + i];
+        for (int u = 0; u < 4; ++u) {
+          const int64_t g = g0 + (int64_t)u * NORM_PARTS;
+          if (4 * g < K) load4<VEC>(xr + 4 * g, v[u]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float sq = v[i] * v[i];
-          acc = acc + sq;
+        for (int u = 0; u < 4; ++u) {
+          if (4 * (g0 + (int64_t)u * NORM_PARTS) < K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sq = v[u][i] * v[u][i];
+              acc = acc + sq;
+            }
+          }
         }
       }
       part[tid] = acc;
     }
     __syncthreads();
-    for (int h = NORM_PARTS / 2; h >= 1; h >>= 1) {
-      if (tid < h) part[tid] = part[tid] + part[tid + h];
-      __syncthreads();
+    if (tid < 128) part[tid] = part[tid] + part[tid + 128];
+    __syncthreads();
+    if (wave == 0) {
+      float p = part[lane] + part[lane + 64];  // h = 64: lane j < 64 holds partial[j]
+#pragma unroll
+      for (int h = 32; h >= 1; h >>= 1) {
+        const float o = __shfl_down(p, h, 64);  // partial[j + h] for lanes j < h
+        p = p + o;
+      }
+      if (lane == 0) part[0] = p;
     }
+    __syncthreads();
     const float mean = part[0] / (float)K;
     rinv = 1.0f / __builtin_sqrtf(mean + eps);
   }
 
-  for (int b = wave; b < nb; b += NORM_THREADS / 64) {
+  for (int b = wave; b < nb; b += NORM_WAVES) {
     uint8_t *rec = qa + ((int64_t)b * (Mpad / ACT_ROWS) + mb) * ACT_RECORD;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (valid) {
-      const int64_t k0 = (int64_t)b * QK + 4 * lane;
+      if (b != wave) {
+        load4<VEC>(xr + (int64_t)b * QK + 4 * lane, xv);
+        load4<VEC>(gamma + (int64_t)b * QK + 4 * lane, gv);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float t = xr[k0 + i] * rinv;
-        v[i] = t * gamma[k0 + i];
+        const float t = xv[i] * rinv;
+        v[i] = t * gv[i];
       }
     }
     quantize_lane(v, rec, r, lane);
@@ -334,7 +373,8 @@ hipError_t launch_rmsnorm_quantize(int64_t M, int64_t K, const float *x, int64_t
                                    hipStream_t stream) {
   const int nb = (int)(K / QK);
   const int64_t Mpad = (M + ACT_ROWS - 1) / ACT_ROWS * ACT_ROWS;
-  const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldx % 4 == 0);
+  const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldx % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(gamma) % 16 == 0);
   dim3 grid((unsigned)Mpad), block(NORM_THREADS);
   if (vec)
     hipLaunchKernelGGL((rmsnorm_quantize_kernel<true>), grid, block, 0, stream, M, Mpad, nb, x,
