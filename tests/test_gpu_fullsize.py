@@ -72,6 +72,40 @@ def test_llada_projection_full_size(dq, name):
     _sampled_check(type_, xq, xd, W, y, 7, f"LLaDA {name}")
 
 
+def test_llada_stacked_gate_up_full_size(dq):
+    # the benchmark's dominant GEMM: gate and up of a layer stacked into one 24576 x 4096 Q4_K
+    # matrix, its input made by the RMSNorm producer
+    projs = {p[0]: p for p in synth.llada_layer(0)}
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    W = np.concatenate([synth.weights(np.random.default_rng(synth.seed(1, 0, names.index(n))),
+                                      projs[n][1], projs[n][2], projs[n][3])
+                        for n in ("gate", "up")])
+    N, K = W.shape[0], projs["gate"][3]
+    M = synth.LLADA["L"]
+    x = synth.activations(np.random.default_rng(1100), M, K)
+    gamma = (1.0 + 0.1 * np.random.default_rng(1101).standard_normal(K)).astype(np.float32)
+    xq, xd, xb = oracle.rmsnorm_quantize_act(x, gamma, 1e-5)
+    act = dq.rmsnorm_quantize_act(_t(x), _t(gamma), 1e-5)
+    q, d, b, padding_ok = act_layout.unpack(act.buf.cpu().numpy(), M, K)
+    assert padding_ok and np.array_equal(q, xq) and np.array_equal(b, xb)
+    assert np.array_equal(d.view(np.uint32), xd.view(np.uint32))
+    packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(oracle.Q4_K, act, packed, N).cpu().numpy()
+    _sampled_check(oracle.Q4_K, xq, xd, W, y, 11, "LLaDA stacked gate/up")
+
+
+def test_llada_q4k_down_full_size(dq):
+    # even layers: down is Q4_K (8-wave workgroups over 48 super-blocks)
+    _, type_, N, K = {p[0]: p for p in synth.llada_layer(0)}["down"]
+    assert type_ == oracle.Q4_K
+    M = synth.LLADA["L"]
+    W = synth.weights(np.random.default_rng(synth.seed(1, 0, 6)), type_, N, K)
+    _, (xq, xd, xb), act = _run_set(dq, None, M, K, 1200 + K)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(type_, act, packed, N).cpu().numpy()
+    _sampled_check(type_, xq, xd, W, y, 12, "LLaDA down (Q4_K)")
+
+
 @pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
 def test_dream_projection_full_size(dq, name):
     proj = {p[0]: p for p in synth.dream_layer()}[name]
