@@ -884,10 +884,10 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
 // else 2) as keep the workgroups' LDS within the CU's 160 KB; a third slab
 // measured no faster at 8 waves or for Q6_K.  WAVES = 8 (one workgroup per
 // CU) splits the reduction twice as finely as WAVES = 4 (two workgroups per
-// CU) over the same tile grid.  One Q4_K
-// variant takes three n-tiles per wave (five m-blocks, two slabs, four waves):
-// every activation fragment read then feeds three tiles, and its cross-wave
-// sums (60 KB) still leave room for two workgroups per CU.
+// CU) over the same tile grid.  Two variants take three n-tiles per wave
+// (four waves, two slabs; five m-blocks for Q4_K, four for the larger Q6_K
+// tiles): every activation fragment read then feeds three tiles, and the
+// rings (68.6 KB and 81.5 KB) still leave room for two workgroups per CU.
 template <int TYPE, int MB, int WAVES, int NT = 2>
 struct ShapeOf {
   using type = Shape<MB, NT, (TYPE == 14 || NT == 3 || WAVES == 8) ? 2 : 3, WAVES, WAVES == 8 ? 1 : 2>;
@@ -911,14 +911,15 @@ inline double fill(int64_t wgs, int64_t per_cu) {
 
 // Prefer the largest MB (weight digits are built once per MB steps) with at
 // most one padded m-block per m-chunk that gives at least one wave per SIMD
-// (1024 waves at 4 waves per workgroup).  For Q4_K with MB = 5, take three
-// n-tiles per wave when that fills the workgroup slots at least as well and
-// still makes a full round of two workgroups per CU (LLaDA-8B's stacked
-// Q/K/V and gate/up at L = 160: 512 and 1024 workgroups instead of 768 and
-// 1536; measured 8-11% faster on MI355X).  Use 8 waves per workgroup when
-// the reduction has at least 16 super-blocks (each wave still gets 2 or
-// more) and that fills the CUs in whole rounds better than 4 (one 8-wave or
-// two 4-wave workgroups per CU).
+// (1024 waves at 4 waves per workgroup).  Take three n-tiles per wave (Q4_K
+// with MB = 5, Q6_K with MB = 4) when that makes at least a full round of two
+// workgroups per CU and fills the workgroup slots at least as well, or runs
+// four or more rounds (LLaDA-8B's stacked Q/K/V and gate/up at L = 160: 512
+// and 1024 workgroups instead of 768 and 1536, 8-11% faster on MI355X;
+// Dream-7B's logits on 64 gathered rows: 3168 workgroups, 8% faster).  Use
+// 8 waves per workgroup when the reduction has at least 16 super-blocks
+// (each wave still gets 2 or more) and that fills the CUs in whole rounds
+// better than 4 (one 8-wave or two 4-wave workgroups per CU).
 inline Pick pick_shape(int type, int mode, int64_t M, int64_t N, int64_t nb) {
   const int64_t mblocks = (M + MBLK - 1) / MBLK;
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
@@ -941,9 +942,10 @@ inline Pick pick_shape(int type, int mode, int64_t M, int64_t N, int64_t nb) {
   }
   const int64_t chunks = (mblocks + mb - 1) / mb;
   const int64_t wgs = tiles * chunks;
-  if (type == 12 && mode != 3 && mb == 5) {
+  if (mode != 3 && ((type == 12 && mb == 5) || (type == 14 && mb == 4))) {
     const int64_t wgs3 = (ntiles + 2) / 3 * chunks;
-    if (wgs3 >= 2 * CUS && fill(wgs3, 2) >= fill(wgs, 2)) return Pick{5, 4, 3};
+    if (wgs3 >= 2 * CUS && (fill(wgs3, 2) >= fill(wgs, 2) || wgs3 >= 8 * CUS))
+      return Pick{mb, 4, 3};
   }
   const bool eight = nb >= 16 && fill(wgs, 1) > fill(wgs, 2) + 0.05;
   return Pick{mb, eight ? 8 : 4, 2};
@@ -954,9 +956,11 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
                        const uint8_t *packed, float *y, int64_t ldy, const Extra &x,
                        hipStream_t stream) {
   const Pick pk = pick_shape(TYPE, mode, M, N, nb);
-  if (TYPE == 12 && pk.nt == 3)
-    return launch2<TYPE, typename ShapeOf<TYPE, 5, 4, 3>::type>(mode, M, N, nb, qa, packed, y,
-                                                                ldy, x, stream);
+  if (pk.nt == 3)
+    return TYPE == 12 ? launch2<TYPE, typename ShapeOf<TYPE, 5, 4, 3>::type>(
+                            mode, M, N, nb, qa, packed, y, ldy, x, stream)
+                      : launch2<TYPE, typename ShapeOf<TYPE, 4, 4, 3>::type>(
+                            mode, M, N, nb, qa, packed, y, ldy, x, stream);
 #define DQ_MB(X)                                                                               \
   case X:                                                                                      \
     if (pk.waves == 8)                                                                         \
