@@ -805,6 +805,167 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
   }
 }
 
+// Single-row Q6_K projection (M = 1, e.g. the logits of one committed
+// position).  With one row, 15 of the 16 rows of the MFMA's activation
+// operand would be padding; here they carry the row's 16 sub-blocks instead.
+// Operand row j holds the row's codes where k lies in sub-block j and zeros
+// elsewhere (the lane of row j and k-quarter kq has them in chunk j - 4kq),
+// so one int32 accumulation over the super-block's four chunks against the
+// raw 6-bit codes q (0..63, no digit split) leaves dot_j(q) = sum over
+// sub-block j of q * x in accumulator row j: every per-sub-block dot of the
+// super-block at once, for a quarter of the MFMAs and none of the digit
+// work.  The Q6_K offset enters as dot_j(q - 32) = dot_j(q) - 32 * xs_j (xs_j
+// the sum of the row's codes over sub-block j, formed once per launch), and
+// the lane of column n and k-quarter kq holds sub-blocks 4kq .. 4kq + 3 --
+// the four scale bytes its tile dword already carries -- so it forms
+// sum_j sc_j * dot_j(q - 32) over them in exact integers (|dot_j| < 2^18,
+// |sc_j * dot_j| < 2^25), scales it by d_x * d in binary32, and the four
+// k-quarters of a column are added by two lane exchanges in a fixed order.
+// Streaming, slots, waits and the cross-wave sum are those of the narrow
+// kernel above, with one float per column and wave.
+template <int S, bool VEC, bool STATS>
+__global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_row1_kernel(
+    int64_t N, int nb, const uint8_t *__restrict__ qa, const uint8_t *__restrict__ packed,
+    float *__restrict__ y, float beta, float4 *__restrict__ part, int npart) {
+  constexpr int TB = Q6K_TILE;
+  constexpr int WSLOT = wslot_bytes<true>();
+  constexpr int SET = NW_KB * WSLOT;
+  constexpr int DPS = NW_KB * dma_per_tile<true>();
+  constexpr int SC = STATS ? 0 : VEC ? 1 : 4;
+  static_assert(S >= 2 && (S - 1) * DPS + S * SC < 64, "pipeline shape");
+  constexpr int RED = 2 * NW_WAVES * 64 * 4;  // column sums per wave, double buffered
+  static_assert(RED + NW_WAVES * S * SET <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RED + NW_WAVES * S * SET];
+  float *red = reinterpret_cast<float *>(lds);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  const int nw = nb / NW_KB;
+  const int64_t G = gridDim.x;
+
+  // activation operands of super-blocks wave and wave + nw (one record each,
+  // one 16-row block of which only row 0 is real)
+  i32x4 act[NW_KB][4];
+  int xs32[NW_KB][4];  // 32 * xs_j for the lane's sub-blocks j = 4kq + t
+  float dx[NW_KB];
+  const int cs = col - 4 * kq;  // the chunk holding sub-block `col` in this lane's k-quarter
+#pragma unroll
+  for (int i = 0; i < NW_KB; ++i) {
+    const uint8_t *rec = qa + (int64_t)(wave + nw * i) * ACT_RECORD;  // row 0: unit u at 16 u
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(rec + 16 * (4 * kq + c));
+      act[i][c] = c == cs ? v : i32x4{};
+      int sum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum = __builtin_amdgcn_sdot4(v[e], 0x01010101, sum, false);
+      xs32[i][c] = 32 * sum;
+    }
+    dx[i] = *reinterpret_cast<const float *>(rec + ACT_DX_OFF);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  uint8_t *slots = lds + RED + wave * S * SET;
+  const uint32_t slots_a = (uint32_t)(uintptr_t)(lds_ptr_t)slots;
+  auto issue = [&](int64_t kk, int slot) {
+    int64_t nt = blockIdx.x + kk * G;
+    nt = nt < ntiles ? nt : ntiles - 1;
+    const i32x4 d = desc(packed + nt * nb * TB, (uint32_t)(nb * TB));
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i)
+      dma_tile<true>(d, slots_a + slot * SET + i * WSLOT, (wave + nw * i) * TB, lane);
+  };
+
+  // wave 0 stores: lanes 0..3 carry columns 4 * lane .. 4 * lane + 3 of the tile
+  const bool storer = wave == 0;
+  const int c0 = 4 * (lane & 3);
+  const i32x4 dy = STATS ? i32x4{} : desc(y, (uint32_t)(N * 4));
+  RowStat st = stat_empty();
+
+#pragma unroll
+  for (int p = 0; p < S; ++p) issue(p, p);
+
+  int slot = 0;
+  for (int64_t k = 0;; ++k) {
+    const int64_t nt = blockIdx.x + k * G;
+    if (nt >= ntiles) break;
+    if (SC > 0 && storer && k >= S)
+      wait_vm<(S - 1) * DPS + S * SC>();
+    else
+      wait_vm<(S - 1) * DPS>();
+    RawQ6 w[NW_KB];
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) read_w(slots + slot * SET + i * WSLOT, lane, col, kq, w[i]);
+    wait_lds();
+    issue(k + S, slot);
+    slot = slot + 1 == S ? 0 : slot + 1;
+
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) {
+      i32x4 dot = i32x4{};
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = 2 * r + h;
+          const uint32_t u = (uint32_t)w[i].qh[c];
+          const uint32_t w0 = (uint32_t)w[i].rec[r][2 * h], w1 = (uint32_t)w[i].rec[r][2 * h + 1];
+          const i32x4 q = {(int)((w0 & 0x0f0f0f0fu) | ((u << 4) & 0x30303030u)),
+                           (int)(((w0 >> 4) & 0x0f0f0f0fu) | ((u << 2) & 0x30303030u)),
+                           (int)((w1 & 0x0f0f0f0fu) | (u & 0x30303030u)),
+                           (int)(((w1 >> 4) & 0x0f0f0f0fu) | ((u >> 2) & 0x30303030u))};
+          dot = __builtin_amdgcn_mfma_i32_16x16x64_i8(act[i][c], q, dot, 0, 0, 0);
+        }
+      }
+      // accumulator element t: sub-block 4kq + t of column `col`
+      int sacc = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sc = (int)(int8_t)((w[i].sw >> (8 * t)) & 255u);
+        sacc += sc * (dot[t] - xs32[i][t]);
+      }
+      const float dd = dx[i] * half_bits_to_float(w[i].d);
+      acc += dd * (float)sacc;
+    }
+    // the column's four k-quarters, in a fixed order
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+
+    float *buf = red + (int)(k & 1) * NW_WAVES * 64;
+    if (lane < 16) buf[wave * 64 + lane] = acc;
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (storer) {
+      const float *src = buf + c0;
+      f32x4 v = *reinterpret_cast<const f32x4 *>(src);
+      for (int ww = 1; ww < nw; ++ww) v += *reinterpret_cast<const f32x4 *>(src + ww * 64);
+      const int64_t n0 = nt * TILE_N + c0;
+      const bool ok = lane < 4;
+      const uint32_t off = (uint32_t)(n0 * 4);
+      if (STATS) {
+        const int64_t left = ok ? N - n0 : 0;
+        const float z[4] = {beta * v[0], beta * v[1], beta * v[2], beta * v[3]};
+        stat_push4(st, z, (int)n0, left < 0 ? 0 : left > 4 ? 4 : (int)left);
+      } else if (VEC) {
+        bstore4(dy, ok && n0 < N ? off : NW_DROP, v);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bstore1(dy, ok && n0 + c < N ? off + 4 * c : NW_DROP, v[c]);
+      }
+    }
+  }
+  wait_vm<0>();  // no LDS write may land after the workgroup ends
+  if (STATS && storer) {
+    st = stat_merge(st, stat_shfl_xor(st, 1));
+    st = stat_merge(st, stat_shfl_xor(st, 2));
+    if (lane == 0) part[blockIdx.x] = stat_pack(st);
+  }
+}
+
 // Narrow launches: one workgroup per CU (fewer if there are fewer tiles).
 constexpr int NW_CUS = 256;
 
@@ -833,6 +994,23 @@ hipError_t launch_narrow(int64_t M, int64_t N, int nb, const uint8_t *qa, const 
   else
     hipLaunchKernelGGL((qgemm_narrow_kernel<TYPE, MB, S, false, false>), grid, block, 0, stream, m,
                        N, nb, qa, packed, y, ldy, 0.0f, nullptr, 0);
+  return hipGetLastError();
+}
+
+// Single-row Q6_K launches (the same grid and eligibility as the narrow kernel).
+hipError_t launch_row1(int64_t N, int nb, const uint8_t *qa, const uint8_t *packed, float *y,
+                       float beta, float4 *part, hipStream_t stream) {
+  dim3 grid((unsigned)narrow_grid(N)), block(64 * (nb / NW_KB));
+  const bool vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (N % 4 == 0);
+  if (part)
+    hipLaunchKernelGGL((qgemm_row1_kernel<2, true, true>), grid, block, 0, stream, N, nb, qa,
+                       packed, nullptr, beta, part, (int)grid.x);
+  else if (vec)
+    hipLaunchKernelGGL((qgemm_row1_kernel<2, true, false>), grid, block, 0, stream, N, nb, qa,
+                       packed, y, 0.0f, nullptr, 0);
+  else
+    hipLaunchKernelGGL((qgemm_row1_kernel<2, false, false>), grid, block, 0, stream, N, nb, qa,
+                       packed, y, 0.0f, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -992,6 +1170,7 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
   const int nb = (int)(K / QK);
   if (use_narrow(mode, M, N, nb, ldy)) {
     const bool two = M > MBLK;
+    if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, y, 0.0f, nullptr, stream);
     if (type == 12)
       return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
                  : launch_narrow<12, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
@@ -1021,6 +1200,7 @@ hipError_t launch_qgemm_stats(int type, int64_t M, int64_t N, int64_t K, const u
   const int nb = (int)(K / QK);
   if (use_narrow(3, M, N, nb, 0)) {
     const bool two = M > MBLK;
+    if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, nullptr, beta, part, stream);
     if (type == 12)
       return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream)
                  : launch_narrow<12, 1>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream);

@@ -349,6 +349,8 @@ def test_superblock_sums_bit_exact_multi_tile(dq, type_, M, N):
     (oracle.Q4_K, 32, 16384, 4096, 3),   # row stride N + 3 (element stores)
     (oracle.Q6_K, 16, 32776, 2560, 0),   # 5 waves, many n-tiles per workgroup
     (oracle.Q4_K, 5, 16384, 4096, 0),    # one partial 16-row block, vector stores
+    (oracle.Q6_K, 1, 16390, 4096, 0),    # one row (sub-blocks as operand rows), element stores
+    (oracle.Q6_K, 1, 32768, 2560, 2),    # one row, 5 waves, vector stores
 ])
 def test_qgemm_narrow_m(dq, type_, M, N, K, pad):
     W = _weights(type_, N, K, 700 + M + K // 256, full_scales=True)
