@@ -966,6 +966,173 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_row1_kernel(
   }
 }
 
+// Q6_K projection of 2 to 4 rows (R = 1; the template also takes R = 2 for 8
+// rows), the same idea for more than one row.  In row group g (rows 4g ..
+// 4g + 3) operand row 4m + p holds row 4g + m's codes
+// where k lies in k-quarter p of the chunk and zeros elsewhere, so one MFMA
+// per chunk c separates the chunk's four sub-blocks: accumulator element i
+// of the lane of column n and k-quarter kq is the dot of row 4g + kq over
+// k-quarter i of chunk c, i.e. sub-block 4i + c.  Over the four chunks a
+// lane thus sees all 16 sub-blocks of its own row and forms S = sum_j sc_j *
+// dot_j in exact integers (|dot_j| < 2^16), the weight operand being q - 32
+// as a byte (no digit split); the rows need no exchange between lanes.
+// Streaming, slots and waits follow the narrow kernel; wave g < R stores row
+// group g, one element per lane and tile.
+template <int R, int S, bool STATS>
+__global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_rows4_kernel(
+    int M, int64_t N, int nb, const uint8_t *__restrict__ qa, const uint8_t *__restrict__ packed,
+    float *__restrict__ y, int64_t ldy, float beta, float4 *__restrict__ part, int npart) {
+  constexpr int TB = Q6K_TILE;
+  constexpr int WSLOT = wslot_bytes<true>();
+  constexpr int SET = NW_KB * WSLOT;
+  constexpr int DPS = NW_KB * dma_per_tile<true>();
+  constexpr int SC = STATS ? 0 : 1;
+  static_assert(R >= 1 && R <= 2, "at most 8 rows");
+  static_assert(S >= 2 && (S - 1) * DPS + S * SC < 64, "pipeline shape");
+  constexpr int RED = 2 * NW_WAVES * R * 64 * 4;  // per wave and row group, double buffered
+  static_assert(RED + NW_WAVES * S * SET <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RED + NW_WAVES * S * SET];
+  float *red = reinterpret_cast<float *>(lds);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  const int nw = nb / NW_KB;
+  const int64_t G = gridDim.x;
+
+  // operand rows: this lane supplies row 4g + col / 4 in k-quarter kq when
+  // col % 4 == kq, zeros otherwise; dx of the lane's output row 4g + kq
+  i32x4 act[NW_KB][R][4];
+  float dx[NW_KB][R];
+  const bool mine = (col & 3) == kq;
+#pragma unroll
+  for (int i = 0; i < NW_KB; ++i) {
+    const uint8_t *rec = qa + (int64_t)(wave + nw * i) * ACT_RECORD;  // one 16-row block
+#pragma unroll
+    for (int g = 0; g < R; ++g) {
+      const int r = 4 * g + (col >> 2);  // the operand row's row of the record
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(rec + r * QK + 16 * ((4 * kq + c) ^ r));
+        act[i][g][c] = mine ? v : i32x4{};
+      }
+      dx[i][g] = *reinterpret_cast<const float *>(rec + ACT_DX_OFF + 4 * (4 * g + kq));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  uint8_t *slots = lds + RED + wave * S * SET;
+  const uint32_t slots_a = (uint32_t)(uintptr_t)(lds_ptr_t)slots;
+  auto issue = [&](int64_t kk, int slot) {
+    int64_t nt = blockIdx.x + kk * G;
+    nt = nt < ntiles ? nt : ntiles - 1;
+    const i32x4 d = desc(packed + nt * nb * TB, (uint32_t)(nb * TB));
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i)
+      dma_tile<true>(d, slots_a + slot * SET + i * WSLOT, (wave + nw * i) * TB, lane);
+  };
+
+  // storing wave g: row 4g + kq, column `col` of each tile
+  const bool storer = wave < R;
+  const int row_st = 4 * (storer ? wave : 0) + kq;
+  const bool row_ok = row_st < M;
+  const i32x4 dy = STATS ? i32x4{} : desc(y, (uint32_t)(((int64_t)(M - 1) * ldy + N) * 4));
+  RowStat st = stat_empty();
+
+#pragma unroll
+  for (int p = 0; p < S; ++p) issue(p, p);
+
+  int slot = 0;
+  for (int64_t k = 0;; ++k) {
+    const int64_t nt = blockIdx.x + k * G;
+    if (nt >= ntiles) break;
+    if (SC > 0 && storer && k >= S)
+      wait_vm<(S - 1) * DPS + S * SC>();
+    else
+      wait_vm<(S - 1) * DPS>();
+    RawQ6 w[NW_KB];
+    uint32_t scw[NW_KB][4];  // scale dword of k-quarter i: byte c = sub-block 4i + c
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) {
+      const uint8_t *tile = slots + slot * SET + i * WSLOT;
+      read_w(tile, lane, col, kq, w[i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        scw[i][q] = *reinterpret_cast<const uint32_t *>(tile + Q6K_SC_OFF + (q * 16 + col) * 4);
+    }
+    wait_lds();
+    issue(k + S, slot);
+    slot = slot + 1 == S ? 0 : slot + 1;
+
+    float acc[R];
+#pragma unroll
+    for (int g = 0; g < R; ++g) acc[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) {
+      int sacc[R];
+#pragma unroll
+      for (int g = 0; g < R; ++g) sacc[g] = 0;
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = 2 * r2 + h;
+          const uint32_t u = (uint32_t)w[i].qh[c];
+          const uint32_t w0 = (uint32_t)w[i].rec[r2][2 * h], w1 = (uint32_t)w[i].rec[r2][2 * h + 1];
+          const uint32_t code[4] = {(w0 & 0x0f0f0f0fu) | ((u << 4) & 0x30303030u),
+                                    ((w0 >> 4) & 0x0f0f0f0fu) | ((u << 2) & 0x30303030u),
+                                    (w1 & 0x0f0f0f0fu) | (u & 0x30303030u),
+                                    ((w1 >> 4) & 0x0f0f0f0fu) | ((u >> 2) & 0x30303030u)};
+          // q - 32 as a two's-complement byte: (q + 128 - 32) with bit 7 flipped,
+          // no borrow between bytes
+          i32x4 qm;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) qm[t] = (int)(((code[t] | 0x80808080u) - 0x20202020u) ^ 0x80808080u);
+#pragma unroll
+          for (int g = 0; g < R; ++g) {
+            const i32x4 dot = __builtin_amdgcn_mfma_i32_16x16x64_i8(act[i][g][c], qm, i32x4{}, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int sc = (int)(int8_t)((scw[i][q] >> (8 * c)) & 255u);  // sub-block 4q + c
+              sacc[g] += sc * dot[q];
+            }
+          }
+        }
+      }
+      const float dw = half_bits_to_float(w[i].d);
+#pragma unroll
+      for (int g = 0; g < R; ++g) acc[g] += (dx[i][g] * dw) * (float)sacc[g];
+    }
+
+    float *buf = red + (int)(k & 1) * NW_WAVES * R * 64;
+#pragma unroll
+    for (int g = 0; g < R; ++g) buf[(wave * R + g) * 64 + lane] = acc[g];
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (storer) {
+      const float *src = buf + wave * 64 + lane;  // row group `wave` of wave 0
+      float v = src[0];
+      for (int ww = 1; ww < nw; ++ww) v += src[ww * R * 64];
+      const int64_t n = nt * TILE_N + col;
+      if (STATS) {
+        const float z[4] = {beta * v, 0.f, 0.f, 0.f};
+        stat_push4(st, z, (int)n, row_ok && n < N ? 1 : 0);
+      } else {
+        const uint32_t off = (uint32_t)(((int64_t)row_st * ldy + n) * 4);
+        bstore1(dy, row_ok && n < N ? off : NW_DROP, v);
+      }
+    }
+  }
+  wait_vm<0>();  // no LDS write may land after the workgroup ends
+  if (STATS && storer) {
+#pragma unroll
+    for (int x = 1; x < 16; x <<= 1) st = stat_merge(st, stat_shfl_xor(st, x));
+    if (col == 0 && row_ok) part[(int64_t)row_st * npart + blockIdx.x] = stat_pack(st);
+  }
+}
+
 // Narrow launches: one workgroup per CU (fewer if there are fewer tiles).
 constexpr int NW_CUS = 256;
 
@@ -1011,6 +1178,22 @@ hipError_t launch_row1(int64_t N, int nb, const uint8_t *qa, const uint8_t *pack
   else
     hipLaunchKernelGGL((qgemm_row1_kernel<2, false, false>), grid, block, 0, stream, N, nb, qa,
                        packed, y, 0.0f, nullptr, 0);
+  return hipGetLastError();
+}
+
+// Q6_K launches for 2 to 4 rows (the same grid and eligibility as the narrow
+// kernel).  One row group only: at 5 to 8 rows the two-group variant measured
+// no faster than the narrow kernel (both stream at about 5.3 TB/s there).
+hipError_t launch_rows4(int64_t M, int64_t N, int nb, const uint8_t *qa, const uint8_t *packed,
+                        float *y, int64_t ldy, float beta, float4 *part, hipStream_t stream) {
+  dim3 grid((unsigned)narrow_grid(N)), block(64 * (nb / NW_KB));
+  const int m = (int)M, np = (int)grid.x;
+  if (part)
+    hipLaunchKernelGGL((qgemm_rows4_kernel<1, 2, true>), grid, block, 0, stream, m, N, nb, qa,
+                       packed, nullptr, (int64_t)0, beta, part, np);
+  else
+    hipLaunchKernelGGL((qgemm_rows4_kernel<1, 2, false>), grid, block, 0, stream, m, N, nb, qa,
+                       packed, y, ldy, 0.0f, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1171,6 +1354,7 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
   if (use_narrow(mode, M, N, nb, ldy)) {
     const bool two = M > MBLK;
     if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, y, 0.0f, nullptr, stream);
+    if (type == 14 && M <= 4) return launch_rows4(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
     if (type == 12)
       return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
                  : launch_narrow<12, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
@@ -1201,6 +1385,8 @@ hipError_t launch_qgemm_stats(int type, int64_t M, int64_t N, int64_t K, const u
   if (use_narrow(3, M, N, nb, 0)) {
     const bool two = M > MBLK;
     if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, nullptr, beta, part, stream);
+    if (type == 14 && M <= 4)
+      return launch_rows4(M, N, nb, qa, packed, nullptr, 0, beta, part, stream);
     if (type == 12)
       return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream)
                  : launch_narrow<12, 1>(M, N, nb, qa, packed, nullptr, 0, beta, part, stream);

@@ -351,6 +351,10 @@ def test_superblock_sums_bit_exact_multi_tile(dq, type_, M, N):
     (oracle.Q4_K, 5, 16384, 4096, 0),    # one partial 16-row block, vector stores
     (oracle.Q6_K, 1, 16390, 4096, 0),    # one row (sub-blocks as operand rows), element stores
     (oracle.Q6_K, 1, 32768, 2560, 2),    # one row, 5 waves, vector stores
+    (oracle.Q6_K, 2, 16400, 4096, 0),    # 2 to 4 rows: k-quarters as operand rows
+    (oracle.Q6_K, 3, 16390, 2048, 3),    # 3 rows, row stride N + 3, ragged n-tile
+    (oracle.Q6_K, 4, 20000, 3584, 0),    # 4 rows, 7 waves
+    (oracle.Q6_K, 5, 16390, 2048, 3),    # 5 rows: back on the narrow kernel
 ])
 def test_qgemm_narrow_m(dq, type_, M, N, K, pad):
     W = _weights(type_, N, K, 700 + M + K // 256, full_scales=True)

@@ -135,6 +135,7 @@ def _check_against_reference(tok, st, y_ref, T, beta, what):
     (oracle.Q4_K, 37, 17, 1000, 768, 0.1),     # canvas kernel, Q4_K
     (oracle.Q6_K, 160, 32, 16400, 2048, 0.02),  # narrow kernel, 2 blocks of 16 rows
     (oracle.Q6_K, 160, 1, 16390, 2048, 1.0),   # narrow kernel, one row, ragged N
+    (oracle.Q6_K, 64, 4, 16390, 2048, 0.3),    # 2 to 4 rows, a duplicate
     (oracle.Q4_K, 64, 9, 16384, 2560, 0.05),   # narrow kernel, Q4_K, 5 waves
 ])
 def test_rows_sample_against_oracle(dq, type_, L, M, N, K, beta):
