@@ -1245,13 +1245,16 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
 // else 2) as keep the workgroups' LDS within the CU's 160 KB; a third slab
 // measured no faster at 8 waves or for Q6_K.  WAVES = 8 (one workgroup per
 // CU) splits the reduction twice as finely as WAVES = 4 (two workgroups per
-// CU) over the same tile grid.  Two variants take three n-tiles per wave
+// CU) over the same tile grid, and WAVES = 2 (four workgroups per CU, the
+// same 8 waves) splits it half as finely: each wave's pipeline is twice as
+// long and the cross-wave sum has two partials.  Two variants take three n-tiles per wave
 // (four waves, two slabs; five m-blocks for Q4_K, four for the larger Q6_K
 // tiles): every activation fragment read then feeds three tiles, and the
 // rings (68.6 KB and 81.5 KB) still leave room for two workgroups per CU.
 template <int TYPE, int MB, int WAVES, int NT = 2>
 struct ShapeOf {
-  using type = Shape<MB, NT, (TYPE == 14 || NT == 3 || WAVES == 8) ? 2 : 3, WAVES, WAVES == 8 ? 1 : 2>;
+  using type = Shape<MB, NT, (TYPE == 14 || NT == 3 || WAVES != 4) ? 2 : 3, WAVES,
+                     WAVES == 8 ? 1 : WAVES == 2 ? 4 : 2>;
 };
 constexpr int MB_SET[] = {8, 5, 4, 3, 2, 1};
 constexpr int NT_STATS = 2;  // n-tiles per wave of the sampler-state launches (mode 3)
@@ -1277,7 +1280,10 @@ inline double fill(int64_t wgs, int64_t per_cu) {
 // workgroups per CU and fills the workgroup slots at least as well, or runs
 // four or more rounds (LLaDA-8B's stacked Q/K/V and gate/up at L = 160: 512
 // and 1024 workgroups instead of 768 and 1536, 8-11% faster on MI355X;
-// Dream-7B's logits on 64 gathered rows: 3168 workgroups, 8% faster).  Use
+// Dream-7B's logits on 64 gathered rows: 3168 workgroups, 8% faster).  With
+// 1024 or more workgroups, the three-tile shapes and Q4_K at MB = 8 take
+// 2-wave workgroups, four per CU (LLaDA's gate/up 7% and Dream's gate/up 4%
+// faster; below 1024 workgroups four per CU cannot fill the CUs).  Use
 // 8 waves per workgroup when the reduction has at least 16 super-blocks
 // (each wave still gets 2 or more) and that fills the CUs in whole rounds
 // better than 4 (one 8-wave or two 4-wave workgroups per CU).
@@ -1303,13 +1309,20 @@ inline Pick pick_shape(int type, int mode, int64_t M, int64_t N, int64_t nb) {
   }
   const int64_t chunks = (mblocks + mb - 1) / mb;
   const int64_t wgs = tiles * chunks;
-  if (mode != 3 && ((type == 12 && mb == 5) || (type == 14 && mb == 4))) {
-    const int64_t wgs3 = (ntiles + 2) / 3 * chunks;
-    if (wgs3 >= 2 * CUS && (fill(wgs3, 2) >= fill(wgs, 2) || wgs3 >= 8 * CUS))
-      return Pick{mb, 4, 3};
-  }
-  const bool eight = nb >= 16 && fill(wgs, 1) > fill(wgs, 2) + 0.05;
-  return Pick{mb, eight ? 8 : 4, 2};
+  Pick pk{mb, 4, 2};
+  const int64_t wgs3 = (ntiles + 2) / 3 * chunks;
+  if (((type == 12 && mb == 5) || (type == 14 && mb == 4)) && wgs3 >= 2 * CUS &&
+      (fill(wgs3, 2) >= fill(wgs, 2) || wgs3 >= 8 * CUS))
+    pk = Pick{mb, wgs3 >= 4 * CUS ? 2 : 4, 3};
+  else if (type == 12 && mb == 8 && wgs >= 4 * CUS)
+    pk = Pick{8, 2, 2};
+  else if (nb >= 16 && fill(wgs, 1) > fill(wgs, 2) + 0.05)
+    pk = Pick{mb, 8, 2};
+  // The sampler-state launch keeps two tiles per wave (one state per row per
+  // 32-column group) but the same waves: each output element is then summed
+  // in the same order as the plain launch stores it, bit for bit.
+  if (mode == 3) pk.nt = 2;
+  return pk;
 }
 
 template <int TYPE>
@@ -1317,11 +1330,26 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
                        const uint8_t *packed, float *y, int64_t ldy, const Extra &x,
                        hipStream_t stream) {
   const Pick pk = pick_shape(TYPE, mode, M, N, nb);
-  if (pk.nt == 3)
-    return TYPE == 12 ? launch2<TYPE, typename ShapeOf<TYPE, 5, 4, 3>::type>(
-                            mode, M, N, nb, qa, packed, y, ldy, x, stream)
-                      : launch2<TYPE, typename ShapeOf<TYPE, 4, 4, 3>::type>(
-                            mode, M, N, nb, qa, packed, y, ldy, x, stream);
+  if (pk.nt == 3) {
+    constexpr int MB3 = TYPE == 12 ? 5 : 4;
+    if (pk.waves == 2)
+      return launch2<TYPE, typename ShapeOf<TYPE, MB3, 2, 3>::type>(mode, M, N, nb, qa, packed, y,
+                                                                    ldy, x, stream);
+    return launch2<TYPE, typename ShapeOf<TYPE, MB3, 4, 3>::type>(mode, M, N, nb, qa, packed, y,
+                                                                  ldy, x, stream);
+  }
+  if (pk.waves == 2) {  // (Q4_K, MB 5 or 8) or (Q6_K, MB 4), two tiles per wave
+    if constexpr (TYPE == 12) {
+      if (pk.mb == 8)
+        return launch2<TYPE, typename ShapeOf<TYPE, 8, 2>::type>(mode, M, N, nb, qa, packed, y,
+                                                                 ldy, x, stream);
+      return launch2<TYPE, typename ShapeOf<TYPE, 5, 2>::type>(mode, M, N, nb, qa, packed, y, ldy,
+                                                               x, stream);
+    } else {
+      return launch2<TYPE, typename ShapeOf<TYPE, 4, 2>::type>(mode, M, N, nb, qa, packed, y, ldy,
+                                                               x, stream);
+    }
+  }
 #define DQ_MB(X)                                                                               \
   case X:                                                                                      \
     if (pk.waves == 8)                                                                         \

@@ -308,6 +308,9 @@ def test_abi_errors_on_gpu(dq):
     (oracle.Q4_K, 160, 12270, 512),   # three n-tiles per wave, ragged last column group
     (oracle.Q4_K, 160, 4096, 4096),   # 8 waves over 16 super-blocks
     (oracle.Q6_K, 64, 24568, 512),    # Q6_K, three n-tiles per wave, ragged last n-tile
+    (oracle.Q4_K, 160, 24560, 512),   # three n-tiles, 2-wave workgroups (1024 of them)
+    (oracle.Q6_K, 64, 49144, 512),    # Q6_K, three n-tiles, 2-wave workgroups
+    (oracle.Q4_K, 512, 8192, 768),    # 8 m-blocks, 2-wave workgroups, 3 super-blocks over 2 waves
 ])
 def test_qgemm_every_m_tiling(dq, type_, M, N, K):
     W = _weights(type_, N, K, 300 + M, full_scales=True)
@@ -323,7 +326,9 @@ def test_qgemm_every_m_tiling(dq, type_, M, N, K):
 @pytest.mark.parametrize("type_,M,N", [(oracle.Q4_K, 160, 8192), (oracle.Q6_K, 128, 8192),
                                        (oracle.Q4_K, 64, 8192),
                                        (oracle.Q4_K, 160, 12270),   # three n-tiles per wave
-                                       (oracle.Q6_K, 64, 24568)])
+                                       (oracle.Q6_K, 64, 24568),
+                                       (oracle.Q4_K, 160, 24560),   # 2-wave workgroups
+                                       (oracle.Q4_K, 512, 8192)])
 def test_superblock_sums_bit_exact_multi_tile(dq, type_, M, N):
     K = 512
     W = _weights(type_, N, K, 500 + M, full_scales=True)
