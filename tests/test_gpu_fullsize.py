@@ -134,3 +134,34 @@ def test_logits_rows_full_size(dq, model, Ms):
         yn = y.cpu().numpy()
         gq, gd, _ = oracle.qgemm_rows_inputs(canvas, idx)
         _sampled_check(oracle.Q6_K, gq, gd, W, yn, 9 + M, f"{model} logits M={M}")
+
+
+def _random_shapes(count, seed):
+    """Seeded shapes spread over the launcher's regimes: narrow and few-row
+    kernels (M <= 32, 8 to 16 super-blocks, wide N), the canvas kernel with two
+    or three n-tiles per wave and 2-, 4- or 8-wave workgroups, ragged M and N."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(count):
+        type_ = oracle.Q4_K if rng.integers(2) == 0 else oracle.Q6_K
+        if i % 3 == 0:      # narrow / single-row / few-row: M <= 32, nb even in [8, 16]
+            M = int(rng.choice([1, 2, 3, 4, 7, 16, 23, 32]))
+            nb = int(rng.choice([8, 10, 12, 14, 16]))
+            N = int(rng.integers(16384, 40000))
+        else:               # canvas kernel
+            M = int(rng.integers(33, 600))
+            nb = int(rng.choice([1, 2, 3, 5, 14, 16, 20, 48]))
+            N = int(rng.integers(17, 30000))
+        shapes.append((type_, M, N, 256 * nb))
+    return shapes
+
+
+@pytest.mark.parametrize("type_,M,N,K", _random_shapes(12, 2024))
+def test_random_shapes_sampled(dq, type_, M, N, K):
+    W = synth.weights(np.random.default_rng(M * 7 + N), type_, N, K)
+    x = synth.activations(np.random.default_rng(M + N), M, K)
+    xq, xd, _ = oracle.quantize_act(x)
+    act = dq.quantize_act(_t(x))
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    y = dq.qgemm(type_, act, packed, N).cpu().numpy()
+    _sampled_check(type_, xq, xd, W, y, 13, f"type {type_} {M}x{N}x{K}")
