@@ -160,6 +160,7 @@ def test_rows_sample_against_oracle(dq, type_, L, M, N, K, beta):
     (oracle.Q6_K, 160, 32, 126464, 4096, 1.0 / 64),  # LLaDA output projection, 32 rows
     (oracle.Q6_K, 160, 8, 126464, 4096, 1.0),
     (oracle.Q6_K, 160, 1, 126464, 4096, 0.01),
+    (oracle.Q6_K, 160, 3, 126464, 4096, 0.5),        # 2 to 4 rows
     (oracle.Q6_K, 512, 64, 152064, 3584, 1.0 / 64),  # Dream output projection, 64 rows
 ])
 def test_rows_sample_matches_rows_logits_at_full_size(dq, type_, L, M, N, K, beta):
