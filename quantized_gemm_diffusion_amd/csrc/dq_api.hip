@@ -233,7 +233,12 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
   uint8_t *qa = w + rows_ws_flags(M);
   if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
   int32_t *flags = reinterpret_cast<int32_t *>(w);
-  hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
+  hipError_t e = hipSuccess;
+  if (dq::launch_rows_gather_row1(type, M, N, K, canvas, ldc, idx, L, flags,
+                                  static_cast<const uint8_t *>(packed), y, 0.0f, nullptr, stream,
+                                  e))
+    return launched(e, "dq_qgemm_rows (single-row gather + gemm)");
+  e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
   if (e != hipSuccess) return launched(e, "dq_qgemm_rows (gather-quantize)");
   return launched(dq::launch_qgemm(type, 1, M, N, K, qa, static_cast<const uint8_t *>(packed), y,
                                    ldy, nullptr, nullptr, stream),
@@ -322,10 +327,15 @@ int dq_qgemm_rows_sample(int type, int64_t L, int64_t M, int64_t N, int64_t K,
   int32_t *flags = reinterpret_cast<int32_t *>(w);
   float4 *part = reinterpret_cast<float4 *>(w + rows);
   const int npart = dq::qgemm_stats_parts(M, N, K);
-  hipError_t e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
-  if (e != hipSuccess) return launched(e, "dq_qgemm_rows_sample (gather-quantize)");
-  e = dq::launch_qgemm_stats(type, M, N, K, qa, static_cast<const uint8_t *>(packed), beta, part,
-                             npart, stream);
+  hipError_t e = hipSuccess;
+  if (!dq::launch_rows_gather_row1(type, M, N, K, canvas, ldc, idx, L, flags,
+                                   static_cast<const uint8_t *>(packed), nullptr, beta, part,
+                                   stream, e)) {
+    e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
+    if (e != hipSuccess) return launched(e, "dq_qgemm_rows_sample (gather-quantize)");
+    e = dq::launch_qgemm_stats(type, M, N, K, qa, static_cast<const uint8_t *>(packed), beta,
+                               part, npart, stream);
+  }
   if (e != hipSuccess) return launched(e, "dq_qgemm_rows_sample (gemm)");
   return launched(dq::launch_row_stats_finish(M, npart, part, token, stats, stream),
                   "dq_qgemm_rows_sample (finish)");

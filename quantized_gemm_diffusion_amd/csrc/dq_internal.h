@@ -61,6 +61,67 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------------------
+// The activation quantization rule of one 256-value block, shared by every
+// kernel that quantizes (so their codes agree bit for bit).  A wave holds the
+// block with lane l owning values 4l .. 4l+3.
+
+// Cross-lane moves inside a row of 16 lanes (DPP): quad permutations
+// [1,0,3,2] and [2,3,0,1], half-row mirror (lane i <-> 7-i of each 8) and
+// row mirror (lane i <-> 15-i).  Broadcasts of lane 15 / 31 into the next
+// row(s) finish a reduction over the wave in lane 63.
+constexpr int DPP_QUAD_1032 = 0xb1, DPP_QUAD_2301 = 0x4e;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// max |x| over the wave (max is exact in any order), the same in every lane
+__device__ inline float wave_max(float v) {
+  auto step = [](float a, int b) { return fmaxf(a, __builtin_bit_cast(float, b)); };
+  v = step(v, dpp<DPP_QUAD_1032>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_QUAD_2301>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_ROW_HALF_MIRROR>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_ROW_MIRROR>(__builtin_bit_cast(int, v)));
+  // lanes of rows 1 and 3 take the max with lane 15 of the row before, then
+  // rows 2 and 3 with lane 31: lane 63 holds the maximum of all 64 lanes
+  v = step(v, dpp<DPP_ROW_BCAST15, 0xa>(__builtin_bit_cast(int, v)));
+  v = step(v, dpp<DPP_ROW_BCAST31, 0xc>(__builtin_bit_cast(int, v)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// The block's max |x| (every lane of the wave takes part).
+__device__ inline float block_amax(const float (&v)[4]) {
+  return wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+}
+
+// The lane's 4 codes, packed in k order: inv = 127 / amax (one correctly
+// rounded division), q = clamp(rint(x * inv), -127, 127) (one multiply, ties
+// to even); all zero when amax is 0.  No step can be contracted.
+__device__ inline void quant4(const float (&v)[4], float amax, int (&c)[4]) {
+  c[0] = c[1] = c[2] = c[3] = 0;
+  if (amax != 0.0f) {
+    const float inv = 127.0f / amax;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float t = __builtin_rintf(v[i] * inv);
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      c[i] = (int)t;
+    }
+  }
+}
+
+__device__ inline uint32_t pack4(const int (&c)[4]) {
+  return (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) |
+         ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)(c[3] & 255) << 24);
+}
+
+// The block's activation scale d_x.
+__device__ inline float block_dx(float amax) { return amax != 0.0f ? amax / 127.0f : 0.0f; }
+
 // Launchers (each returns the hipError_t of its launch).
 // Quantize M rows (row m = x[m], or x[idx[m]] when idx is given) into the
 // record layout; err[m] flags an index outside [0, L).

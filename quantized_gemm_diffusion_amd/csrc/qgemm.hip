@@ -823,10 +823,23 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_narrow_kernel(
 // k-quarters of a column are added by two lane exchanges in a fixed order.
 // Streaming, slots, waits and the cross-wave sum are those of the narrow
 // kernel above, with one float per column and wave.
-template <int S, bool VEC, bool STATS>
+//
+// With GATHER the row is canvas row idx[0], read and quantized here (every
+// wave its own two blocks, by the quantization rule every quantizer shares)
+// instead of by a separate gather-quantize launch; flags[0] reports an index
+// outside [0, L) (the row is then taken as zeros).
+struct Gather {
+  const float *canvas = nullptr;
+  int64_t ldc = 0, L = 0;
+  const int32_t *idx = nullptr;
+  int32_t *flags = nullptr;
+  int vec = 0;  // rows 16-byte aligned
+};
+
+template <int S, bool VEC, bool STATS, bool GATHER>
 __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_row1_kernel(
     int64_t N, int nb, const uint8_t *__restrict__ qa, const uint8_t *__restrict__ packed,
-    float *__restrict__ y, float beta, float4 *__restrict__ part, int npart) {
+    float *__restrict__ y, float beta, float4 *__restrict__ part, int npart, Gather gx) {
   constexpr int TB = Q6K_TILE;
   constexpr int WSLOT = wslot_bytes<true>();
   constexpr int SET = NW_KB * WSLOT;
@@ -851,19 +864,59 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_row1_kernel(
   int xs32[NW_KB][4];  // 32 * xs_j for the lane's sub-blocks j = 4kq + t
   float dx[NW_KB];
   const int cs = col - 4 * kq;  // the chunk holding sub-block `col` in this lane's k-quarter
+  if (GATHER) {
+    const int32_t src = gx.idx[0];
+    const bool valid = src >= 0 && (int64_t)src < gx.L;
+    if (blockIdx.x == 0 && threadIdx.x == 0) gx.flags[0] = valid ? 0 : 1;
+    const float *xr = gx.canvas + (valid ? (int64_t)src : 0) * gx.ldc;
 #pragma unroll
-  for (int i = 0; i < NW_KB; ++i) {
-    const uint8_t *rec = qa + (int64_t)(wave + nw * i) * ACT_RECORD;  // row 0: unit u at 16 u
+    for (int i = 0; i < NW_KB; ++i) {
+      // lane l holds values 4l .. 4l+3 of the block, i.e. a quarter of unit l / 4
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        const float *p = xr + (int64_t)(wave + nw * i) * QK + 4 * lane;
+        if (gx.vec) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(p);
+          v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+        } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(rec + 16 * (4 * kq + c));
-      act[i][c] = c == cs ? v : i32x4{};
-      int sum = 0;
+          for (int e = 0; e < 4; ++e) v[e] = p[e];
+        }
+      }
+      const float amax = block_amax(v);
+      int c4[4];
+      quant4(v, amax, c4);
+      const int word = (int)pack4(c4);
+      dx[i] = block_dx(amax);
+      // the unit (16 codes) of sub-block `col`: the words of lanes 4 col .. 4 col + 3
+      i32x4 unit;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum = __builtin_amdgcn_sdot4(v[e], 0x01010101, sum, false);
-      xs32[i][c] = 32 * sum;
+      for (int e = 0; e < 4; ++e) unit[e] = __shfl(word, 4 * col + e, 64);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) act[i][c] = c == cs ? unit : i32x4{};
+      // code sums of units 4kq + t: each lane's 4 codes, summed over the quad
+      // of lanes that holds a unit, then fetched from the quad's first lane
+      int q4 = __builtin_amdgcn_sdot4(word, 0x01010101, 0, false);
+      q4 += dpp<DPP_QUAD_1032>(q4);
+      q4 += dpp<DPP_QUAD_2301>(q4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xs32[i][t] = 32 * __shfl(q4, 4 * (4 * kq + t), 64);
     }
-    dx[i] = *reinterpret_cast<const float *>(rec + ACT_DX_OFF);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW_KB; ++i) {
+      const uint8_t *rec = qa + (int64_t)(wave + nw * i) * ACT_RECORD;  // row 0: unit u at 16 u
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(rec + 16 * (4 * kq + c));
+        act[i][c] = c == cs ? v : i32x4{};
+        int sum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum = __builtin_amdgcn_sdot4(v[e], 0x01010101, sum, false);
+        xs32[i][c] = 32 * sum;
+      }
+      dx[i] = *reinterpret_cast<const float *>(rec + ACT_DX_OFF);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -1164,20 +1217,25 @@ hipError_t launch_narrow(int64_t M, int64_t N, int nb, const uint8_t *qa, const 
   return hipGetLastError();
 }
 
-// Single-row Q6_K launches (the same grid and eligibility as the narrow kernel).
+// Single-row Q6_K launches (the same grid and eligibility as the narrow kernel);
+// with gx.idx set the kernel gathers and quantizes the row itself.
 hipError_t launch_row1(int64_t N, int nb, const uint8_t *qa, const uint8_t *packed, float *y,
-                       float beta, float4 *part, hipStream_t stream) {
+                       float beta, float4 *part, const Gather &gx, hipStream_t stream) {
   dim3 grid((unsigned)narrow_grid(N)), block(64 * (nb / NW_KB));
   const bool vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (N % 4 == 0);
-  if (part)
-    hipLaunchKernelGGL((qgemm_row1_kernel<2, true, true>), grid, block, 0, stream, N, nb, qa,
-                       packed, nullptr, beta, part, (int)grid.x);
-  else if (vec)
-    hipLaunchKernelGGL((qgemm_row1_kernel<2, true, false>), grid, block, 0, stream, N, nb, qa,
-                       packed, y, 0.0f, nullptr, 0);
-  else
-    hipLaunchKernelGGL((qgemm_row1_kernel<2, false, false>), grid, block, 0, stream, N, nb, qa,
-                       packed, y, 0.0f, nullptr, 0);
+#define DQ_ROW1(VEC, STATS, GATHER)                                                           \
+  hipLaunchKernelGGL((qgemm_row1_kernel<2, VEC, STATS, GATHER>), grid, block, 0, stream, N, nb, \
+                     qa, packed, y, beta, part, (int)grid.x, gx)
+  if (gx.idx) {
+    if (part) DQ_ROW1(true, true, true);
+    else if (vec) DQ_ROW1(true, false, true);
+    else DQ_ROW1(false, false, true);
+  } else {
+    if (part) DQ_ROW1(true, true, false);
+    else if (vec) DQ_ROW1(true, false, false);
+    else DQ_ROW1(false, false, false);
+  }
+#undef DQ_ROW1
   return hipGetLastError();
 }
 
@@ -1381,7 +1439,7 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
   const int nb = (int)(K / QK);
   if (use_narrow(mode, M, N, nb, ldy)) {
     const bool two = M > MBLK;
-    if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, y, 0.0f, nullptr, stream);
+    if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, y, 0.0f, nullptr, Gather{}, stream);
     if (type == 14 && M <= 4) return launch_rows4(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
     if (type == 12)
       return two ? launch_narrow<12, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
@@ -1399,6 +1457,27 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
 // The sampler-state GEMM takes the narrow kernel where the plain one would
 // (its row-stride condition does not apply: nothing is stored per column),
 // else the canvas kernel with one state per row per column group.
+// The single-row output projection with the gather and quantization folded
+// into the GEMM launch (Q6_K, one row, where the narrow kernel would run):
+// part == nullptr stores y (row stride irrelevant for one row), else folds
+// sampler states.  Returns false, launching nothing, where it does not apply.
+bool launch_rows_gather_row1(int type, int64_t M, int64_t N, int64_t K, const float *canvas,
+                             int64_t ldc, const int32_t *idx, int64_t L, int32_t *flags,
+                             const uint8_t *packed, float *y, float beta, float4 *part,
+                             hipStream_t stream, hipError_t &err) {
+  const int nb = (int)(K / QK);
+  if (type != 14 || M != 1 || !use_narrow(part ? 3 : 1, M, N, nb, part ? 0 : N)) return false;
+  Gather gx;
+  gx.canvas = canvas;
+  gx.ldc = ldc;
+  gx.L = L;
+  gx.idx = idx;
+  gx.flags = flags;
+  gx.vec = reinterpret_cast<uintptr_t>(canvas) % 16 == 0 && ldc % 4 == 0;
+  err = launch_row1(N, nb, nullptr, packed, y, beta, part, gx, stream);
+  return true;
+}
+
 int qgemm_stats_parts(int64_t M, int64_t N, int64_t K) {
   const int nb = (int)(K / QK);
   if (use_narrow(3, M, N, nb, 0)) return (int)narrow_grid(N);
@@ -1412,7 +1491,8 @@ hipError_t launch_qgemm_stats(int type, int64_t M, int64_t N, int64_t K, const u
   const int nb = (int)(K / QK);
   if (use_narrow(3, M, N, nb, 0)) {
     const bool two = M > MBLK;
-    if (type == 14 && M == 1) return launch_row1(N, nb, qa, packed, nullptr, beta, part, stream);
+    if (type == 14 && M == 1)
+      return launch_row1(N, nb, qa, packed, nullptr, beta, part, Gather{}, stream);
     if (type == 14 && M <= 4)
       return launch_rows4(M, N, nb, qa, packed, nullptr, 0, beta, part, stream);
     if (type == 12)

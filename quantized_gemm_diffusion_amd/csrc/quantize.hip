@@ -29,33 +29,6 @@ namespace {
 
 constexpr int WAVES_PER_BLOCK = 4;
 
-// Cross-lane moves inside a row of 16 lanes (DPP): quad permutations
-// [1,0,3,2] and [2,3,0,1], half-row mirror (lane i <-> 7-i of each 8) and
-// row mirror (lane i <-> 15-i).  Broadcasts of lane 15 / 31 into the next
-// row(s) finish a reduction over the wave in lane 63.
-constexpr int DPP_QUAD_1032 = 0xb1, DPP_QUAD_2301 = 0x4e;
-constexpr int DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
-constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
-
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ inline int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
-}
-
-// max |x| over the wave (max is exact in any order), the same in every lane
-__device__ inline float wave_max(float v) {
-  auto step = [](float a, int b) { return fmaxf(a, __builtin_bit_cast(float, b)); };
-  v = step(v, dpp<DPP_QUAD_1032>(__builtin_bit_cast(int, v)));
-  v = step(v, dpp<DPP_QUAD_2301>(__builtin_bit_cast(int, v)));
-  v = step(v, dpp<DPP_ROW_HALF_MIRROR>(__builtin_bit_cast(int, v)));
-  v = step(v, dpp<DPP_ROW_MIRROR>(__builtin_bit_cast(int, v)));
-  // lanes of rows 1 and 3 take the max with lane 15 of the row before, then
-  // rows 2 and 3 with lane 31: lane 63 holds the maximum of all 64 lanes
-  v = step(v, dpp<DPP_ROW_BCAST15, 0xa>(__builtin_bit_cast(int, v)));
-  v = step(v, dpp<DPP_ROW_BCAST31, 0xc>(__builtin_bit_cast(int, v)));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 // sum over each group of 8 lanes (the 32 codes of one group), in every lane
 __device__ inline int group8_sum(int s) {
   s += dpp<DPP_QUAD_1032>(s);
@@ -69,22 +42,11 @@ __device__ inline int group8_sum(int s) {
 // takes part (the maximum and the group sums are reductions over the wave).
 __device__ inline void quantize_lane(const float (&v)[4], uint8_t *__restrict__ rec, int r,
                                      int lane) {
-  const float amax =
-      wave_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-
-  int c[4] = {0, 0, 0, 0};
-  if (amax != 0.0f) {
-    const float inv = 127.0f / amax;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t = __builtin_rintf(v[i] * inv);
-      t = fminf(fmaxf(t, -127.0f), 127.0f);
-      c[i] = (int)t;
-    }
-  }
+  const float amax = block_amax(v);
+  int c[4];
+  quant4(v, amax, c);
   // codes: lane owns bytes 4*lane .. 4*lane+3, i.e. unit u = lane/4 of the row
-  const uint32_t word = (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) |
-                        ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)(c[3] & 255) << 24);
+  const uint32_t word = pack4(c);
   const int u = lane >> 2;
   *reinterpret_cast<uint32_t *>(rec + r * QK + 16 * (u ^ r) + 4 * (lane & 3)) = word;
 
@@ -96,8 +58,7 @@ __device__ inline void quantize_lane(const float (&v)[4], uint8_t *__restrict__ 
     *reinterpret_cast<uint32_t *>(rec + ACT_SUMS_OFF + r * 32 + 4 * (lane >> 3)) =
         __builtin_bit_cast(uint32_t, h);
   }
-  if (lane == 0)
-    *reinterpret_cast<float *>(rec + ACT_DX_OFF + 4 * r) = amax != 0.0f ? amax / 127.0f : 0.0f;
+  if (lane == 0) *reinterpret_cast<float *>(rec + ACT_DX_OFF + 4 * r) = block_dx(amax);
   // the record's zero tail: 448 bytes, 28 per row
   if (lane < 7) *reinterpret_cast<uint32_t *>(rec + ACT_PAD_OFF + 28 * r + 4 * lane) = 0u;
 }

@@ -101,6 +101,12 @@ hipError_t launch_row_stats_finish(int64_t M, int npart, const float4 *part, int
 // The gathered-row GEMM whose epilogue folds each output row into partial
 // states instead of storing it; qgemm_stats_parts gives their count per row.
 int qgemm_stats_parts(int64_t M, int64_t N, int64_t K);
+// Single-row Q6_K projection with the gather-quantize in the GEMM launch (see
+// qgemm.hip); false (nothing launched) where it does not apply.
+bool launch_rows_gather_row1(int type, int64_t M, int64_t N, int64_t K, const float *canvas,
+                             int64_t ldc, const int32_t *idx, int64_t L, int32_t *flags,
+                             const uint8_t *packed, float *y, float beta, float4 *part,
+                             hipStream_t stream, hipError_t &err);
 hipError_t launch_qgemm_stats(int type, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
                               const uint8_t *packed, float beta, float4 *part, int npart,
                               hipStream_t stream);

@@ -268,6 +268,35 @@ def test_rows_out_of_range_index_is_flagged_not_read(dq):
     _check_tol(yn[[0, 3]], yr, T, "valid rows")
 
 
+@pytest.mark.parametrize("ldc_pad", [0, 1])  # 16-byte-aligned rows, and rows that are not
+def test_rows_single_row_gathers_in_the_gemm(dq, ldc_pad):
+    # one Q6_K row over a wide vocabulary: the gather and quantization run inside
+    # the GEMM launch; codes and sums must be those of the separate quantizer, so
+    # the row equals, bit for bit, the single-row GEMM of that row quantized apart
+    L, K, N = 40, 2048, 20000
+    W = _weights(oracle.Q6_K, N, K, 13, full_scales=True)
+    canvas = np.zeros((L, K + ldc_pad), np.float32)
+    canvas[:, :K] = synth.activations(np.random.default_rng(14), L, K)
+    canvas[5, :256] = 0.0  # a zero block
+    packed = dq.repack_weights(oracle.Q6_K, N, K, _t(W.reshape(-1)))
+    ct = _t(canvas)[:, :K] if ldc_pad else _t(canvas)
+    for r in (5, 0, L - 1):
+        y, ws = dq.qgemm_rows(oracle.Q6_K, ct, _t(np.array([r], np.int32)), packed, N)
+        y1 = dq.qgemm(oracle.Q6_K, dq.quantize_act(ct[r:r + 1]), packed, N)
+        _sync()
+        assert ws[:4].view(torch.int32).cpu().numpy()[0] == 0
+        yn = y.cpu().numpy()[0]
+        assert np.array_equal(yn.view(np.uint32), y1.cpu().numpy()[0].view(np.uint32)), r
+        gq, gd, _ = oracle.qgemm_rows_inputs(canvas[:, :K], np.array([r], np.int32))
+        yr, T = oracle.qgemm_ref(oracle.Q6_K, gq, gd, W, N)
+        _check_tol(yn[None, :], yr, T, f"single row {r}")
+    for bad in (L, -3):
+        y, ws = dq.qgemm_rows(oracle.Q6_K, ct, _t(np.array([bad], np.int32)), packed, N)
+        _sync()
+        assert ws[:4].view(torch.int32).cpu().numpy()[0] == 1
+        assert np.all(y.cpu().numpy() == 0)
+
+
 # --------------------------------------------------------------------------- #
 # ABI errors through the binding on the GPU                                   #
 # --------------------------------------------------------------------------- #
