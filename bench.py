@@ -62,7 +62,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--cpu-layers", type=int, default=16,
                    help="layers of the step the CPU oracle baseline runs on")
-    p.add_argument("--cpu-threads", type=int, default=min(os.cpu_count() or 1, 16))
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="oracle threads (default: every core this process may use, capped by "
+                        "OMP_NUM_THREADS -- the job's CPU share)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-configuration lines (Dream-7B, logits at 1 and 8 rows)")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (for profiler runs)")
     p.add_argument("--counters", action="store_true",
@@ -110,12 +114,32 @@ def stored_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+def host_clocks():
+    """GPU clocks as rocm-smi reports them, read in a child process before this
+    process touches the GPU (None if the tool is missing)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                             text=True, timeout=30)
+        data = json.loads(out.stdout)
+    except Exception:  # noqa: BLE001 -- the tool is optional
+        return None
+    res = {}
+    for card, d in data.items():
+        for k, v in d.items():
+            if "sclk" in k.lower() or "mclk" in k.lower() or "fclk" in k.lower():
+                res[f"{card} {k}"] = v
+        break
+    return res or None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         log("bench.py measures one GPU: this build runs the hot path on a single MI355X; "
             "multi-GPU sharding is a design note only, so --gpus must be 1.")
         sys.exit(2)
+    clocks_before = host_clocks()
 
     import torch
     import quantized_gemm_diffusion_amd as dq
@@ -336,6 +360,10 @@ def main():
     else:
         achieved, peak, unit = dom_ops / dom_avg_s / 1e12, INT8_PEAK_TOPS, "TOPS"
     traffic = stored_traffic(dominant)
+    configs = None if args.no_configs else config_lines(lib, dq, torch, stream, sp, up,
+                                                        out_packed, canvas)
+    if configs:
+        log("configurations:", json.dumps(configs))
 
     step_s = ms_per_step * 1e-3
     result = {
@@ -365,15 +393,25 @@ def main():
         "mfma_frac": round(step_ops / step_s / 1e12 / INT8_PEAK_TOPS, 4),
         "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "avg_launch_us": round(dom_avg_s * 1e6, 3),
+                     "traffic": traffic,
+                     "traffic_source": ("profiles/traffic.json: rocprofv3 FETCH_SIZE + "
+                                        "WRITE_SIZE per launch of this kernel, calibrated by a "
+                                        f"plain copy; taken on sources with hash "
+                                        f"{source_hash()}" if traffic is not None else
+                                        "none: the kernel's sources changed since the counters "
+                                        "were taken"),
+                     "avg_launch_us": round(dom_avg_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": int(dom_bytes),
                      "ops_per_launch": int(dom_ops), "launches": dom_launches},
         "kernels_isolated": kernels,
         "sampler_output_projection": sampler,
         "attention": attn,
         "embedding_rows": emb,
+        "configs": configs,
         "step_timing": f"HIP graph replay of the step's {len(calls)} launches",
-        "device": torch.cuda.get_device_properties(dev).name,
+        "device": device_info(torch, dev),
+        "clocks_rocm_smi": clocks_before,
+        "host_cores": {"os_cpu_count": os.cpu_count(), "usable": _usable_cores()},
     }
 
     # ------------------------------------------------- CPU oracle baseline
@@ -381,6 +419,139 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts,
                                                 gammas)
     print(json.dumps(result), flush=True)
+
+
+def _usable_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count()
+
+
+def device_info(torch, dev):
+    """Name, architecture, compute units and peak shader clock (hipDeviceGetAttribute)."""
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        # hipDeviceAttributeClockRate: peak clock in kHz
+        attr = 5
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev.index or 0) == 0:
+            info["peak_sclk_MHz"] = v.value // 1000
+    except OSError:
+        pass
+    return info
+
+
+def config_lines(lib, dq, torch, stream, sp, up, out_packed, canvas, reps=10):
+    """Per-configuration lines beside the LLaDA-8B step (whose shapes are configs
+    2 and 3, and config 4 at 32 rows):
+      * config 1, the single 16x256x512 Q4_K GEMM: a correctness configuration
+        (launch-bound; its parity is in the tests), timed only;
+      * config 4 at 1 and 8 gathered rows (126,464 x 4096 Q6_K logits);
+      * config 5, Dream-7B at canvas L = 512 (K = 3584): Q/K/V stacked into one
+        4608 x 3584 Q4_K matrix, O 3584 x 3584, gate/up stacked 37888 x 3584, down
+        3584 x 18944 Q6_K, over 8 layers of seeded weights (1.2 GB, rotated so
+        that HBM, not the 256 MB last-level cache, serves them), plus the output
+        projection on 64 gathered rows (152,064 x 3584 Q6_K).
+    HIP events around `reps` rounds of launches on the step's stream; per GEMM:
+    us, TOPS, algorithmic GB/s and the fraction of the binding roofline
+    (max of bytes / HBM peak and operations / int8 MFMA peak)."""
+    dev = canvas.device
+
+    def line(us, ops, nbytes, extra=None):
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = ops / (INT8_PEAK_TOPS * 1e12)
+        d = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 2),
+             "GB_s": round(nbytes / us / 1e3, 1), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+             "bound_us": round(1e6 * max(t_hbm, t_mfma), 2),
+             "roofline_frac": round(1e6 * max(t_hbm, t_mfma) / us, 4)}
+        if extra:
+            d.update(extra)
+        return d
+
+    def timed(fns):
+        for f in fns:
+            if f():
+                raise RuntimeError(lib.dq_last_error().decode())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for f in fns:
+                f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / (reps * len(fns))
+
+    res = {}
+    # config 1
+    rng = np.random.default_rng(0)
+    x1 = up(synth.activations(rng, 16, 512))
+    W1 = synth.q4k_weights(rng, 256, 512)
+    p1 = dq.repack_weights(Q4_K, 256, 512, up(W1.reshape(-1)))
+    a1 = dq.quantize_act(x1)
+    y1 = torch.empty((16, 256), dtype=torch.float32, device=dev)
+    us = timed([lambda: lib.dq_qgemm(Q4_K, 16, 256, 512, a1.buf.data_ptr(), p1.data_ptr(),
+                                     y1.data_ptr(), 256, sp)])
+    res["config1_q4k_16x256x512"] = line(us, 2 * 16 * 256 * 512, gemm_bytes(Q4_K, 16, 256, 512),
+                                         {"note": "correctness configuration: launch-bound"})
+    # config 4 at 1 and 8 rows
+    for M in (1, 8):
+        idx = up(synth.row_index(np.random.default_rng(synth.seed(3, 0, 2) + M), L, M))
+        y = torch.empty((M, V), dtype=torch.float32, device=dev)
+        wsr = torch.empty(dq.qgemm_rows_workspace(M, K), dtype=torch.uint8, device=dev)
+        us = timed([lambda: lib.dq_qgemm_rows(Q6_K, L, M, V, K, canvas.data_ptr(), K,
+                                              idx.data_ptr(), out_packed.data_ptr(),
+                                              y.data_ptr(), V, wsr.data_ptr(), wsr.numel(), sp)])
+        nbytes = V * (K // 256) * BLOCK[Q6_K] + M * K * 4 + M * 4 + M * V * 4
+        res[f"config4_llada_logits_rows{M}"] = line(us, 2 * M * V * K, nbytes)
+    # config 5
+    D, LD = synth.DREAM, 512
+    KD, FD, KVD, VD = D["K"], D["ffn"], D["kv"], D["vocab"]
+    layers = 8
+    xd = up(synth.activations(np.random.default_rng(synth.seed(4, 0, 9)), LD, KD))
+    xf = up(synth.activations(np.random.default_rng(synth.seed(4, 0, 8)), LD, FD))
+    ad, af = dq.quantize_act(xd), dq.quantize_act(xf)
+    shapes = {"qkv": (Q4_K, KD + 2 * KVD, KD, ad), "o": (Q4_K, KD, KD, ad),
+              "gateup": (Q4_K, 2 * FD, KD, ad), "down": (Q6_K, KD, FD, af)}
+    mats = {n: [] for n in shapes}
+    for layer in range(layers):
+        for n, (t, N, KK, _) in shapes.items():
+            W = synth.weights(np.random.default_rng(synth.seed(4, layer + 1, len(mats[n]) + 17)),
+                              t, N, KK)
+            mats[n].append(dq.repack_weights(t, N, KK, up(W.reshape(-1))))
+            del W
+    ys = {n: torch.empty((LD, shapes[n][1]), dtype=torch.float32, device=dev) for n in shapes}
+    total_us = 0.0
+    for n, (t, N, KK, a) in shapes.items():
+        fns = [(lambda pk=pk, t=t, N=N, KK=KK, a=a, y=ys[n]:
+                lib.dq_qgemm(t, LD, N, KK, a.buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N, sp))
+               for pk in mats[n]]
+        us = timed(fns)
+        total_us += us
+        res[f"config5_dream_{n}_{LD}x{N}x{KK}_{'q4k' if t == Q4_K else 'q6k'}"] = line(
+            us, 2 * LD * N * KK, gemm_bytes(t, LD, N, KK))
+    ops = sum(2 * LD * N * KK for t, N, KK, _ in shapes.values())
+    nbytes = sum(gemm_bytes(t, LD, N, KK) for t, N, KK, _ in shapes.values())
+    res["config5_dream_layer_gemms"] = line(total_us, ops, nbytes,
+                                            {"note": "Q/K/V + O + gate/up + down of one layer"})
+    del mats
+    Wd = synth.q6k_weights(np.random.default_rng(synth.seed(4, 0, 7)), VD, KD)
+    pd = dq.repack_weights(Q6_K, VD, KD, up(Wd.reshape(-1)))
+    del Wd
+    cd = up(synth.activations(np.random.default_rng(synth.seed(4, 0, 6)), LD, KD))
+    idx = up(synth.row_index(np.random.default_rng(synth.seed(4, 0, 5)), LD, 64))
+    y = torch.empty((64, VD), dtype=torch.float32, device=dev)
+    wsr = torch.empty(dq.qgemm_rows_workspace(64, KD), dtype=torch.uint8, device=dev)
+    us = timed([lambda: lib.dq_qgemm_rows(Q6_K, LD, 64, VD, KD, cd.data_ptr(), KD,
+                                          idx.data_ptr(), pd.data_ptr(), y.data_ptr(), VD,
+                                          wsr.data_ptr(), wsr.numel(), sp)])
+    nbytes = VD * (KD // 256) * BLOCK[Q6_K] + 64 * KD * 4 + 64 * 4 + 64 * VD * 4
+    res["config5_dream_logits_rows64"] = line(us, 2 * 64 * VD * KD, nbytes)
+    return res
 
 
 def _oracle_seconds(fn):
@@ -556,7 +727,7 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):
     """The oracle, as it stands, on the first layers of the step plus 1/4 of the vocab rows."""
     import oracle
 
-    th = args.cpu_threads
+    th = args.cpu_threads or oracle.host_threads()
     xs = {k: v.cpu().numpy() for k, v in acts.items()}
     ops = 0
     t0 = time.perf_counter()

@@ -11,17 +11,24 @@
  *
  * Conventions shared by every entry point
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
- *     allocates nothing, keeps no state besides a per-device property cache,
- *     and is safe to call from several host threads.
+ *     allocates nothing and is safe to call from several host threads.  Its
+ *     only state: a per-device cache of the compute-unit and XCD counts the
+ *     launchers size their grids by (queried on the first call on a device).
  *   - Every call only validates its arguments on the host and enqueues work on
  *     `stream`; it returns before the work runs.  Results are visible after
  *     the caller synchronizes the stream.
  *   - Shapes: K is the reduction length and must be a positive multiple of
  *     256 (one K-quant super-block).  M (activation rows) and N (weight rows)
  *     may be any value >= 0; M == 0 or N == 0 is a valid no-op.
- *   - Return value: DQ_OK or one of the DQ_E* codes below.  On any error no
- *     work is enqueued.  dq_last_error() gives a message for the last error
- *     raised on the calling host thread.
+ *   - Return value: DQ_OK or one of the DQ_E* codes below.  A call that
+ *     returns DQ_EINVAL, DQ_EUNSUPPORTED or DQ_EWORKSPACE has enqueued
+ *     nothing (every argument is checked before the first launch).  DQ_EHIP
+ *     means the HIP runtime refused a launch; in a call that makes several
+ *     launches (dq_qgemm_rows, dq_qgemm_rows_sample, dq_logits_stats,
+ *     dq_attention) the launches before the refused one may already be
+ *     enqueued and may have written the workspace, the flags or the output.
+ *     dq_last_error() gives a message for the last error raised on the
+ *     calling host thread.
  *   - Types: weights are GGUF tensors of type DQ_Q4_K or DQ_Q6_K (the GGUF
  *     type ids).  A 2-D GGUF weight of shape N x K is N rows, each of K/256
  *     consecutive super-blocks (144 bytes for Q4_K, 210 bytes for Q6_K).
@@ -58,6 +65,13 @@ const char *dq_last_error(void);
 
 /* --------------------------------------------------------------------------
  * dq_packed_size -- bytes of the repacked matrix (host-only, no GPU work).
+ *
+ * Source (of this and the other size queries, dq_act_size and the
+ * *_workspace calls): Architecture page, "A forward pass" (the forward pass
+ * allocates nothing; every buffer is sized once, up front, for the longest
+ * canvas) and the aiboss88 news page, licence and limits (when free VRAM is
+ * short the program reports the VRAM it needs and exits): the caller learns
+ * every size before it allocates, and the library never allocates.
  *
  * The repacked layout holds the same bits as the GGUF blocks (4.5 bits per
  * Q4_K weight, 6.5625 bits per Q6_K weight), permuted into tiles of 16 weight
@@ -105,6 +119,7 @@ int dq_repack_weights(int type, int64_t N, int64_t K, const void *gguf, void *pa
 #define DQ_ACT_RECORD 5120
 
 /* Bytes of the quantized-activation buffer for M rows of length K (host-only).
+ * Source: as for dq_packed_size (sizes known before any allocation).
  * Errors: DQ_EINVAL (K, M < 0, bytes NULL, size beyond 2^32). */
 int dq_act_size(int64_t M, int64_t K, size_t *bytes);
 
@@ -205,6 +220,7 @@ int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const void *qa, const vo
  * dq_qgemm_rows_workspace -- workspace bytes dq_qgemm_rows needs for M
  * gathered rows of length K (host-only): the index flags, then the quantized
  * activations of the gathered rows.
+ * Source: as for dq_packed_size (sizes known before any allocation).
  * ------------------------------------------------------------------------ */
 int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes);
 
@@ -270,7 +286,9 @@ int dq_logits_stats(int64_t M, int64_t N, const float *y, int64_t ldy, float bet
  * projection on the requested canvas rows (as dq_qgemm_rows) with the sampler
  * statistics above computed in the GEMM's epilogue: the logits are reduced
  * where they are formed and never written to memory.  The logits reduced are
- * bit-identical to the y that dq_qgemm_rows writes for the same arguments.
+ * bit-identical to the y that dq_qgemm_rows writes for the same arguments
+ * when that call's row stride ldy is at most 2^25 floats (dq_qgemm_rows takes
+ * another kernel, with another summation order, for longer rows).
  *   canvas, ldc, idx, packed : as for dq_qgemm_rows (idx flags likewise in the
  *           first 4*M bytes of ws).
  *   beta, token, stats       : as for dq_logits_stats.

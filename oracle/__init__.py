@@ -116,8 +116,21 @@ def _rows(W: np.ndarray, type_: int, K: int) -> np.ndarray:
     return W.reshape(-1, nb * BLOCK_BYTES[type_])
 
 
+def host_threads() -> int:
+    """Threads the oracle runs on: the cores this process may use, capped by
+    OMP_NUM_THREADS when the environment sets it (a job's CPU share)."""
+    try:
+        t = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        t = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        t = min(t, int(cap))
+    return max(1, t)
+
+
 def _threads(n: int, threads: int | None):
-    t = threads or os.cpu_count() or 1
+    t = threads or host_threads()
     t = max(1, min(t, n))
     bounds = [n * i // t for i in range(t + 1)]
     return [(bounds[i], bounds[i + 1]) for i in range(t) if bounds[i + 1] > bounds[i]]

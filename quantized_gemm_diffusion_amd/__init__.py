@@ -8,7 +8,7 @@ the current stream; tensors must live on a GPU.
 
 Names follow the C ABI:
   packed_size, repack_weights, act_size, quantize_act, swiglu_quantize_act,
-  rmsnorm_quantize_act, qgemm, qgemm_rows_workspace, qgemm_rows, debug_superblock_sums.
+  rmsnorm_quantize_act, qgemm, qgemm_rows_workspace, qgemm_rows, debug_superblock_sums, ...
 Quantized activations travel as an ``Act`` (the device buffer in the record
 layout that include/dq.h documents, with its M and K).
 """

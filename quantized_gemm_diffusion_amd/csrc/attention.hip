@@ -177,14 +177,13 @@ __device__ inline void store_out(float lsum, const f32x4 (&o)[8], float *orow, i
   }
 }
 
-// Workgroups are dealt to the 8 XCDs in turn, and each XCD has its own L2:
-// number the workgroups of one kv head 8 apart (while whole groups of 8 kv
-// heads remain) so that they run on one XCD and fetch that head's images into
-// one L2.
-// With fewer than 8 kv heads (dividing 8), each kv head's workgroups go to
-// 8 / nkv XCDs instead (all 8 stay busy).
-__device__ inline void place_kv(int id, int nkv, int per, int &kv, int &item) {
-  constexpr int XCDS = 8;
+// Workgroups are dealt to the device's XCDS XCDs in turn, and each XCD has
+// its own L2: number the workgroups of one kv head XCDS apart (while whole
+// groups of XCDS kv heads remain) so that they run on one XCD and fetch that
+// head's images into one L2.
+// With fewer kv heads than XCDs (dividing XCDS), each kv head's workgroups go
+// to XCDS / nkv XCDs instead (all of them stay busy).
+__device__ inline void place_kv(int id, int nkv, int per, int XCDS, int &kv, int &item) {
   if (nkv < XCDS && XCDS % nkv == 0 && per % (XCDS / nkv) == 0) {
     const int slot = id / XCDS, xcd = id - slot * XCDS;
     kv = xcd % nkv;
@@ -217,10 +216,11 @@ __global__ __launch_bounds__(256) void attention_pack_kernel(int L, int H, int H
                                                              const float *__restrict__ qkv,
                                                              int64_t ldqkv,
                                                              const float *__restrict__ rope,
-                                                             uint8_t *__restrict__ img) {
+                                                             uint8_t *__restrict__ img,
+                                                             int xcds) {
   const int nblk = (L + KB - 1) / KB;
   int hk, item;  // the kv head's workgroups on the XCD its attention workgroups use
-  place_kv(blockIdx.x, Hkv, nblk * 5, hk, item);
+  place_kv(blockIdx.x, Hkv, nblk * 5, xcds, hk, item);
   const int b = item / 5;
   const int im = hk * nblk + b;  // image hk * nblk + b
   const int kcol = (H + hk) * AD, vcol = (H + Hkv + hk) * AD;
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(int L, int H, int Hk
                                                             const float *__restrict__ rope,
                                                             const uint8_t *__restrict__ img,
                                                             float *__restrict__ out, int64_t ldo,
-                                                            int out_vec) {
+                                                            int out_vec, int xcds) {
   constexpr int LPW = IMG_BYTES / 1024 / QW;  // loads per wave per block
   constexpr int RING = ring_slots(QW);
   // the first RING - 1 copies, then Q's 8 + 16 loads (rows and RoPE table)
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(int L, int H, int Hk
   const int qblocks = (L + 16 * QW - 1) / (16 * QW);
   const int G = H / Hkv;
   int hk, item;  // kv head, and (query head in its group, query block)
-  place_kv(blockIdx.x, Hkv, G * qblocks, hk, item);
+  place_kv(blockIdx.x, Hkv, G * qblocks, xcds, hk, item);
   const int h = hk * G + item / qblocks;
   const int q0 = (item % qblocks) * 16 * QW + 16 * wave;
   const int nblk = (L + KB - 1) / KB;
@@ -423,22 +423,23 @@ hipError_t launch_mode(int64_t L, int64_t H, int64_t Hkv, const float *qkv, int6
                        const float *rope, uint8_t *img, float *out, int64_t ldo,
                        hipStream_t stream) {
   const int64_t nblk = (L + KB - 1) / KB;
+  const int xcds = device_props().xcds;
   hipLaunchKernelGGL((attention_pack_kernel<MODE>), dim3((unsigned)(Hkv * nblk * 5)), dim3(256),
-                     0, stream, (int)L, (int)H, (int)Hkv, qkv, ldqkv, rope, img);
+                     0, stream, (int)L, (int)H, (int)Hkv, qkv, ldqkv, rope, img, xcds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_vec = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ldo % 4 == 0);
   // 32 queries per workgroup; 64 once that still gives a workgroup to half the
   // CUs (measured: Dream-7B's 224 four-wave workgroups beat its 448 two-wave
   // ones by 6%, LLaDA-8B's 96 would lose to its 160)
-  if (H * ((L + 63) / 64) >= 128) {
+  if (H * ((L + 63) / 64) >= device_props().cus / 2) {
     hipLaunchKernelGGL((attention_kernel<MODE, 4>), dim3((unsigned)(H * ((L + 63) / 64))),
                        dim3(256), 0, stream, (int)L, (int)H, (int)Hkv, qkv, ldqkv, rope, img, out,
-                       ldo, out_vec);
+                       ldo, out_vec, xcds);
   } else {
     hipLaunchKernelGGL((attention_kernel<MODE, 2>), dim3((unsigned)(H * ((L + 31) / 32))),
                        dim3(128), 0, stream, (int)L, (int)H, (int)Hkv, qkv, ldqkv, rope, img, out,
-                       ldo, out_vec);
+                       ldo, out_vec, xcds);
   }
   return hipGetLastError();
 }

@@ -210,9 +210,12 @@ int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes) {
   return ok();
 }
 
-int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
-                  int64_t ldc, const int32_t *idx, const void *packed, float *y, int64_t ldy,
-                  void *ws, size_t ws_bytes, hipStream_t stream) {
+// Arguments of the gathered-row projection, checked; M == 0 or N == 0 is a
+// valid no-op (returns DQ_OK with *noop set).
+static int check_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
+                      int64_t ldc, const int32_t *idx, const void *packed, const float *y,
+                      int64_t ldy, bool *noop) {
+  *noop = true;
   if (int s = check_type(type)) return s;
   if (int s = check_k(K)) return s;
   if (L < 0 || L > kMaxRows) return fail(DQ_EINVAL, "L = %lld out of range", (long long)L);
@@ -220,29 +223,47 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
   if (N < 0 || N > kMaxRows) return fail(DQ_EINVAL, "N = %lld out of range", (long long)N);
   if (ldc < K) return fail(DQ_EINVAL, "ldc = %lld < K = %lld", (long long)ldc, (long long)K);
   if (ldy < N) return fail(DQ_EINVAL, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
-  if (M == 0 || N == 0) return ok();
+  if (M == 0 || N == 0) return DQ_OK;
   if (!canvas || !idx || !packed || !y) return fail(DQ_EINVAL, "NULL pointer argument");
   if (!aligned(canvas, 4) || !aligned(idx, 4) || !aligned(y, 4) || !aligned(packed, 16))
     return fail(DQ_EINVAL, "canvas, idx, y must be 4-byte aligned, packed 16-byte aligned");
+  *noop = false;
+  return DQ_OK;
+}
+
+// The launches of the gathered-row projection: flags[M] and the records qa of
+// the gathered rows are device memory the caller of this function provides.
+static int rows_launch(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
+                       int64_t ldc, const int32_t *idx, const void *packed, float *y, int64_t ldy,
+                       int32_t *flags, uint8_t *qa, hipStream_t stream, const char *who) {
+  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
+  hipError_t e = hipSuccess;
+  if (dq::launch_rows_gather_row1(type, M, N, K, canvas, ldc, idx, L, flags,
+                                  static_cast<const uint8_t *>(packed), y, 0.0f, nullptr, stream,
+                                  e))
+    return launched(e, who);
+  e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
+  if (e != hipSuccess) return launched(e, who);
+  return launched(dq::launch_qgemm(type, 1, M, N, K, qa, static_cast<const uint8_t *>(packed), y,
+                                   ldy, nullptr, nullptr, stream),
+                  who);
+}
+
+int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
+                  int64_t ldc, const int32_t *idx, const void *packed, float *y, int64_t ldy,
+                  void *ws, size_t ws_bytes, hipStream_t stream) {
+  bool noop = true;
+  if (int s = check_rows(type, L, M, N, K, canvas, ldc, idx, packed, y, ldy, &noop)) return s;
+  if (noop) return ok();
   size_t need = 0;
   if (int s = dq_qgemm_rows_workspace(M, K, &need)) return s;
   if (!ws || ws_bytes < need)
     return fail(DQ_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
   if (!aligned(ws, 256)) return fail(DQ_EINVAL, "workspace must be 256-byte aligned");
   uint8_t *w = static_cast<uint8_t *>(ws);
-  uint8_t *qa = w + rows_ws_flags(M);
-  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
-  int32_t *flags = reinterpret_cast<int32_t *>(w);
-  hipError_t e = hipSuccess;
-  if (dq::launch_rows_gather_row1(type, M, N, K, canvas, ldc, idx, L, flags,
-                                  static_cast<const uint8_t *>(packed), y, 0.0f, nullptr, stream,
-                                  e))
-    return launched(e, "dq_qgemm_rows (single-row gather + gemm)");
-  e = dq::launch_quantize(M, K, canvas, ldc, idx, L, qa, flags, stream);
-  if (e != hipSuccess) return launched(e, "dq_qgemm_rows (gather-quantize)");
-  return launched(dq::launch_qgemm(type, 1, M, N, K, qa, static_cast<const uint8_t *>(packed), y,
-                                   ldy, nullptr, nullptr, stream),
-                  "dq_qgemm_rows (gemm)");
+  return rows_launch(type, L, M, N, K, canvas, ldc, idx, packed, y, ldy,
+                     reinterpret_cast<int32_t *>(w), w + rows_ws_flags(M), stream,
+                     "dq_qgemm_rows");
 }
 
 static int check_beta(float beta) {

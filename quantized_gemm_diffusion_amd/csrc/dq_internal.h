@@ -122,6 +122,15 @@ __device__ inline uint32_t pack4(const int (&c)[4]) {
 // The block's activation scale d_x.
 __device__ inline float block_dx(float amax) { return amax != 0.0f ? amax / 127.0f : 0.0f; }
 
+// Compute units and XCDs (each with its own L2) of the current device, queried
+// once per device (device.hip); {256, 8} -- a whole MI355X -- if the query
+// fails.  The launchers size persistent grids and XCD-aware placements by it.
+struct DeviceProps {
+  int cus = 256;
+  int xcds = 8;
+};
+DeviceProps device_props();
+
 // Launchers (each returns the hipError_t of its launch).
 // Quantize M rows (row m = x[m], or x[idx[m]] when idx is given) into the
 // record layout; err[m] flags an index outside [0, L).

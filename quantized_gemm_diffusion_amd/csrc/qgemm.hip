@@ -375,17 +375,17 @@ constexpr int lds_bytes() {
 }
 constexpr int cap63(int v) { return v > 63 ? 63 : v; }
 
-// Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8), and
-// each XCD has its own L2.  The nrg row groups of one column group read the
-// same weight tiles, so they are placed 8 apart in launch order: they run on
-// one XCD at about the same time, and the tiles come from HBM once.  Column
-// groups past the last complete set of 8 are numbered in order.
-constexpr int XCDS = 8;
-__device__ inline void place(int id, int ncg, int nrg, int &cg, int &rg) {
-  const int full = ncg / XCDS * XCDS;
+// Workgroups are dealt to the device's xcds XCDs in turn (workgroup i to XCD
+// i mod xcds), and each XCD has its own L2.  The nrg row groups of one column
+// group read the same weight tiles, so they are placed xcds apart in launch
+// order: they run on one XCD at about the same time, and the tiles come from
+// HBM once.  Column groups past the last complete set of xcds are numbered in
+// order.
+__device__ inline void place(int id, int ncg, int nrg, int xcds, int &cg, int &rg) {
+  const int full = ncg / xcds * xcds;
   if (id < full * nrg) {
-    const int slot = id / XCDS, xcd = id - slot * XCDS;
-    cg = slot / nrg * XCDS + xcd;
+    const int slot = id / xcds, xcd = id - slot * xcds;
+    cg = slot / nrg * xcds + xcd;
     rg = slot % nrg;
   } else {
     const int t = id - full * nrg;
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
                                                                    int32_t *__restrict__ dbg_Mn,
                                                                    float beta,
                                                                    float4 *__restrict__ part,
-                                                                   int npart) {
+                                                                   int npart, int xcds) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
   constexpr int MB = SH::MB, NT = SH::NT, R = SH::R, D = R - 1, WAVES = SH::WAVES;
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
   const int nmb = (M + MBLK - 1) / MBLK;
   int cg, rg;  // column group (NT n-tiles) and row group (MB m-blocks) of this workgroup
-  place((int)blockIdx.x, (int)((ntiles + NT - 1) / NT), (nmb + MB - 1) / MB, cg, rg);
+  place((int)blockIdx.x, (int)((ntiles + NT - 1) / NT), (nmb + MB - 1) / MB, xcds, cg, rg);
   const int64_t nt0 = (int64_t)cg * NT;
   const int mb0 = rg * MB;  // first 16-row block of this workgroup
   // this wave's LDS: R activation slabs, then NT tile slots
@@ -1187,11 +1187,10 @@ __global__ __launch_bounds__(64 * NW_WAVES, 1) void qgemm_rows4_kernel(
 }
 
 // Narrow launches: one workgroup per CU (fewer if there are fewer tiles).
-constexpr int NW_CUS = 256;
-
 inline int64_t narrow_grid(int64_t N) {
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
-  return ntiles < NW_CUS ? ntiles : NW_CUS;
+  const int64_t cus = device_props().cus;
+  return ntiles < cus ? ntiles : cus;
 }
 
 // part == nullptr: store y; otherwise fold the rows into part (npart =
@@ -1263,7 +1262,7 @@ hipError_t launch_rows4(int64_t M, int64_t N, int nb, const uint8_t *qa, const u
 inline bool use_narrow(int mode, int64_t M, int64_t N, int nb, int64_t ldy) {
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
   return mode != 2 && M <= 2 * MBLK && nb % NW_KB == 0 && nb >= 4 * NW_KB &&
-         nb <= NW_WAVES * NW_KB && ntiles >= 4 * NW_CUS && ldy <= (int64_t(1) << 25);
+         nb <= NW_WAVES * NW_KB && ntiles >= 4 * device_props().cus && ldy <= (int64_t(1) << 25);
 }
 
 struct Extra {  // arguments of the debug and sampler-state modes
@@ -1287,7 +1286,8 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
   const int y_vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);
 #define DQ_LAUNCH(MODE)                                                                        \
   hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, MODE>), grid, block, 0, stream, m, N, nb, qa,        \
-                     qa_bytes, packed, y, ldy, y_vec, x.dbg_S, x.dbg_Mn, x.beta, x.part, x.npart)
+                     qa_bytes, packed, y, ldy, y_vec, x.dbg_S, x.dbg_Mn, x.beta, x.part, x.npart, \
+                     device_props().xcds)
   switch (mode) {
     case 1: DQ_LAUNCH(1); break;
     case 2: DQ_LAUNCH(2); break;
@@ -1321,12 +1321,10 @@ struct Pick {
   int mb, waves, nt;
 };
 
-constexpr int64_t CUS = 256;
-
 // Fraction of workgroup slots used over a launch of wgs workgroups with
 // per_cu workgroups resident per CU.
 inline double fill(int64_t wgs, int64_t per_cu) {
-  const int64_t slots = CUS * per_cu;
+  const int64_t slots = device_props().cus * per_cu;
   const int64_t rounds = (wgs + slots - 1) / slots;
   return (double)wgs / (double)(rounds * slots);
 }
@@ -1369,6 +1367,7 @@ inline Pick pick_shape(int type, int mode, int64_t M, int64_t N, int64_t nb) {
   const int64_t wgs = tiles * chunks;
   Pick pk{mb, 4, 2};
   const int64_t wgs3 = (ntiles + 2) / 3 * chunks;
+  const int64_t CUS = device_props().cus;
   if (((type == 12 && mb == 5) || (type == 14 && mb == 4)) && wgs3 >= 2 * CUS &&
       (fill(wgs3, 2) >= fill(wgs, 2) || wgs3 >= 8 * CUS))
     pk = Pick{mb, wgs3 >= 4 * CUS ? 2 : 4, 3};

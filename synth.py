@@ -16,6 +16,8 @@ Draws (numpy ``default_rng(seed)``, PCG64), in this order per matrix:
     bytes and 64 high-bit bytes uniform (every 6-bit code uniform on [0, 63]).
   * Activations: N(0, 1) float32, then round(0.01 * K) columns drawn without
     replacement and multiplied by 20 in every row.
+  * Edge-case option (tests only): ``mixed_scales`` draws d (and dmin) as a
+    mixture of positive, negative, signed-zero and subnormal fp16 values.
 """
 from __future__ import annotations
 
@@ -27,8 +29,21 @@ QK = 256
 BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
 
 
-def _fp16_bytes(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+def _fp16_bytes(rng: np.random.Generator, shape, scale: float, mixed: bool = False) -> np.ndarray:
+    """fp16 scale fields: |N(0,1)| * scale, or with ``mixed`` a mixture of
+    signs and special values (the format allows any fp16 here): 35% positive
+    and 35% negative normal values of that size, 10% signed zeros, 20% random
+    subnormal patterns of either sign."""
     v = (np.abs(rng.standard_normal(shape)) * scale).astype(np.float16)
+    if mixed:
+        bits = v.view(np.uint16).copy()
+        u = rng.random(shape)
+        sign = rng.integers(0, 2, shape).astype(np.uint16) << 15
+        sub = rng.integers(1, 1024, shape).astype(np.uint16)
+        bits = np.where(u < 0.35, bits, bits | np.uint16(0x8000))
+        bits = np.where((u >= 0.70) & (u < 0.80), sign, bits)
+        bits = np.where(u >= 0.80, sign | sub, bits)
+        v = bits.astype(np.uint16).view(np.float16)
     return v.view(np.uint8).reshape(tuple(shape) + (2,))
 
 
@@ -37,23 +52,26 @@ def _bytes(rng: np.random.Generator, shape) -> np.ndarray:
     return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape)
 
 
-def q4k_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-3) -> np.ndarray:
-    """N x K weights as raw Q4_K blocks, uint8 [N, K/256, 144]."""
+def q4k_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-3,
+                mixed_scales: bool = False) -> np.ndarray:
+    """N x K weights as raw Q4_K blocks, uint8 [N, K/256, 144].  With
+    ``mixed_scales`` d and dmin take signs, zeros and subnormals too."""
     nb = K // QK
     out = np.empty((N, nb, 144), np.uint8)
-    out[..., 0:2] = _fp16_bytes(rng, (N, nb), d_scale)
-    out[..., 2:4] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 0:2] = _fp16_bytes(rng, (N, nb), d_scale, mixed_scales)
+    out[..., 2:4] = _fp16_bytes(rng, (N, nb), d_scale, mixed_scales)
     out[..., 4:16] = _bytes(rng, (N, nb, 12))
     out[..., 16:144] = _bytes(rng, (N, nb, 128))
     return out
 
 
 def q6k_weights(rng: np.random.Generator, N: int, K: int, d_scale: float = 2e-3,
-                sc_lo: int = -32, sc_hi: int = 31) -> np.ndarray:
-    """N x K weights as raw Q6_K blocks, uint8 [N, K/256, 210]."""
+                sc_lo: int = -32, sc_hi: int = 31, mixed_scales: bool = False) -> np.ndarray:
+    """N x K weights as raw Q6_K blocks, uint8 [N, K/256, 210].  With
+    ``mixed_scales`` d takes signs, zeros and subnormals too."""
     nb = K // QK
     out = np.empty((N, nb, 210), np.uint8)
-    out[..., 208:210] = _fp16_bytes(rng, (N, nb), d_scale)
+    out[..., 208:210] = _fp16_bytes(rng, (N, nb), d_scale, mixed_scales)
     out[..., 192:208] = rng.integers(sc_lo, sc_hi + 1, size=(N, nb, 16)).astype(np.int8).view(
         np.uint8)
     out[..., 0:192] = _bytes(rng, (N, nb, 192))

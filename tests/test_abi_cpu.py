@@ -34,6 +34,31 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, s), s
 
 
+def _doc_blocks():
+    """The comment block in front of each declaration of include/dq.h."""
+    text = open(HEADER).read()
+    blocks = {}
+    for m in re.finditer(r"/\*(.*?)\*/\s*(?:#define[^\n]*\n\s*)?((?:int|const char \*)[^;]*;\s*)+",
+                         text, re.S):
+        for name in re.findall(r"(dq_\w+)\s*\(", m.group(0)[m.group(0).rfind("*/"):]):
+            blocks[name] = m.group(1)
+    return blocks
+
+
+def test_every_entry_point_cites_its_source():
+    # each declaration's comment names the passage it implements (the size
+    # queries among them)
+    blocks = _doc_blocks()
+    for name in declared_symbols():
+        if name in ("dq_status_string", "dq_last_error"):
+            continue
+        doc = blocks.get(name)
+        assert doc is not None, name
+        assert "Source" in doc or "as for dq_" in doc or "Runs the dq_qgemm kernel" in doc, name
+    for q in ("dq_packed_size", "dq_act_size", "dq_qgemm_rows_workspace"):
+        assert "Source" in blocks[q], q
+
+
 def test_status_strings(lib):
     assert lib.dq_status_string(dq.DQ_OK) == b"DQ_OK"
     assert lib.dq_status_string(dq.DQ_EWORKSPACE) == b"DQ_EWORKSPACE"

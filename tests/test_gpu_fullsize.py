@@ -1,12 +1,16 @@
-"""Parity at the workloads' full sizes, on sampled outputs.
+"""Parity at the workloads' full sizes: every output.
 
-Every GEMM of the LLaDA-8B (L = 160) and Dream-7B (L = 512) projection sets,
-and the gathered-row output projections (LLaDA vocab 126,464 at M = 1, 8, 32 of
-160 rows; Dream vocab 152,064 at M = 64 of 512 rows), run through the C ABI in
-the launch configuration the benchmark uses.  The quantizer is compared bit
-for bit on the whole activation; 1,024 sampled outputs per GEMM are compared
-with the oracle's f64 plain definition (|err| <= 1e-4 * T); every output must
-be finite.
+Every GEMM of the LLaDA-8B (L = 160) and Dream-7B (L = 512) projection sets
+in the form the benchmark runs them (Q/K/V stacked into one matrix, gate and
+up stacked into one matrix, O, down), and the gathered-row output projections
+(LLaDA vocab 126,464 at M = 1, 8, 32 of 160 rows; Dream vocab 152,064 at
+M = 64 of 512 rows), run through the C ABI in the launch configuration the
+benchmark uses.  The quantizer (or the fused RMSNorm producer) is compared bit
+for bit on the whole activation, and every output of every GEMM against the
+oracle's f64 plain definition (|err| <= 1e-4 * T), the oracle threaded over
+the host's cores.  Seeded random shapes over the launcher's regimes are
+checked on 4,096 random outputs plus one output in every (16-row block,
+16-column tile) pair, or in full where the oracle finishes in seconds.
 """
 import numpy as np
 import pytest
@@ -19,7 +23,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = 1e-4
-SAMPLES = 1024
+SAMPLES = 4096
+NAMES = ["q", "k", "v", "o", "gate", "up", "down"]
 
 
 @pytest.fixture(scope="module")
@@ -35,51 +40,76 @@ def _t(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def _full_check(type_, xq, xd, W, y, what):
+    N = y.shape[1]
+    assert np.all(np.isfinite(y)), what
+    yr, T = oracle.qgemm_ref(type_, xq, xd, W, N)
+    err = np.abs(y.astype(np.float64) - yr)
+    bad = err > TOL * T
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance, " \
+                          f"worst err/T {np.max(err / np.maximum(T, 1e-300)):.3g}"
+
+
 def _sampled_check(type_, xq, xd, W, y, seed, what):
+    """4,096 random outputs, the four corners, and one output in every
+    (16-row block, 16-column tile) pair."""
     M, N = y.shape
     rng = np.random.default_rng(seed)
-    mi = rng.integers(0, M, SAMPLES)
-    ni = rng.integers(0, N, SAMPLES)
-    mi[:4] = [0, M - 1, 0, M - 1]
-    ni[:4] = [0, N - 1, N - 1, 0]
+    mb, nt = (M + 15) // 16, (N + 15) // 16
+    bm, bn = np.meshgrid(np.arange(mb), np.arange(nt), indexing="ij")
+    tm = np.minimum(bm.ravel() * 16 + rng.integers(0, 16, bm.size), M - 1)
+    tn = np.minimum(bn.ravel() * 16 + rng.integers(0, 16, bn.size), N - 1)
+    mi = np.concatenate([[0, M - 1, 0, M - 1], rng.integers(0, M, SAMPLES), tm])
+    ni = np.concatenate([[0, N - 1, N - 1, 0], rng.integers(0, N, SAMPLES), tn])
     yr, T = oracle.qgemm_ref_points(type_, xq, xd, W, mi, ni)
     err = np.abs(y[mi, ni].astype(np.float64) - yr)
     assert np.all(np.isfinite(y)), what
     assert np.all(err <= TOL * T), f"{what}: worst err/T {np.max(err / T):.3g}"
 
 
-def _run_set(dq, layers, M, K_act, seed0):
-    x = synth.activations(np.random.default_rng(seed0), M, K_act)
+def _quantized(dq, M, K, seed):
+    x = synth.activations(np.random.default_rng(seed), M, K)
     xq, xd, xb = oracle.quantize_act(x)
     act = dq.quantize_act(_t(x))
-    q, d, b, padding_ok = act_layout.unpack(act.buf.cpu().numpy(), M, K_act)
+    q, d, b, padding_ok = act_layout.unpack(act.buf.cpu().numpy(), M, K)
     assert padding_ok
     assert np.array_equal(q, xq) and np.array_equal(b, xb)
-    assert np.array_equal(d, xd)
-    return x, (xq, xd, xb), act
+    assert np.array_equal(d.view(np.uint32), xd.view(np.uint32))
+    return xq, xd, act
 
 
-@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
-def test_llada_projection_full_size(dq, name):
-    proj = {p[0]: p for p in synth.llada_layer(1)}[name]  # layer 1: down is Q6_K
-    _, type_, N, K = proj
+def _stacked(layer_projs, config, layer, names):
+    return np.concatenate([synth.weights(np.random.default_rng(synth.seed(config, layer,
+                                                                          NAMES.index(n))),
+                                         layer_projs[n][1], layer_projs[n][2], layer_projs[n][3])
+                           for n in names])
+
+
+@pytest.mark.parametrize("which", ["qkv", "o", "down_q6k", "down_q4k"])
+def test_llada_projection_full_size(dq, which):
+    layer = 0 if which == "down_q4k" else 1  # layer 1: down is Q6_K
+    projs = {p[0]: p for p in synth.llada_layer(layer)}
     M = synth.LLADA["L"]
-    W = synth.weights(np.random.default_rng(synth.seed(1, 1, ["q", "k", "v", "o", "gate", "up",
-                                                              "down"].index(name))), type_, N, K)
-    _, (xq, xd, xb), act = _run_set(dq, None, M, K, 1000 + K)
+    if which == "qkv":
+        type_, K = oracle.Q4_K, projs["q"][3]
+        W = _stacked(projs, 1, layer, ["q", "k", "v"])
+    else:
+        name = "o" if which == "o" else "down"
+        _, type_, N, K = projs[name]
+        W = synth.weights(np.random.default_rng(synth.seed(1, layer, NAMES.index(name))),
+                          type_, N, K)
+    N = W.shape[0]
+    xq, xd, act = _quantized(dq, M, K, 1000 + K + layer)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
     y = dq.qgemm(type_, act, packed, N).cpu().numpy()
-    _sampled_check(type_, xq, xd, W, y, 7, f"LLaDA {name}")
+    _full_check(type_, xq, xd, W, y, f"LLaDA {which} {M}x{N}x{K}")
 
 
 def test_llada_stacked_gate_up_full_size(dq):
     # the benchmark's dominant GEMM: gate and up of a layer stacked into one 24576 x 4096 Q4_K
     # matrix, its input made by the RMSNorm producer
     projs = {p[0]: p for p in synth.llada_layer(0)}
-    names = ["q", "k", "v", "o", "gate", "up", "down"]
-    W = np.concatenate([synth.weights(np.random.default_rng(synth.seed(1, 0, names.index(n))),
-                                      projs[n][1], projs[n][2], projs[n][3])
-                        for n in ("gate", "up")])
+    W = _stacked(projs, 1, 0, ["gate", "up"])
     N, K = W.shape[0], projs["gate"][3]
     M = synth.LLADA["L"]
     x = synth.activations(np.random.default_rng(1100), M, K)
@@ -91,32 +121,26 @@ def test_llada_stacked_gate_up_full_size(dq):
     assert np.array_equal(d.view(np.uint32), xd.view(np.uint32))
     packed = dq.repack_weights(oracle.Q4_K, N, K, _t(W.reshape(-1)))
     y = dq.qgemm(oracle.Q4_K, act, packed, N).cpu().numpy()
-    _sampled_check(oracle.Q4_K, xq, xd, W, y, 11, "LLaDA stacked gate/up")
+    _full_check(oracle.Q4_K, xq, xd, W, y, "LLaDA stacked gate/up")
 
 
-def test_llada_q4k_down_full_size(dq):
-    # even layers: down is Q4_K (8-wave workgroups over 48 super-blocks)
-    _, type_, N, K = {p[0]: p for p in synth.llada_layer(0)}["down"]
-    assert type_ == oracle.Q4_K
-    M = synth.LLADA["L"]
-    W = synth.weights(np.random.default_rng(synth.seed(1, 0, 6)), type_, N, K)
-    _, (xq, xd, xb), act = _run_set(dq, None, M, K, 1200 + K)
-    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    y = dq.qgemm(type_, act, packed, N).cpu().numpy()
-    _sampled_check(type_, xq, xd, W, y, 12, "LLaDA down (Q4_K)")
-
-
-@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
-def test_dream_projection_full_size(dq, name):
-    proj = {p[0]: p for p in synth.dream_layer()}[name]
-    _, type_, N, K = proj
+@pytest.mark.parametrize("which", ["qkv", "o", "gate_up", "down"])
+def test_dream_projection_full_size(dq, which):
+    projs = {p[0]: p for p in synth.dream_layer()}
     M = synth.DREAM["L"]
-    W = synth.weights(np.random.default_rng(synth.seed(4, 0, ["q", "k", "v", "o", "gate", "up",
-                                                              "down"].index(name))), type_, N, K)
-    _, (xq, xd, xb), act = _run_set(dq, None, M, K, 4000 + K)
+    if which in ("qkv", "gate_up"):
+        names = ["q", "k", "v"] if which == "qkv" else ["gate", "up"]
+        type_, K = oracle.Q4_K, projs[names[0]][3]
+        W = _stacked(projs, 4, 0, names)
+    else:
+        _, type_, N, K = projs[which]
+        W = synth.weights(np.random.default_rng(synth.seed(4, 0, NAMES.index(which))),
+                          type_, N, K)
+    N = W.shape[0]
+    xq, xd, act = _quantized(dq, M, K, 4000 + K)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
     y = dq.qgemm(type_, act, packed, N).cpu().numpy()
-    _sampled_check(type_, xq, xd, W, y, 8, f"Dream {name}")
+    _full_check(type_, xq, xd, W, y, f"Dream {which} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("model,Ms", [("llada", (1, 8, 32)), ("dream", (64,))])
@@ -132,8 +156,9 @@ def test_logits_rows_full_size(dq, model, Ms):
         idx = synth.row_index(np.random.default_rng(100 + M), L, M)
         y, ws = dq.qgemm_rows(oracle.Q6_K, ct, _t(idx), packed, V)
         yn = y.cpu().numpy()
+        assert not ws[: 4 * M].view(torch.int32).cpu().numpy().any()
         gq, gd, _ = oracle.qgemm_rows_inputs(canvas, idx)
-        _sampled_check(oracle.Q6_K, gq, gd, W, yn, 9 + M, f"{model} logits M={M}")
+        _full_check(oracle.Q6_K, gq, gd, W, yn, f"{model} logits M={M}")
 
 
 def _random_shapes(count, seed):
@@ -157,11 +182,15 @@ def _random_shapes(count, seed):
 
 
 @pytest.mark.parametrize("type_,M,N,K", _random_shapes(12, 2024))
-def test_random_shapes_sampled(dq, type_, M, N, K):
+def test_random_shapes(dq, type_, M, N, K):
     W = synth.weights(np.random.default_rng(M * 7 + N), type_, N, K)
     x = synth.activations(np.random.default_rng(M + N), M, K)
     xq, xd, _ = oracle.quantize_act(x)
     act = dq.quantize_act(_t(x))
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
     y = dq.qgemm(type_, act, packed, N).cpu().numpy()
-    _sampled_check(type_, xq, xd, W, y, 13, f"type {type_} {M}x{N}x{K}")
+    what = f"type {type_} {M}x{N}x{K}"
+    if M * N * K <= 4_000_000_000:
+        _full_check(type_, xq, xd, W, y, what)
+    else:
+        _sampled_check(type_, xq, xd, W, y, 13, what)

@@ -17,8 +17,10 @@ dq_qgemm_rows_sample (the statistics formed in the projection's epilogue):
   * at the output projection's real shapes (126,464 x 4096 on 1, 8, 32 rows;
     152,064 x 3584 on 64 rows), against the logits dq_qgemm_rows writes for
     the same arguments (the two share the GEMM's accumulation, so the token
-    and maximum must agree bit for bit); those logits are themselves checked
-    against the oracle on sampled outputs in test_gpu_parity;
+    and maximum must agree bit for bit), and on sampled rows against the
+    oracle's f64 logits within the bounds above;
+  * an index outside [0, L) at one row (the in-GEMM gather): flagged, the row
+    taken as zeros, so its statistics are those of N equal logits;
   * edge cases: a single row, duplicate and unsorted indices, ties at the
     maximum (the first column wins), flat and peaked temperatures.
 """
@@ -169,7 +171,6 @@ def test_rows_sample_matches_rows_logits_at_full_size(dq, type_, L, M, N, K, bet
     canvas = synth.activations(rng, L, K)
     idx = synth.row_index(rng, L, M)
     packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
-    del W
     c, i = _t(canvas), _t(idx)
     y, _ = dq.qgemm_rows(type_, c, i, packed, N)
     tok, st, _ = dq.qgemm_rows_sample(type_, c, i, packed, N, beta)
@@ -178,6 +179,11 @@ def test_rows_sample_matches_rows_logits_at_full_size(dq, type_, L, M, N, K, bet
     tok, st = tok.cpu().numpy(), st.cpu().numpy().astype(np.float64)
     tok_r, st_r = oracle.logits_stats(yb.astype(np.float64), 1.0)
     _check_exact_inputs(tok, st, tok_r, st_r, f"{M}x{N}x{K}")
+    # and against the oracle's own f64 logits of sampled rows (first, last, one more)
+    rows = np.unique([0, M - 1, int(rng.integers(0, M))])
+    gq, gd, _ = oracle.qgemm_rows_inputs(canvas, idx[rows])
+    y_ref, T = oracle.qgemm_ref(type_, gq, gd, W, N)
+    _check_against_reference(tok[rows], st[rows], y_ref, T, beta, f"{M}x{N}x{K} rows {rows}")
 
 
 def test_rows_sample_tie_goes_to_first_column(dq):
@@ -204,3 +210,23 @@ def test_rows_sample_tie_goes_to_first_column(dq):
         tok, st = tok.cpu().numpy(), st.cpu().numpy()
         assert tok[0] == min(p, t), (p, t, tok[0])
         assert st[0, 0] == st0[0, 0]
+
+
+@pytest.mark.parametrize("bad", [160, -1])
+def test_rows_sample_single_row_out_of_range_index(dq, bad):
+    # one row over a wide vocabulary takes the single-row kernel, which gathers and
+    # quantizes the row itself: an index outside [0, L) is flagged and the row is
+    # zeros, so every logit is 0 (token 0, max 0, lse = entropy = log N, p = 1/N)
+    L, K, N = 160, 4096, 126464
+    W = synth.q6k_weights(np.random.default_rng(31), N, K)
+    canvas = synth.activations(np.random.default_rng(32), L, K)
+    packed = dq.repack_weights(oracle.Q6_K, N, K, _t(W.reshape(-1)))
+    tok, st, ws = dq.qgemm_rows_sample(oracle.Q6_K, _t(canvas), _t(np.array([bad], np.int32)),
+                                       packed, N, 0.7)
+    torch.cuda.synchronize()
+    assert ws[:4].view(torch.int32).cpu().numpy()[0] == 1
+    tok, st = tok.cpu().numpy(), st.cpu().numpy().astype(np.float64)
+    assert tok[0] == 0 and st[0, 0] == 0.0
+    logn = np.log(N)
+    assert abs(st[0, 1] - logn) <= SUM_TOL * logn and abs(st[0, 2] - logn) <= SUM_TOL * logn
+    assert abs(st[0, 3] * N - 1.0) <= SUM_TOL
