@@ -13,7 +13,8 @@
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
  *     allocates nothing and is safe to call from several host threads.  Its
  *     only state: a per-device cache of the compute-unit and XCD counts the
- *     launchers size their grids by (queried on the first call on a device).
+ *     launchers size their grids by (queried on the first call on a device),
+ *     and the device address of dq_qgemm_rows_noalloc's built-in array.
  *   - Every call only validates its arguments on the host and enqueues work on
  *     `stream`; it returns before the work runs.  Results are visible after
  *     the caller synchronizes the stream.
@@ -249,6 +250,34 @@ int dq_qgemm_rows_workspace(int64_t M, int64_t K, size_t *bytes);
 int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const float *canvas,
                   int64_t ldc, const int32_t *idx, const void *packed, float *y, int64_t ldy,
                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_qgemm_rows_noalloc -- dq_qgemm_rows without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The call itself
+ * allocates nothing: the gathered rows' quantized activations (and, when
+ * flags is NULL, the index flags) go to a device array built into the library,
+ * DQ_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held from the first call
+ * on that GPU until the process ends.  Its device address is looked up on the
+ * first call on each device (with that device current).
+ *   Arguments and results as for dq_qgemm_rows, except:
+ *   flags  : optional device int32 [M], 4-byte aligned: flags[i] = 1 if idx[i]
+ *            is outside [0, L), else 0.  NULL keeps them in the array.
+ *   stream : must belong to the current device (else DQ_EINVAL).
+ * Limits: 256 * ceil(M*4/256) (without flags) + ceil(M/16) * (K/256) * 5120
+ * bytes must fit in DQ_NOALLOC_SCRATCH_BYTES (e.g. M <= 64 at K <= 51200, or
+ * M <= 256 at K <= 12800); larger calls return DQ_EWORKSPACE and enqueue
+ * nothing.  Every call on a GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (different streams, or host threads without ordering) race
+ * and give undefined results.  Each call overwrites the parts it uses before
+ * reading them, so nothing needs clearing between calls.
+ * Errors: as dq_qgemm_rows; DQ_EWORKSPACE for sizes beyond the array.
+ * ------------------------------------------------------------------------ */
+#define DQ_NOALLOC_SCRATCH_BYTES 4194304u
+int dq_qgemm_rows_noalloc(int type, int64_t L, int64_t M, int64_t N, int64_t K,
+                          const float *canvas, int64_t ldc, const int32_t *idx,
+                          const void *packed, float *y, int64_t ldy, int32_t *flags,
+                          hipStream_t stream);
 
 /* --------------------------------------------------------------------------
  * Sampler statistics of requested rows of logits.

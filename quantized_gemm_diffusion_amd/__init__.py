@@ -8,7 +8,8 @@ the current stream; tensors must live on a GPU.
 
 Names follow the C ABI:
   packed_size, repack_weights, act_size, quantize_act, swiglu_quantize_act,
-  rmsnorm_quantize_act, qgemm, qgemm_rows_workspace, qgemm_rows, debug_superblock_sums, ...
+  rmsnorm_quantize_act, qgemm, qgemm_rows_workspace, qgemm_rows, qgemm_rows_noalloc,
+  debug_superblock_sums, ...
 Quantized activations travel as an ``Act`` (the device buffer in the record
 layout that include/dq.h documents, with its M and K).
 """
@@ -32,7 +33,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdq.so")
 
 EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_weights",
            "dq_act_size", "dq_quantize_act", "dq_swiglu_quantize_act", "dq_rmsnorm_quantize_act",
-           "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_logits_stats_workspace",
+           "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_qgemm_rows_noalloc",
+           "dq_logits_stats_workspace",
            "dq_logits_stats", "dq_qgemm_rows_sample_workspace", "dq_qgemm_rows_sample",
            "dq_attention_workspace", "dq_attention", "dq_row_bytes", "dq_embed_rows",
            "dq_debug_superblock_sums")
@@ -81,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
             "dq_qgemm_rows_workspace": [i64, i64, psz],
             "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
+            "dq_qgemm_rows_noalloc": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp],
             "dq_logits_stats_workspace": [i64, i64, psz],
             "dq_logits_stats": [i64, i64, vp, i64, ctypes.c_float, vp, vp, vp, sz, vp],
             "dq_qgemm_rows_sample_workspace": [i64, i64, i64, psz],
@@ -273,6 +276,38 @@ def qgemm_rows(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packed: torc
                              y.stride(0) if M > 1 else N, _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(canvas)), "dq_qgemm_rows")
     return y, ws
+
+
+NOALLOC_SCRATCH_BYTES = 4194304  # DQ_NOALLOC_SCRATCH_BYTES
+
+
+def qgemm_rows_noalloc(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packed: torch.Tensor,
+                       N: int, y: torch.Tensor, flags: torch.Tensor | None = None):
+    """qgemm_rows with the workspace in the library's built-in device array
+    (dq_qgemm_rows_noalloc): y [M, >=N] f32 and the optional flags [M] int32
+    are caller memory; the call itself allocates nothing."""
+    lib = load_library()
+    _need(canvas, torch.float32, "canvas")
+    _need(idx, torch.int32, "idx")
+    _need(y, torch.float32, "y")
+    _need(packed, torch.uint8, "packed")
+    if canvas.dim() != 2 or canvas.stride(1) != 1:
+        raise ValueError("canvas must be 2-D with unit column stride")
+    L, K = canvas.shape
+    M = idx.numel()
+    if not idx.is_contiguous():
+        raise ValueError("idx must be contiguous")
+    if y.dim() != 2 or y.shape[0] != M or y.shape[1] < N or y.stride(1) != 1:
+        raise ValueError("y must be [M, >=N] with unit column stride")
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
+        if flags.numel() < M or not flags.is_contiguous():
+            raise ValueError("flags must be a contiguous int32 tensor of at least M entries")
+    _check(lib.dq_qgemm_rows_noalloc(type_, L, M, N, K, _ptr(canvas),
+                                     canvas.stride(0) if L > 1 else K, _ptr(idx), _ptr(packed),
+                                     _ptr(y), y.stride(0) if M > 1 else N, _ptr(flags),
+                                     _stream(canvas)), "dq_qgemm_rows_noalloc")
+    return y
 
 
 def _stats_out(M: int, token, stats, dev):

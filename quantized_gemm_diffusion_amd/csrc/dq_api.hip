@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dq.h"
 #include "attention.h"
 #include "dq_internal.h"
@@ -264,6 +266,64 @@ int dq_qgemm_rows(int type, int64_t L, int64_t M, int64_t N, int64_t K, const fl
   return rows_launch(type, L, M, N, K, canvas, ldc, idx, packed, y, ldy,
                      reinterpret_cast<int32_t *>(w), w + rows_ws_flags(M), stream,
                      "dq_qgemm_rows");
+}
+
+// ---------------------------------------------------------------------------
+// dq_qgemm_rows_noalloc: the gathered-row projection with its workspace in a
+// file-scope device array (one copy per GPU, held until the process ends)
+// instead of caller memory.  The array's name is a host-side stand-in; its
+// device address is looked up once per device, with that device current, and
+// only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[DQ_NOALLOC_SCRATCH_BYTES];
+
+static int scratch_address(hipStream_t stream, uint8_t **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DQ_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DQ_EHIP, "device %d out of range", dev);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(DQ_EHIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if ((int)sdev != dev)
+      return fail(DQ_EINVAL, "stream belongs to device %d, the current device is %d", (int)sdev,
+                  dev);
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DQ_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = static_cast<uint8_t *>(addr[dev]);
+  return DQ_OK;
+}
+
+int dq_qgemm_rows_noalloc(int type, int64_t L, int64_t M, int64_t N, int64_t K,
+                          const float *canvas, int64_t ldc, const int32_t *idx,
+                          const void *packed, float *y, int64_t ldy, int32_t *flags,
+                          hipStream_t stream) {
+  bool noop = true;
+  if (int s = check_rows(type, L, M, N, K, canvas, ldc, idx, packed, y, ldy, &noop)) return s;
+  if (noop) return ok();
+  if (flags && !aligned(flags, 4)) return fail(DQ_EINVAL, "flags must be 4-byte aligned");
+  size_t act = 0;
+  if (int s = act_bytes(M, K, &act)) return s;
+  const size_t fbytes = flags ? 0 : rows_ws_flags(M);
+  if (fbytes + act > (size_t)DQ_NOALLOC_SCRATCH_BYTES)
+    return fail(DQ_EWORKSPACE,
+                "M = %lld rows of K = %lld need %zu bytes of scratch, more than the %u built in",
+                (long long)M, (long long)K, fbytes + act, (unsigned)DQ_NOALLOC_SCRATCH_BYTES);
+  uint8_t *w = nullptr;
+  if (int s = scratch_address(stream, &w)) return s;
+  int32_t *f = flags ? flags : reinterpret_cast<int32_t *>(w);
+  return rows_launch(type, L, M, N, K, canvas, ldc, idx, packed, y, ldy, f, w + fbytes, stream,
+                     "dq_qgemm_rows_noalloc");
 }
 
 static int check_beta(float beta) {
