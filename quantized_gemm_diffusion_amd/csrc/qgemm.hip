@@ -624,6 +624,258 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
 }
 
 // ---------------------------------------------------------------------------
+// Canvas GEMM with one n-tile per wave and shared activation records.
+//
+// Every wave of a workgroup owns one 16-column n-tile and a contiguous range of
+// super-blocks (its K-part), and runs all MB m-blocks of the workgroup's row
+// group against that tile: acc[MB] f32x4, one digit set and one fragment keep
+// a wave within 168 registers, so three waves share each SIMD and one wave's
+// fold and digit work issues while another's MFMAs run.  The NTW waves of a
+// K-part read the same activation records, so each record is copied into LDS
+// once for all of them: the K-part's ring holds two phases of P steps, and
+// the workgroup crosses one barrier per phase.
+//   step s of a K-part: record (super-block sb0 + s / MB, m-block mb0 + s % MB)
+//   phase ph          : steps ph*P .. ph*P + P - 1, read from ring half ph & 1
+// At the start of phase ph (just after the barrier that ends phase ph - 1)
+// the records of phase ph + 1 are copied into the other half, which every
+// wave finished reading in phase ph - 1; P of the K-part's waves each copy
+// one record (five 1 KB buffer-to-LDS loads).  Each wave's weight tile goes
+// into its own LDS slot the same way: the next super-block's tile is copied
+// in the super-block's first phase, once this super-block's digits have
+// read the slot, and only the phase that ends the super-block waits for it.
+// Each phase ends with every wave waiting for its own loads and the barrier,
+// so the records of phase ph + 1 are complete before any wave reads them.
+// Column groups visit their K-parts' super-blocks in rotated order, so the
+// workgroups running at once copy different records.  K-parts are balanced
+// to within one super-block; every wave crosses the same barriers, whether
+// or not its K-part has steps left.  At the end the KS partial sums of each
+// output are added in K-part order through LDS and stored with 16-byte row
+// segments.
+template <int MB_, int NTW_, int KS_, int P_>
+struct RingShape {
+  static constexpr int MB = MB_, NTW = NTW_, KS = KS_, P = P_, WAVES = NTW_ * KS_;
+};
+
+template <bool Q6, class RS>
+constexpr int ring_bytes() {
+  return RS::KS * 2 * RS::P * SLAB + RS::WAVES * wslot_bytes<Q6>();
+}
+template <class RS>
+constexpr int ring_red_bytes() {
+  return RS::WAVES * RS::MB * 4 * 64 * 4;
+}
+template <bool Q6, class RS>
+constexpr int ring_lds_bytes() {
+  return ring_bytes<Q6, RS>() > ring_red_bytes<RS>() ? ring_bytes<Q6, RS>() : ring_red_bytes<RS>();
+}
+
+// End of a phase: this wave's loads other than the newest N have landed and
+// its LDS reads are done; then every wave of the workgroup meets.
+template <int N>
+__device__ inline void phase_barrier() {
+  wait_vm<N>();
+  wait_lds();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int TYPE, class RS, int MODE>
+__global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_kernel(
+    int M, int64_t N, int nb, const uint8_t *__restrict__ qa, uint32_t qa_bytes,
+    const uint8_t *__restrict__ packed, float *__restrict__ y, int64_t ldy, int y_vec,
+    int32_t *__restrict__ dbg_S, int32_t *__restrict__ dbg_Mn, int xcds) {
+  constexpr bool Q6 = TYPE == 14;
+  constexpr bool DEBUG = MODE == 2;
+  constexpr int MB = RS::MB, NTW = RS::NTW, KS = RS::KS, P = RS::P, HP = MB / P;
+  constexpr int TB = Q6 ? Q6K_TILE : Q4K_TILE;
+  constexpr int GW = dma_per_tile<Q6>();
+  static_assert(MB % P == 0 && P <= NTW, "phases split super-blocks; one record per wave");
+  static_assert(ring_lds_bytes<Q6, RS>() * (12 / RS::WAVES) <= 160 * 1024, "LDS per CU");
+  using Raw = typename std::conditional<Q6, RawQ6, RawQ4>::type;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring_lds_bytes<Q6, RS>()];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int kp = wave / NTW, tw = wave - kp * NTW;  // K-part and tile of this wave
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  const int nmb = (M + MBLK - 1) / MBLK;
+  int cg, rg;
+  place((int)blockIdx.x, (int)((ntiles + NTW - 1) / NTW), (nmb + MB - 1) / MB, xcds, cg, rg);
+  const int64_t tile = (int64_t)cg * NTW + tw;
+  const int64_t tile_c = tile < ntiles ? tile : ntiles - 1;  // past the last: repeat it, store nothing
+  const int mb0 = rg * MB;
+  const int sb0 = kp * nb / KS, nsb = (kp + 1) * nb / KS - sb0;  // this K-part's super-blocks
+  const int nsb_max = (nb + KS - 1) / KS;                           // the longest K-part's
+  const int steps = nsb * MB;
+  // Column groups start their K-parts at different super-blocks, so the
+  // workgroups running at the same time copy different records.
+  const int rot = nsb > 0 ? cg % nsb : 0;
+  auto sb_of = [&](int sbi) { return sb0 + (sbi + rot < nsb ? sbi + rot : sbi + rot - nsb); };
+
+  uint8_t *ring = lds + kp * (2 * P * SLAB);
+  uint8_t *wslot = lds + KS * 2 * P * SLAB + wave * wslot_bytes<Q6>();
+  const uint32_t ring_a = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
+  const uint32_t wslot_a = (uint32_t)(uintptr_t)(lds_ptr_t)wslot;
+  const i32x4 dqa = desc(qa, qa_bytes);
+  const i32x4 dw = desc(packed + tile_c * nb * TB, (uint32_t)(nb * TB));
+  int frag[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) frag[c] = col * QK + 16 * ((4 * kq + c) ^ col);
+
+  // records of phase ph of this K-part (ring half ph & 1): wave tw copies
+  // step ph * P + tw
+  auto issue_phase = [&](int ph) {
+    const int s = ph * P + tw;
+    if (tw < P && s < steps) {
+      const int sbi = s / MB, t = s - sbi * MB;
+      const int mb = mb0 + t < nmb ? mb0 + t : nmb - 1;  // past the last m-block: repeat it
+      dma_record(dqa, ring_a + ((ph & 1) * P + tw) * SLAB, (sb_of(sbi) * nmb + mb) * ACT_RECORD,
+                 lane);
+    }
+  };
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int t = 0; t < MB; ++t) acc[t] = f32x4{};
+  Digits Dg;
+  if (steps > 0) dma_tile<Q6>(dw, wslot_a, sb_of(0) * TB, lane);
+  issue_phase(0);
+  phase_barrier<0>();
+
+  for (int sbi = 0; sbi < nsb_max; ++sbi) {
+    const bool active = sbi < nsb;
+    const bool wnext = sbi + 1 < nsb;
+#pragma unroll
+    for (int h = 0; h < HP; ++h) {
+      const int ph = sbi * HP + h;
+      if (h == 0 && active) {
+        Raw w;
+        read_w(wslot, lane, col, kq, w);
+        make_digits(w, kq, Dg);
+      }
+      // the other ring half was read in phase ph - 1, which every wave has
+      // finished; the weight slot is refilled with the next super-block's
+      // tile once its reads above are done, and only the phase that ends
+      // the super-block waits for it
+      issue_phase(ph + 1);
+      if (h == 0 && wnext) {
+        wait_lds();
+        dma_tile<Q6>(dw, wslot_a, sb_of(sbi + 1) * TB, lane);
+      }
+      if (active) {
+        const uint8_t *half = ring + (ph & 1) * (P * SLAB);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const int t = h * P + i;
+          Frag f;
+          read_frag<Q6>(half + i * SLAB, frag, col, kq, f);
+          StepOut o;
+          step_mfma<Q6>(f, Dg, o);
+          if (DEBUG)
+            step_debug<Q6>(o, (int64_t)(mb0 + t) * MBLK, kq, tile * TILE_N + col, M,
+                           tile < ntiles ? N : 0, nb, sb_of(sbi), dbg_S, dbg_Mn);
+          else
+            step_fold<Q6>(o, f.x4, Dg.dw, Dg.dmw, acc[t]);
+        }
+      }
+      // the records of phase ph + 1 have landed once at most the tile
+      // copies issued after them are outstanding
+      if (h < HP - 1 && wnext)
+        phase_barrier<GW>();
+      else
+        phase_barrier<0>();
+    }
+  }
+  if (DEBUG) return;
+
+  // Every wave stores its partial sums (the ring is no longer read: the last
+  // phase ended with a barrier); wave (kp, tw) then adds the KS partials of
+  // tile tw, in K-part order, for m-blocks t = kp, kp + KS, ..., and stores
+  // them.  Lane L takes row r = 4 * ((L >> 2) & 3) + (L >> 4) and columns
+  // 4 * (L & 3) .. +3 of the tile.
+  float *red = reinterpret_cast<float *>(lds);
+  {
+    float *dst = red + wave * (MB * 4 * 64);
+#pragma unroll
+    for (int t = 0; t < MB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(t * 4 + i) * 64 + lane] = acc[t][i];
+  }
+  __syncthreads();
+  const int ri = lane >> 4, rq = (lane >> 2) & 3, c0 = 4 * (lane & 3);
+  const int r = 4 * rq + ri;
+  const int64_t n0 = tile * TILE_N + c0;
+  for (int t = kp; t < MB; t += KS) {
+    const int row = (mb0 + t) * MBLK + r;
+    const float *src = red + tw * (MB * 4 * 64) + (t * 4 + ri) * 64 + 16 * rq + c0;
+    f32x4 v = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+    for (int k = 1; k < KS; ++k) v += *reinterpret_cast<const f32x4 *>(src + k * NTW * (MB * 4 * 64));
+    if (tile >= ntiles || row >= M || n0 >= N) continue;
+    float *yp = y + (int64_t)row * ldy + n0;
+    if (y_vec && n0 + 3 < N) {
+      *reinterpret_cast<f32x4 *>(yp) = v;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (n0 + c < N) yp[c] = v[c];
+    }
+  }
+}
+
+template <int TYPE, class RS>
+hipError_t launch_ring(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
+                       const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
+                       int32_t *dbg_Mn, hipStream_t stream) {
+  const int64_t nmb = (M + MBLK - 1) / MBLK;
+  const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
+  dim3 grid((unsigned)(((ntiles + RS::NTW - 1) / RS::NTW) * ((nmb + RS::MB - 1) / RS::MB)));
+  dim3 block(64 * RS::WAVES);
+  const uint32_t qa_bytes = (uint32_t)(nmb * nb * ACT_RECORD);
+  const int y_vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);
+  if (mode == 2)
+    hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 2>), grid, block, 0, stream, (int)M, N, nb,
+                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
+  else
+    hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 0>), grid, block, 0, stream, (int)M, N, nb,
+                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
+  return hipGetLastError();
+}
+
+// Shapes of the shared-record kernel: 160 rows (10 m-blocks) in two K-parts,
+// 128 rows (8 m-blocks) in two K-parts, 80 rows (5 m-blocks) in two K-parts;
+// six n-tiles per K-part, twelve waves per workgroup.
+using RingA = RingShape<10, 6, 2, 5>;
+using RingB = RingShape<8, 6, 2, 4>;
+using RingC = RingShape<5, 6, 2, 5>;
+
+// The shared-record kernel runs one workgroup per CU for the whole launch,
+// so it is taken where its grid makes one round that fills at least 70% of
+// the CUs (more rounds measured slower than the two-workgroup-per-CU canvas
+// kernel), with at most one padded m-block per row group and at least four
+// super-blocks per K-part pair.  Measured on MI355X against the canvas
+// kernel on the same device: LLaDA-8B's stacked gate/up (160 x 24576 x 4096,
+// 256 workgroups of RingA) 2% and stacked Q/K/V (160 x 12288 x 4096, 256 of
+// RingC) 4% faster, Dream-7B's stacked Q/K/V (512 x 4608 x 3584, 192 of
+// RingB) 12% faster.  Returns 0 (none), 1 (RingA), 2 (RingB) or 3 (RingC).
+inline int ring_pick(int64_t M, int64_t N, int nb) {
+  if (nb < 4) return 0;
+  const int64_t nmb = (M + MBLK - 1) / MBLK, ntiles = (N + TILE_N - 1) / TILE_N;
+  const int64_t cus = device_props().cus;
+  const int mbs[3] = {RingA::MB, RingB::MB, RingC::MB};
+  for (int i = 0; i < 3; ++i) {
+    const int mb = mbs[i];
+    if (nmb < mb) continue;
+    const int64_t rgs = (nmb + mb - 1) / mb;
+    if (rgs * mb - nmb > 1) continue;
+    const int64_t wgs = (ntiles + 5) / 6 * rgs;
+    if (wgs <= cus && 10 * wgs >= 7 * cus) return i + 1;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
 // Narrow M (at most 32 rows, K of 8 to 16 super-blocks in pairs): the weight
 // stream is the whole cost (the output projection on the requested rows moves
 // 425 MB of weights for 32 rows), so the operands switch roles.  One
@@ -1445,6 +1697,18 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
                  : launch_narrow<12, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
     return two ? launch_narrow<14, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
                : launch_narrow<14, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
+  }
+  switch (mode == 0 || mode == 2 ? ring_pick(M, N, nb) : 0) {
+    case 1:
+      return type == 12 ? launch_ring<12, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
+                        : launch_ring<14, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+    case 2:
+      return type == 12 ? launch_ring<12, RingB>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
+                        : launch_ring<14, RingB>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+    case 3:
+      return type == 12 ? launch_ring<12, RingC>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
+                        : launch_ring<14, RingC>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+    default: break;
   }
   Extra x;
   x.dbg_S = dbg_S;
