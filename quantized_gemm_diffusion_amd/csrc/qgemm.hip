@@ -398,8 +398,8 @@ __device__ inline void place(int id, int ncg, int nrg, int xcds, int &cg, int &r
 // the whole reduction.  Wave w takes super-blocks b = w, w + WAVES, ...; it builds a
 // super-block's weight digits once per tile and runs the MB steps of that
 // super-block against them, each step reading its activation operands once
-// for all NT tiles.  The WAVES f32 partial sums are added in LDS (pairwise
-// tree, fixed order) at the end.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its
+// for all NT tiles.  The WAVES f32 partial sums are added through LDS at the
+// end, one after another in wave order.  MODE: 0 = canvas GEMM, 1 = gathered-row GEMM (same code, its
 // own symbol so profiles tell the two workloads apart), 2 = debug stores of
 // S and Mn, 3 = gathered-row GEMM whose output rows are folded into sampler
 // states (one per row per workgroup, at part[row * npart + column group])
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
 #pragma unroll
     for (int c = 0; c < 4; ++c) frag[c] = col * QK + 16 * ((4 * kq + c) ^ col);
 
-    // step s -> record of (super-block wave + 4 * (s / MB), block mb0 + s % MB);
+    // step s -> record of (super-block wave + WAVES * (s / MB), block mb0 + s % MB);
     // blocks past the last one re-load the last (their rows are never stored)
     auto issue_a = [&](int s, int slot) {
       s = s < S ? s : S - 1;
@@ -779,9 +779,11 @@ __global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_ker
             step_fold<Q6>(o, f.x4, Dg.dw, Dg.dmw, acc[t]);
         }
       }
-      // the records of phase ph + 1 have landed once at most the tile
-      // copies issued after them are outstanding
-      if (h < HP - 1 && wnext)
+      // the records of phase ph + 1 have landed once at most the loads
+      // issued after them are outstanding: in a super-block's first phase,
+      // the next tile's copies (unless this phase also ends the super-block,
+      // whose end must find the tile in place); in any later phase, none
+      if (h == 0 && HP > 1 && wnext)
         phase_barrier<GW>();
       else
         phase_barrier<0>();
