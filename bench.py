@@ -6,14 +6,16 @@ One timed step is one LLaDA-8B denoising step's GEMM work at canvas L = 160
 canvas, so the runtime is a stream of GEMMs; Architecture page, "A forward
 pass"): for each of 32 layers, 4 activation quantizations (RMSNorm fused in
 front of the one Q/K/V share and of the one gate/up share; O's input as is;
-SiLU(gate) * up fused in front of down's, taken straight from the gate/up
-GEMM's output) and the 7 projections Q, K, V, O (4096 x 4096
+down's input, SiLU(gate) * up, which the gate/up GEMM forms in its epilogue)
+and the 7 projections Q, K, V, O (4096 x 4096
 Q4_K), gate, up (12288 x 4096 Q4_K) and down (4096 x 12288; Q6_K on odd
 layers, Q4_K on even), then the output projection on 32 gathered canvas rows
 (126,464 x 4096 Q6_K).  Q, K and V read the same quantized input, so their
 weights are stacked at load time into one 12,288 x 4096 matrix and run as one
 GEMM (same bytes and operations, two launches fewer per layer); gate and up
-likewise share an input and run as one 24,576 x 4096 GEMM.  Every layer
+likewise share an input and run as one 24,576 x 4096 GEMM, their 16-row
+tiles interleaved so that each workgroup holds matching gate and up columns.
+Every layer
 has its own seeded weights (4.6 GB in all, far above the 256 MB last-level
 cache), resident in HBM before timing.
 
@@ -89,10 +91,6 @@ def norm_quant_bytes(M, K_):  # the row, the norm weights, the quantized record
     return quant_bytes(M, K_) + K_ * 4
 
 
-def swiglu_quant_bytes(M, F_):  # gate and up rows in, the quantized record out
-    return quant_bytes(M, F_) + M * F_ * 4
-
-
 def source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -166,8 +164,9 @@ def main():
     gammas = [{n: up((1.0 + 0.1 * norm_rng.standard_normal(K)).astype(np.float32))
                for n in ("qkv", "ffn")} for _ in range(LAYERS)]
     qbuf = {kk: torch.empty(dq.act_size(L, kk), dtype=torch.uint8, device=dev) for kk in (K, F)}
+    # the gate/up GEMM stores silu(gate) * up, L x F, in its epilogue
     outs = {name: torch.empty((L, N), dtype=torch.float32, device=dev)
-            for name, N in (("qkv", 3 * K), ("o", K), ("gateup", 2 * F), ("down", K))}
+            for name, N in (("qkv", 3 * K), ("o", K), ("gateup", F), ("down", K))}
     host_keep = {}
     packed = []
     for layer in range(LAYERS):
@@ -177,8 +176,10 @@ def main():
                                                   t, N, KK))
         # Q, K, V stacked along N: one 12288 x 4096 Q4_K matrix
         mats["qkv"] = (Q4_K, 3 * K, K, np.concatenate([mats.pop(n)[3] for n in "qkv"]))
-        # gate and up stacked along N: one 24576 x 4096 Q4_K matrix
-        mats["gateup"] = (Q4_K, 2 * F, K, np.concatenate([mats.pop(n)[3] for n in ("gate", "up")]))
+        # gate and up stacked along N with their 16-row tiles interleaved: one
+        # 24576 x 4096 Q4_K matrix, whose GEMM forms silu(gate) * up itself
+        gate_w, up_w = mats.pop("gate")[3], mats.pop("up")[3]
+        mats["gateup"] = (Q4_K, 2 * F, K, dq.interleave_gate_up(gate_w, up_w))
         lp = {}
         for name, (t, N, KK, W) in mats.items():
             if layer < args.cpu_layers:
@@ -217,11 +218,11 @@ def main():
                       "rmsnorm_quantize", 0, norm_quant_bytes(L, K)))
         return buf
 
-    def swiglu_quant():
-        gu = outs["gateup"]
+    def down_quant():
+        h = outs["gateup"]  # silu(gate) * up, from the gate/up GEMM's epilogue
         buf = qbuf[F]
-        calls.append((lib.dq_swiglu_quantize_act, (L, F, gu.data_ptr(), 2 * F, buf.data_ptr()),
-                      "swiglu_quantize", 0, swiglu_quant_bytes(L, F)))
+        calls.append((lib.dq_quantize_act, (L, F, h.data_ptr(), F, buf.data_ptr()),
+                      "quantize_down", 0, quant_bytes(L, F)))
         return buf
 
     def gemm(lp, name, buf):
@@ -229,6 +230,11 @@ def main():
         y = outs[name]
         # one kind per GEMM shape: each kind is one kernel in a profile
         kind = f"qgemm_{'q4k' if t == Q4_K else 'q6k'}_{L}x{N}x{kk}"
+        if name == "gateup":  # stores silu(gate) * up: N/2 outputs per row
+            calls.append((lib.dq_qgemm_swiglu,
+                          (t, L, N // 2, kk, buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N // 2),
+                          kind, 2 * L * N * kk, gemm_bytes(t, L, N, kk) - L * (N // 2) * 4))
+            return
         calls.append((lib.dq_qgemm, (t, L, N, kk, buf.data_ptr(), pk.data_ptr(), y.data_ptr(), N),
                       kind, 2 * L * N * kk, gemm_bytes(t, L, N, kk)))
 
@@ -236,7 +242,7 @@ def main():
         gemm(lp, "qkv", norm_quant(li, "qkv"))
         gemm(lp, "o", quant("o"))
         gemm(lp, "gateup", norm_quant(li, "ffn"))
-        gemm(lp, "down", swiglu_quant())
+        gemm(lp, "down", down_quant())
     # gathered f32 rows and the index list stand in for pre-quantized activations
     rows_bytes = V * (K // 256) * BLOCK[Q6_K] + ROWS * K * 4 + ROWS * 4 + ROWS * V * 4
     calls.append((lib.dq_qgemm_rows,
@@ -380,11 +386,11 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "LLaDA-8B denoising step at canvas L=160: 32 layers x (4 int8 "
-                               "activation quantizations, two fused with RMSNorm and one with "
-                               "SwiGLU on the gate/up output + Q/K/V/O 4096x4096, gate/up "
-                               "12288x4096, down 4096x12288 K-quant GEMMs; down Q6_K on odd "
-                               "layers, Q4_K on even) + output projection on 32 of 160 "
-                               "gathered rows, 126464x4096 Q6_K",
+                               "activation quantizations, two fused with RMSNorm + Q/K/V/O "
+                               "4096x4096, gate/up 12288x4096 (stacked, SiLU(gate)*up formed "
+                               "in the GEMM's epilogue), down 4096x12288 K-quant GEMMs; down "
+                               "Q6_K on odd layers, Q4_K on even) + output projection on 32 of "
+                               "160 gathered rows, 126464x4096 Q6_K",
                    "L": L, "K": K, "ffn": F, "vocab": V, "layers": LAYERS, "rows": ROWS,
                    "step_GOP": round(step_ops / 1e9, 2),
                    "step_algorithmic_MB": round(step_bytes / 1e6, 1)},
@@ -747,8 +753,9 @@ def cpu_baseline(args, host_keep, Wout, canvas_np, idx_np, acts, gammas):
             else:
                 q, d, b = oracle.swiglu_quantize_act(y_gu, F)
             y = oracle.qgemm_f32(t, q, d, b, W, N, threads=th)
-            if name == "gateup":
-                y_gu = y
+            if name == "gateup":  # interleaved 16-row tiles -> [gate | up]
+                yt = y.reshape(L, F // 16, 2, 16)
+                y_gu = np.concatenate([yt[:, :, 0].reshape(L, F), yt[:, :, 1].reshape(L, F)], 1)
             ops += 2 * L * N * KK
     nv = V // 4
     gq, gd, gb = oracle.qgemm_rows_inputs(canvas_np, idx_np)

@@ -218,6 +218,37 @@ int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const void *qa, const vo
              float *y, int64_t ldy, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * dq_qgemm_swiglu -- the stacked gate/up GEMM with the down projection's
+ * input formed in its epilogue: h[m][i] = silu(g[m][i]) * u[m][i], where g
+ * and u are the gate and up outputs, so the 2F-wide GEMM output is never
+ * stored.
+ *
+ * Source: Architecture page, "A forward pass", step 2 (gate and up read one
+ * quantized input; the FFN applies SiLU to gate and multiplies by up before
+ * down's quantization) and "Source map" (SwiGLU among the GPU kernels).
+ * The weight matrix is the 2F x K stack of gate and up with its 16-row tiles
+ * interleaved: rows 32i .. 32i+15 are gate rows 16i .. 16i+15 and rows
+ * 32i+16 .. 32i+31 are up rows 16i .. 16i+15 (the caller orders the GGUF rows
+ * so before dq_repack_weights; a load-time layout choice).  g and u are the
+ * f32 values dq_qgemm computes on that matrix, bit for bit, and
+ * silu(g) * u = (g / (1 + exp(-g))) * u follows dq_swiglu_quantize_act's
+ * binary32 steps exactly.  So dq_quantize_act(h) gives the codes, scales
+ * and sums that dq_swiglu_quantize_act gives on dq_qgemm's output rearranged
+ * to [gate | up].
+ *
+ *   qa     : the output of dq_quantize_act (or a fused producer) for M rows, K.
+ *   packed : output of dq_repack_weights for (type, 2F, K), tiles interleaved
+ *            as above.
+ *   F      : the FFN width, a multiple of 16.
+ *   h      : device f32, M rows, row stride ldh >= F; columns [0, F) of each
+ *            row are written, nothing else.
+ * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (F % 16, shape, ldh < F, NULL,
+ *         alignment), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_qgemm_swiglu(int type, int64_t M, int64_t F, int64_t K, const void *qa,
+                    const void *packed, float *h, int64_t ldh, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * dq_qgemm_rows_workspace -- workspace bytes dq_qgemm_rows needs for M
  * gathered rows of length K (host-only): the index flags, then the quantized
  * activations of the gathered rows.

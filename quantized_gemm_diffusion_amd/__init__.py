@@ -33,7 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdq.so")
 
 EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_weights",
            "dq_act_size", "dq_quantize_act", "dq_swiglu_quantize_act", "dq_rmsnorm_quantize_act",
-           "dq_qgemm", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_qgemm_rows_noalloc",
+           "dq_qgemm", "dq_qgemm_swiglu", "dq_qgemm_rows_workspace", "dq_qgemm_rows", "dq_qgemm_rows_noalloc",
            "dq_logits_stats_workspace",
            "dq_logits_stats", "dq_qgemm_rows_sample_workspace", "dq_qgemm_rows_sample",
            "dq_attention_workspace", "dq_attention", "dq_row_bytes", "dq_embed_rows",
@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dq_swiglu_quantize_act": [i64, i64, vp, i64, vp, vp],
             "dq_rmsnorm_quantize_act": [i64, i64, vp, i64, vp, ctypes.c_float, vp, vp],
             "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
+            "dq_qgemm_swiglu": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
             "dq_qgemm_rows_workspace": [i64, i64, psz],
             "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
             "dq_qgemm_rows_noalloc": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp],
@@ -238,6 +239,36 @@ def qgemm(type_: int, act: Act, packed: torch.Tensor, N: int,
     _check(lib.dq_qgemm(type_, M, N, K, _ptr(act.buf), _ptr(packed), _ptr(y),
                         y.stride(0) if M > 1 else N, _stream(act.buf)), "dq_qgemm")
     return y
+
+
+def qgemm_swiglu(type_: int, act: Act, packed: torch.Tensor, F: int,
+                 h: torch.Tensor | None = None) -> torch.Tensor:
+    """h [M, F] f32 = silu(gate) * up of the interleaved gate/up GEMM (dq.h)."""
+    lib = load_library()
+    M, K = _check_operands(type_, act, packed, 2 * F)
+    if h is None:
+        h = torch.empty((M, F), dtype=torch.float32, device=act.buf.device)
+    _need(h, torch.float32, "h")
+    if h.dim() != 2 or h.shape[0] != M or h.shape[1] < F or h.stride(1) != 1:
+        raise ValueError("h must be [M, >=F] with unit column stride")
+    _check(lib.dq_qgemm_swiglu(type_, M, F, K, _ptr(act.buf), _ptr(packed), _ptr(h),
+                               h.stride(0) if M > 1 else F, _stream(act.buf)), "dq_qgemm_swiglu")
+    return h
+
+
+def interleave_gate_up(gate, up, rows: int = 16):
+    """Stack gate and up (N = F rows each, any row type) with their 16-row
+    tiles interleaved, the weight order dq_qgemm_swiglu takes: rows 32i ..
+    32i+15 from gate, 32i+16 .. 32i+31 from up.  numpy or torch, along dim 0."""
+    F = gate.shape[0]
+    if up.shape != gate.shape or F % rows:
+        raise ValueError("gate and up must have the same shape and a multiple of 16 rows")
+    g = gate.reshape((F // rows, rows) + tuple(gate.shape[1:]))
+    u = up.reshape((F // rows, rows) + tuple(up.shape[1:]))
+    if isinstance(gate, torch.Tensor):
+        return torch.stack([g, u], 1).reshape((2 * F,) + tuple(gate.shape[1:]))
+    import numpy as _np
+    return _np.stack([g, u], 1).reshape((2 * F,) + tuple(gate.shape[1:]))
 
 
 def qgemm_rows_workspace(M: int, K: int) -> int:

@@ -199,6 +199,20 @@ int dq_qgemm(int type, int64_t M, int64_t N, int64_t K, const void *qa, const vo
                   "dq_qgemm");
 }
 
+int dq_qgemm_swiglu(int type, int64_t M, int64_t F, int64_t K, const void *qa,
+                    const void *packed, float *h, int64_t ldh, hipStream_t stream) {
+  if (F < 0 || F % 16 != 0 || F > kMaxRows / 2)
+    return fail(DQ_EINVAL, "F = %lld is not a multiple of 16 in range", (long long)F);
+  if (int s = check_gemm(type, M, 2 * F, K, qa, packed)) return s;
+  if (ldh < F) return fail(DQ_EINVAL, "ldh = %lld < F = %lld", (long long)ldh, (long long)F);
+  if (M == 0 || F == 0) return ok();
+  if (!h || !aligned(h, 4)) return fail(DQ_EINVAL, "h is NULL or not 4-byte aligned");
+  return launched(dq::launch_qgemm(type, 4, M, 2 * F, K, static_cast<const uint8_t *>(qa),
+                                   static_cast<const uint8_t *>(packed), h, ldh, nullptr, nullptr,
+                                   stream),
+                  "dq_qgemm_swiglu");
+}
+
 // Workspace: [flags int32 x M | pad to 256] [quantized-activation records]
 static size_t rows_ws_flags(int64_t M) { return ((size_t)M * 4 + 255) & ~(size_t)255; }
 

@@ -122,6 +122,37 @@ __device__ inline uint32_t pack4(const int (&c)[4]) {
 // The block's activation scale d_x.
 __device__ inline float block_dx(float amax) { return amax != 0.0f ? amax / 127.0f : 0.0f; }
 
+// exp as the SwiGLU producer defines it: clamp t to [-87, 88]; n = rint(t *
+// log2 e); r = (t - n*L1) - n*L2, where L1 + L2 = ln 2 and L1 has few enough
+// significant bits that n*L1 is exact (Cody and Waite's reduction); the
+// degree-7 Taylor polynomial of e^r (coefficients 1/k! in binary32) by
+// Horner; times 2^n, built exactly from its exponent bits.  Every step is
+// one binary32 operation, never contracted, so every kernel that includes
+// this computes the same bits.
+__device__ inline float dq_exp(float t) {
+#pragma clang fp contract(off)
+  t = fminf(fmaxf(t, -87.0f), 88.0f);
+  const float n = __builtin_rintf(t * 1.44269502f);
+  const float r = (t - n * 0.693145751953125f) - n * 1.42860677e-06f;
+  float p = 1.98412698e-04f;
+  p = p * r + 1.38888889e-03f;
+  p = p * r + 8.33333377e-03f;
+  p = p * r + 4.16666679e-02f;
+  p = p * r + 1.66666672e-01f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return p * __builtin_bit_cast(float, (uint32_t)((int)n + 127) << 23);
+}
+
+// silu(g) * u = (g / (1 + exp(-g))) * u, the down projection's input
+__device__ inline float silu_mul(float g, float u) {
+#pragma clang fp contract(off)
+  const float den = 1.0f + dq_exp(-g);
+  const float s = g / den;
+  return s * u;
+}
+
 // Compute units and XCDs (each with its own L2) of the current device, queried
 // once per device (device.hip); {256, 8} -- a whole MI355X -- if the query
 // fails.  The launchers size persistent grids and XCD-aware placements by it.
@@ -143,7 +174,9 @@ hipError_t launch_rmsnorm_quantize(int64_t M, int64_t K, const float *x, int64_t
                                    hipStream_t stream);
 hipError_t launch_repack(int type, int64_t N, int64_t K, const uint8_t *src, uint8_t *dst,
                          hipStream_t stream);
-// mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers.
+// mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers,
+// 4 canvas GEMM over interleaved gate/up tiles storing silu(gate) * up (y is
+// then M x N/2, row stride ldy).
 hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
                         const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
                         int32_t *dbg_Mn, hipStream_t stream);

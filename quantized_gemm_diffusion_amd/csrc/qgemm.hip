@@ -403,7 +403,9 @@ __device__ inline void place(int id, int ncg, int nrg, int xcds, int &cg, int &r
 // own symbol so profiles tell the two workloads apart), 2 = debug stores of
 // S and Mn, 3 = gathered-row GEMM whose output rows are folded into sampler
 // states (one per row per workgroup, at part[row * npart + column group])
-// instead of being stored.
+// instead of being stored, 4 = canvas GEMM over an interleaved gate/up
+// matrix (n-tiles 2i and 2i + 1 are gate and up tile i) that stores
+// silu(gate) * up, M x N/2, instead of the two tiles.
 //
 // Load schedule of one wave (every load is a buffer-to-LDS load, and loads
 // complete in issue order, so a wait for one load also waits for every older
@@ -600,6 +602,36 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
       st = stat_merge(st, stat_shfl_xor(st, 2));
       const int row = (mb0 + t) * MBLK + r;
       if ((lane & 3) == 0 && row < M) part[(int64_t)row * npart + cg] = stat_pack(st);
+    }
+    return;
+  }
+  if constexpr (MODE == 4) {
+    // the workgroup's two n-tiles are gate tile cg and up tile cg of an
+    // interleaved gate/up matrix: wave w takes m-blocks t = w, w + WAVES, ...,
+    // adds each tile's partials exactly as the plain store does, and stores
+    // silu(gate) * up at columns 16 cg + c0 .. +3 of the M x N/2 output
+    static_assert(NT == 2, "one gate/up tile pair per workgroup");
+    for (int t = wave; t < MB; t += WAVES) {
+      const int row = (mb0 + t) * MBLK + r;
+      const float *sg = red + ((t * NT) * 4 + ri) * 64 + 16 * rq + c0;
+      const float *su = red + ((t * NT + 1) * 4 + ri) * 64 + 16 * rq + c0;
+      f32x4 g = *reinterpret_cast<const f32x4 *>(sg);
+      f32x4 u = *reinterpret_cast<const f32x4 *>(su);
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) {
+        g += *reinterpret_cast<const f32x4 *>(sg + w * (PER * 64));
+        u += *reinterpret_cast<const f32x4 *>(su + w * (PER * 64));
+      }
+      if (nt0 + 1 >= ntiles || row >= M) continue;
+      const f32x4 h = {silu_mul(g[0], u[0]), silu_mul(g[1], u[1]), silu_mul(g[2], u[2]),
+                       silu_mul(g[3], u[3])};
+      float *yp = y + (int64_t)row * ldy + (int64_t)cg * TILE_N + c0;
+      if (y_vec) {
+        *reinterpret_cast<f32x4 *>(yp) = h;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) yp[c] = h[c];
+      }
     }
     return;
   }
@@ -807,6 +839,39 @@ __global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_ker
   __syncthreads();
   const int ri = lane >> 4, rq = (lane >> 2) & 3, c0 = 4 * (lane & 3);
   const int r = 4 * rq + ri;
+  if constexpr (MODE == 4) {
+    // tiles 2p and 2p + 1 of the workgroup are gate and up tile cg * NTW / 2
+    // + p of an interleaved gate/up matrix: the (pair, m-block) items are
+    // dealt to the waves in turn; each tile's KS partials are added exactly
+    // as the plain store adds them, then silu(gate) * up is stored
+    static_assert(NTW % 2 == 0, "whole gate/up tile pairs per workgroup");
+    constexpr int PAIRS = NTW / 2;
+    for (int item = wave; item < PAIRS * MB; item += RS::WAVES) {
+      const int pr = item / MB, t = item - pr * MB;
+      const int64_t tg = (int64_t)cg * NTW + 2 * pr;  // the pair's gate tile
+      const int row = (mb0 + t) * MBLK + r;
+      const float *sg = red + (2 * pr) * (MB * 4 * 64) + (t * 4 + ri) * 64 + 16 * rq + c0;
+      const float *su = sg + MB * 4 * 64;
+      f32x4 g = *reinterpret_cast<const f32x4 *>(sg);
+      f32x4 u = *reinterpret_cast<const f32x4 *>(su);
+#pragma unroll
+      for (int k = 1; k < KS; ++k) {
+        g += *reinterpret_cast<const f32x4 *>(sg + k * NTW * (MB * 4 * 64));
+        u += *reinterpret_cast<const f32x4 *>(su + k * NTW * (MB * 4 * 64));
+      }
+      if (tg + 1 >= ntiles || row >= M) continue;
+      const f32x4 h = {silu_mul(g[0], u[0]), silu_mul(g[1], u[1]), silu_mul(g[2], u[2]),
+                       silu_mul(g[3], u[3])};
+      float *yp = y + (int64_t)row * ldy + (tg / 2) * TILE_N + c0;
+      if (y_vec) {
+        *reinterpret_cast<f32x4 *>(yp) = h;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) yp[c] = h[c];
+      }
+    }
+    return;
+  }
   const int64_t n0 = tile * TILE_N + c0;
   for (int t = kp; t < MB; t += KS) {
     const int row = (mb0 + t) * MBLK + r;
@@ -838,6 +903,9 @@ hipError_t launch_ring(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
   const int y_vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);
   if (mode == 2)
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 2>), grid, block, 0, stream, (int)M, N, nb,
+                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
+  else if (mode == 4)
+    hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 4>), grid, block, 0, stream, (int)M, N, nb,
                        qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
   else
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 0>), grid, block, 0, stream, (int)M, N, nb,
@@ -1512,10 +1580,10 @@ hipError_t launch_rows4(int64_t M, int64_t N, int nb, const uint8_t *qa, const u
 // in pairs (2 per wave, at least 4 waves), enough n-tiles to give every CU a
 // stream, a row stride that keeps a 16-row block of y under 2 GB (its store
 // offsets are 32-bit, with the top bit marking a dropped store), and not the
-// debug mode.
+// debug or gate/up mode.
 inline bool use_narrow(int mode, int64_t M, int64_t N, int nb, int64_t ldy) {
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
-  return mode != 2 && M <= 2 * MBLK && nb % NW_KB == 0 && nb >= 4 * NW_KB &&
+  return mode != 2 && mode != 4 && M <= 2 * MBLK && nb % NW_KB == 0 && nb >= 4 * NW_KB &&
          nb <= NW_WAVES * NW_KB && ntiles >= 4 * device_props().cus && ldy <= (int64_t(1) << 25);
 }
 
@@ -1546,6 +1614,13 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
     case 1: DQ_LAUNCH(1); break;
     case 2: DQ_LAUNCH(2); break;
     case 3: DQ_LAUNCH(3); break;
+    case 4:
+      if constexpr (SH::NT == 2) {
+        DQ_LAUNCH(4);
+        break;
+      } else {
+        return hipErrorInvalidValue;  // the launcher gives mode 4 two tiles per wave
+      }
     default: DQ_LAUNCH(0); break;
   }
 #undef DQ_LAUNCH
@@ -1631,8 +1706,10 @@ inline Pick pick_shape(int type, int mode, int64_t M, int64_t N, int64_t nb) {
     pk = Pick{mb, 8, 2};
   // The sampler-state launch keeps two tiles per wave (one state per row per
   // 32-column group) but the same waves: each output element is then summed
-  // in the same order as the plain launch stores it, bit for bit.
-  if (mode == 3) pk.nt = 2;
+  // in the same order as the plain launch stores it, bit for bit.  So does
+  // the gate/up launch with silu(gate) * up in its epilogue (one gate/up tile
+  // pair per workgroup).
+  if (mode == 3 || mode == 4) pk.nt = 2;
   return pk;
 }
 
@@ -1700,7 +1777,7 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
     return two ? launch_narrow<14, 2>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream)
                : launch_narrow<14, 1>(M, N, nb, qa, packed, y, ldy, 0.0f, nullptr, stream);
   }
-  switch (mode == 0 || mode == 2 ? ring_pick(M, N, nb) : 0) {
+  switch (mode == 0 || mode == 2 || mode == 4 ? ring_pick(M, N, nb) : 0) {
     case 1:
       return type == 12 ? launch_ring<12, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
                         : launch_ring<14, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);

@@ -110,33 +110,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t M, int64_t Mpad, 
 }
 
 
-// exp as the SwiGLU producer defines it: clamp t to [-87, 88]; n = rint(t *
-// log2 e); r = (t - n*L1) - n*L2, where L1 + L2 = ln 2 and L1 has few enough
-// significant bits that n*L1 is exact (Cody and Waite's reduction); the
-// degree-7 Taylor polynomial of e^r (coefficients 1/k! in binary32) by
-// Horner; times 2^n, built exactly from its exponent bits.
-__device__ inline float dq_exp(float t) {
-  t = fminf(fmaxf(t, -87.0f), 88.0f);
-  const float n = __builtin_rintf(t * 1.44269502f);
-  const float r = (t - n * 0.693145751953125f) - n * 1.42860677e-06f;
-  float p = 1.98412698e-04f;
-  p = p * r + 1.38888889e-03f;
-  p = p * r + 8.33333377e-03f;
-  p = p * r + 4.16666679e-02f;
-  p = p * r + 1.66666672e-01f;
-  p = p * r + 0.5f;
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  return p * __builtin_bit_cast(float, (uint32_t)((int)n + 127) << 23);
-}
-
-// silu(g) * u = (g / (1 + exp(-g))) * u
-__device__ inline float silu_mul(float g, float u) {
-  const float den = 1.0f + dq_exp(-g);
-  const float s = g / den;
-  return s * u;
-}
-
 // Down-projection input: row m of gu holds [gate (F) | up (F)]; one wave per
 // (row, 256-block) of silu(gate) * up.
 template <bool VEC>

@@ -114,6 +114,14 @@ def test_host_checks_return_codes(lib):
     assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, 16, 1e-5, 8, None) == dq.DQ_EINVAL
     # empty shapes are valid no-ops
     assert lib.dq_qgemm(dq.Q4_K, 0, 32, 256, None, None, None, 32, None) == dq.DQ_OK
+    # the gate/up GEMM with SiLU(gate) * up in its epilogue
+    assert lib.dq_qgemm_swiglu(dq.Q4_K, 4, 24, 512, 16, 16, 16, 24, None) == dq.DQ_EINVAL  # F % 16
+    assert lib.dq_qgemm_swiglu(dq.Q4_K, 4, 32, 512, 16, 16, 16, 31, None) == dq.DQ_EINVAL  # ldh < F
+    assert lib.dq_qgemm_swiglu(dq.Q4_K, 4, 32, 512, 16, 16, None, 32, None) == dq.DQ_EINVAL  # h NULL
+    assert lib.dq_qgemm_swiglu(dq.Q4_K, 4, 32, 512, 8, 16, 16, 32, None) == dq.DQ_EINVAL  # qa misaligned
+    assert lib.dq_qgemm_swiglu(15, 4, 32, 512, 16, 16, 16, 32, None) == dq.DQ_EUNSUPPORTED
+    assert lib.dq_qgemm_swiglu(dq.Q4_K, 0, 32, 256, None, None, None, 32, None) == dq.DQ_OK
+    assert lib.dq_qgemm_swiglu(dq.Q4_K, 4, 0, 256, None, None, None, 0, None) == dq.DQ_OK
     assert lib.dq_quantize_act(0, 256, None, 256, None, None) == dq.DQ_OK
     assert lib.dq_swiglu_quantize_act(0, 256, None, 512, None, None) == dq.DQ_OK
     assert lib.dq_rmsnorm_quantize_act(0, 256, None, 256, None, 0.0, None, None) == dq.DQ_OK
