@@ -26,7 +26,7 @@
  *     nothing (every argument is checked before the first launch).  DQ_EHIP
  *     means the HIP runtime refused a launch; in a call that makes several
  *     launches (dq_qgemm_rows, dq_qgemm_rows_sample, dq_logits_stats,
- *     dq_attention) the launches before the refused one may already be
+ *     dq_attention, dq_debug_subdots) the launches before the refused one may already be
  *     enqueued and may have written the workspace, the flags or the output.
  *     dq_last_error() gives a message for the last error raised on the
  *     calling host thread.
@@ -444,6 +444,25 @@ int dq_embed_rows(int type, int64_t N, int64_t K, const void *table, const int32
  * ------------------------------------------------------------------------ */
 int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const void *qa,
                              const void *packed, int32_t *S, int32_t *Mn, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * dq_debug_subdots -- test hook for the per-sub-block int32 dots.  Runs the
+ * dq_qgemm kernel (the one the launcher picks for this shape) once per
+ * sub-block position j, with the digit builder given scale 1 for sub-block j
+ * and 0 for the others in place of the weights' scales, and stores the exact
+ * integer S of each step, which is then that sub-block's dot:
+ *   dots[((m*N + n)*(K/256) + b)*J + j] = sum over sub-block j of super-block b
+ *                                          of q_w * q_x
+ * with J = 8 sub-blocks of 32 for Q4_K (q_w in [0, 15]) and J = 16 of 16 for
+ * Q6_K (q_w - 32 in [-32, 31]).  Unpack, operand layout and MFMA accumulation
+ * are the production path's; only the scale bytes and the epilogue differ.
+ * qa is a dq_quantize_act buffer (its d_x values are not used); dots is a
+ * device int32 array of M*N*(K/256)*J entries.  J launches on the stream.
+ * Errors: DQ_EUNSUPPORTED, DQ_EINVAL (shape, NULL, alignment, more than 2^40
+ *         entries), DQ_EHIP.
+ * ------------------------------------------------------------------------ */
+int dq_debug_subdots(int type, int64_t M, int64_t N, int64_t K, const void *qa,
+                     const void *packed, int32_t *dots, hipStream_t stream);
 
 #ifdef __cplusplus
 }

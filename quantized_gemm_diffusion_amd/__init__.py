@@ -37,7 +37,7 @@ EXPORTS = ("dq_status_string", "dq_last_error", "dq_packed_size", "dq_repack_wei
            "dq_logits_stats_workspace",
            "dq_logits_stats", "dq_qgemm_rows_sample_workspace", "dq_qgemm_rows_sample",
            "dq_attention_workspace", "dq_attention", "dq_row_bytes", "dq_embed_rows",
-           "dq_debug_superblock_sums")
+           "dq_debug_superblock_sums", "dq_debug_subdots")
 ACT_RECORD = 5120  # bytes per (super-block, 16-row block) record
 
 
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dq_rmsnorm_quantize_act": [i64, i64, vp, i64, vp, ctypes.c_float, vp, vp],
             "dq_qgemm": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
             "dq_qgemm_swiglu": [i32, i64, i64, i64, vp, vp, vp, i64, vp],
+            "dq_debug_subdots": [i32, i64, i64, i64, vp, vp, vp, vp],
             "dq_qgemm_rows_workspace": [i64, i64, psz],
             "dq_qgemm_rows": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp],
             "dq_qgemm_rows_noalloc": [i32, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp],
@@ -418,6 +419,18 @@ def qgemm_rows_sample(type_: int, canvas: torch.Tensor, idx: torch.Tensor, packe
                                     beta, _ptr(token), _ptr(stats), _ptr(ws), ws.numel(),
                                     _stream(canvas)), "dq_qgemm_rows_sample")
     return token, stats, ws
+
+
+def debug_subdots(type_: int, act: Act, packed: torch.Tensor, N: int) -> torch.Tensor:
+    """Per-sub-block int32 dots from the GEMM kernel's own path: [M, N, K/256, J],
+    J = 8 (Q4_K) or 16 (Q6_K)."""
+    lib = load_library()
+    M, K = _check_operands(type_, act, packed, N)
+    J = 8 if type_ == Q4_K else 16
+    dots = torch.empty((M, N, K // 256, J), dtype=torch.int32, device=act.buf.device)
+    _check(lib.dq_debug_subdots(type_, M, N, K, _ptr(act.buf), _ptr(packed), _ptr(dots),
+                                _stream(act.buf)), "dq_debug_subdots")
+    return dots
 
 
 def debug_superblock_sums(type_: int, act: Act, packed: torch.Tensor, N: int):

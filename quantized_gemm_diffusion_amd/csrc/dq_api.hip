@@ -521,4 +521,22 @@ int dq_debug_superblock_sums(int type, int64_t M, int64_t N, int64_t K, const vo
                   "dq_debug_superblock_sums");
 }
 
+int dq_debug_subdots(int type, int64_t M, int64_t N, int64_t K, const void *qa,
+                     const void *packed, int32_t *dots, hipStream_t stream) {
+  if (int s = check_gemm(type, M, N, K, qa, packed)) return s;
+  if (M == 0 || N == 0) return ok();
+  if (!dots || !aligned(dots, 4)) return fail(DQ_EINVAL, "dots must be non-NULL and 4-byte aligned");
+  const int J = type == DQ_Q4_K ? 8 : 16;
+  if ((int64_t)M * N * (K / dq::QK) * J > ((int64_t)1 << 40))
+    return fail(DQ_EINVAL, "debug output too large");
+  // one launch per sub-block position, each storing that sub-block's dots
+  for (int sub = 0; sub < J; ++sub) {
+    const hipError_t e = dq::launch_qgemm(type, 2, M, N, K, static_cast<const uint8_t *>(qa),
+                                          static_cast<const uint8_t *>(packed), nullptr, N, dots,
+                                          dots, stream, sub);
+    if (e != hipSuccess) return launched(e, "dq_debug_subdots");
+  }
+  return ok();
+}
+
 }  // extern "C"

@@ -174,11 +174,13 @@ hipError_t launch_rmsnorm_quantize(int64_t M, int64_t K, const float *x, int64_t
                                    hipStream_t stream);
 hipError_t launch_repack(int type, int64_t N, int64_t K, const uint8_t *src, uint8_t *dst,
                          hipStream_t stream);
-// mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers,
+// mode: 0 canvas GEMM, 1 gathered-row GEMM, 2 debug stores of the exact integers
+// (with sub >= 0: every sub-block scale replaced by 1 for sub-block sub and 0
+// for the rest, S alone stored as that sub-block's dot, J per super-block),
 // 4 canvas GEMM over interleaved gate/up tiles storing silu(gate) * up (y is
 // then M x N/2, row stride ldy).
 hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
                         const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
-                        int32_t *dbg_Mn, hipStream_t stream);
+                        int32_t *dbg_Mn, hipStream_t stream, int sub = -1);
 
 }  // namespace dq

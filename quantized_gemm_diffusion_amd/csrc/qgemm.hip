@@ -142,7 +142,11 @@ struct Digits {
 //   j < 4 : sc = low 6 bits of byte j, mn = low 6 bits of byte j+4
 //   j >= 4: sc = low nibble of byte j+4 | top 2 bits of byte j-4 << 4,
 //           mn = high nibble of byte j+4 | top 2 bits of byte j << 4
-__device__ inline void make_digits(const RawQ4 &w, int kq, Digits &D) {
+//
+// With sub >= 0 (the debug hook for per-sub-block dots) every scale is
+// replaced by 1 for sub-block sub and 0 for the others, so the digits' exact
+// integer sum S is that sub-block's dot.
+__device__ inline void make_digits(const RawQ4 &w, int kq, Digits &D, int sub = -1) {
   D.dw = half_bits_to_float((uint32_t)w.head[0]);
   D.dmw = half_bits_to_float((uint32_t)w.head[0] >> 16);
   const uint32_t D0 = (uint32_t)w.head[1], D1 = (uint32_t)w.head[2], D2 = (uint32_t)w.head[3];
@@ -151,8 +155,9 @@ __device__ inline void make_digits(const RawQ4 &w, int kq, Digits &D) {
   const uint32_t mn_hi = ((D2 >> 4) & 0x0f0f0f0fu) | ((D1 >> 2) & 0x30303030u);
   // bytes 0, 1 of SC / MN: sub-blocks 2kq and 2kq + 1
   const int sh16 = 16 * (kq & 1);
-  const uint32_t SC = (kq < 2 ? sc_lo : sc_hi) >> sh16;
+  uint32_t SC = (kq < 2 ? sc_lo : sc_hi) >> sh16;
   const uint32_t MN = (kq < 2 ? mn_lo : mn_hi) >> sh16;
+  if (sub >= 0) SC = (2 * kq == sub ? 1u : 0u) | (2 * kq + 1 == sub ? 0x100u : 0u);
   const uint32_t SL = SC & 0x07070707u, SH = (SC >> 3) & 0x07070707u;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -180,8 +185,9 @@ __device__ inline void make_digits(const RawQ4 &w, int kq, Digits &D) {
   }
 }
 
-// Q6_K: chunk c of lane quarter kq is sub-block 4kq + c (scale byte c).
-__device__ inline void make_digits(const RawQ6 &w, int kq, Digits &D) {
+// Q6_K: chunk c of lane quarter kq is sub-block 4kq + c (scale byte c);
+// sub >= 0 selects one sub-block as above.
+__device__ inline void make_digits(const RawQ6 &w, int kq, Digits &D, int sub = -1) {
   D.dw = half_bits_to_float(w.d);
   D.dmw = 0.f;
 #pragma unroll
@@ -189,7 +195,7 @@ __device__ inline void make_digits(const RawQ6 &w, int kq, Digits &D) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = 2 * i + h;
-      const int sc = (int)(int8_t)((w.sw >> (8 * c)) & 255);
+      const int sc = sub >= 0 ? (4 * kq + c == sub ? 1 : 0) : (int)(int8_t)((w.sw >> (8 * c)) & 255);
       const uint32_t sc2 = ((uint32_t)sc & 0xffffu) * 0x10001u;
       const uint32_t off2 = ((uint32_t)(128 - 32 * sc) & 0xffffu) * 0x10001u;
       const uint32_t u = (uint32_t)w.qh[c];
@@ -338,16 +344,26 @@ __device__ inline void step_fold(const StepOut &o, const f32x4 &x4, float dw, fl
   }
 }
 
+// Debug stores: S and Mn of (row, n, super-block b) at (row * N + n) * nb + b;
+// with sub >= 0 (one-hot scales) S alone, the dot of sub-block sub, at
+// ((row * N + n) * nb + b) * J + sub, J sub-blocks per super-block.
 template <bool Q6>
 __device__ inline void step_debug(const StepOut &o, int64_t row0, int kq, int64_t n, int64_t M,
-                                  int64_t N, int nb, int b, int32_t *dbg_S, int32_t *dbg_Mn) {
+                                  int64_t N, int nb, int b, int32_t *dbg_S, int32_t *dbg_Mn,
+                                  int sub) {
+  constexpr int J = Q6 ? 16 : 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = row0 + 4 * kq + i;
     if (row < M && n < N) {
       const int64_t o_ = (row * N + n) * nb + b;
-      dbg_S[o_] = Q6 ? o.rl[i] + o.rh[i] * 256 : o.rl[i] + o.rh[i] * 8;
-      dbg_Mn[o_] = Q6 ? 0 : (int32_t)o.mnf[i];
+      const int32_t S = Q6 ? o.rl[i] + o.rh[i] * 256 : o.rl[i] + o.rh[i] * 8;
+      if (sub >= 0) {
+        dbg_S[o_ * J + sub] = S;
+      } else {
+        dbg_S[o_] = S;
+        dbg_Mn[o_] = Q6 ? 0 : (int32_t)o.mnf[i];
+      }
     }
   }
 }
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
                                                                    int32_t *__restrict__ dbg_Mn,
                                                                    float beta,
                                                                    float4 *__restrict__ part,
-                                                                   int npart, int xcds) {
+                                                                   int npart, int xcds, int sub) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
   constexpr int MB = SH::MB, NT = SH::NT, R = SH::R, D = R - 1, WAVES = SH::WAVES;
@@ -517,7 +533,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
       for (int j = 0; j < NT; ++j) {
         Raw w;
         read_w(wslot + j * WSLOT, lane, col, kq, w);
-        make_digits(w, kq, Dg[j]);
+        make_digits(w, kq, Dg[j], DEBUG ? sub : -1);
       }
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
@@ -547,7 +563,7 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
           step_mfma<Q6>(f, Dg[j], out[j]);
           if (DEBUG)
             step_debug<Q6>(out[j], (int64_t)(mb0 + t) * MBLK, kq, (nt0 + j) * TILE_N + col, M,
-                           nt0 + j < ntiles ? N : 0, nb, b, dbg_S, dbg_Mn);
+                           nt0 + j < ntiles ? N : 0, nb, b, dbg_S, dbg_Mn, sub);
           else if (j > 0)
             step_fold<Q6>(out[j - 1], f.x4, Dg[j - 1].dw, Dg[j - 1].dmw, acc[t][j - 1]);
         }
@@ -715,7 +731,7 @@ template <int TYPE, class RS, int MODE>
 __global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_kernel(
     int M, int64_t N, int nb, const uint8_t *__restrict__ qa, uint32_t qa_bytes,
     const uint8_t *__restrict__ packed, float *__restrict__ y, int64_t ldy, int y_vec,
-    int32_t *__restrict__ dbg_S, int32_t *__restrict__ dbg_Mn, int xcds) {
+    int32_t *__restrict__ dbg_S, int32_t *__restrict__ dbg_Mn, int xcds, int sub) {
   constexpr bool Q6 = TYPE == 14;
   constexpr bool DEBUG = MODE == 2;
   constexpr int MB = RS::MB, NTW = RS::NTW, KS = RS::KS, P = RS::P, HP = MB / P;
@@ -784,7 +800,7 @@ __global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_ker
       if (h == 0 && active) {
         Raw w;
         read_w(wslot, lane, col, kq, w);
-        make_digits(w, kq, Dg);
+        make_digits(w, kq, Dg, DEBUG ? sub : -1);
       }
       // the other ring half was read in phase ph - 1, which every wave has
       // finished; the weight slot is refilled with the next super-block's
@@ -806,7 +822,7 @@ __global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_ker
           step_mfma<Q6>(f, Dg, o);
           if (DEBUG)
             step_debug<Q6>(o, (int64_t)(mb0 + t) * MBLK, kq, tile * TILE_N + col, M,
-                           tile < ntiles ? N : 0, nb, sb_of(sbi), dbg_S, dbg_Mn);
+                           tile < ntiles ? N : 0, nb, sb_of(sbi), dbg_S, dbg_Mn, sub);
           else
             step_fold<Q6>(o, f.x4, Dg.dw, Dg.dmw, acc[t]);
         }
@@ -894,7 +910,7 @@ __global__ __launch_bounds__(64 * RS::WAVES, 12 / RS::WAVES) void qgemm_ring_ker
 template <int TYPE, class RS>
 hipError_t launch_ring(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
                        const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
-                       int32_t *dbg_Mn, hipStream_t stream) {
+                       int32_t *dbg_Mn, hipStream_t stream, int sub = -1) {
   const int64_t nmb = (M + MBLK - 1) / MBLK;
   const int64_t ntiles = (N + TILE_N - 1) / TILE_N;
   dim3 grid((unsigned)(((ntiles + RS::NTW - 1) / RS::NTW) * ((nmb + RS::MB - 1) / RS::MB)));
@@ -903,13 +919,13 @@ hipError_t launch_ring(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
   const int y_vec = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (ldy % 4 == 0);
   if (mode == 2)
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 2>), grid, block, 0, stream, (int)M, N, nb,
-                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
+                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds, sub);
   else if (mode == 4)
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 4>), grid, block, 0, stream, (int)M, N, nb,
-                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
+                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds, sub);
   else
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 0>), grid, block, 0, stream, (int)M, N, nb,
-                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds);
+                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds, sub);
   return hipGetLastError();
 }
 
@@ -1589,6 +1605,7 @@ inline bool use_narrow(int mode, int64_t M, int64_t N, int nb, int64_t ldy) {
 
 struct Extra {  // arguments of the debug and sampler-state modes
   int32_t *dbg_S = nullptr, *dbg_Mn = nullptr;
+  int sub = -1;  // debug: the one sub-block whose dot S becomes, or -1
   float beta = 0.0f;
   float4 *part = nullptr;
   int npart = 0;
@@ -1609,7 +1626,7 @@ hipError_t launch2(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa,
 #define DQ_LAUNCH(MODE)                                                                        \
   hipLaunchKernelGGL((qgemm_kernel<TYPE, SH, MODE>), grid, block, 0, stream, m, N, nb, qa,        \
                      qa_bytes, packed, y, ldy, y_vec, x.dbg_S, x.dbg_Mn, x.beta, x.part, x.npart, \
-                     device_props().xcds)
+                     device_props().xcds, x.sub)
   switch (mode) {
     case 1: DQ_LAUNCH(1); break;
     case 2: DQ_LAUNCH(2); break;
@@ -1765,7 +1782,7 @@ hipError_t launch_type(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
 
 hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, const uint8_t *qa,
                         const uint8_t *packed, float *y, int64_t ldy, int32_t *dbg_S,
-                        int32_t *dbg_Mn, hipStream_t stream) {
+                        int32_t *dbg_Mn, hipStream_t stream, int sub) {
   const int nb = (int)(K / QK);
   if (use_narrow(mode, M, N, nb, ldy)) {
     const bool two = M > MBLK;
@@ -1779,19 +1796,20 @@ hipError_t launch_qgemm(int type, int mode, int64_t M, int64_t N, int64_t K, con
   }
   switch (mode == 0 || mode == 2 || mode == 4 ? ring_pick(M, N, nb) : 0) {
     case 1:
-      return type == 12 ? launch_ring<12, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
-                        : launch_ring<14, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+      return type == 12 ? launch_ring<12, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream, sub)
+                        : launch_ring<14, RingA>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream, sub);
     case 2:
-      return type == 12 ? launch_ring<12, RingB>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
-                        : launch_ring<14, RingB>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+      return type == 12 ? launch_ring<12, RingB>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream, sub)
+                        : launch_ring<14, RingB>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream, sub);
     case 3:
-      return type == 12 ? launch_ring<12, RingC>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream)
-                        : launch_ring<14, RingC>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream);
+      return type == 12 ? launch_ring<12, RingC>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream, sub)
+                        : launch_ring<14, RingC>(mode, M, N, nb, qa, packed, y, ldy, dbg_S, dbg_Mn, stream, sub);
     default: break;
   }
   Extra x;
   x.dbg_S = dbg_S;
   x.dbg_Mn = dbg_Mn;
+  x.sub = sub;
   if (type == 12) return launch_type<12>(mode, M, N, nb, qa, packed, y, ldy, x, stream);
   return launch_type<14>(mode, M, N, nb, qa, packed, y, ldy, x, stream);
 }

@@ -57,7 +57,8 @@ def test_every_entry_point_cites_its_source():
         if name == "dq_qgemm_rows_noalloc":
             assert "cannot allocate" in doc, name
         else:
-            assert "Source" in doc or "as for dq_" in doc or "Runs the dq_qgemm kernel" in doc, name
+            flat = re.sub(r"\s*\n\s*\*\s*", " ", doc)  # the comment as one line
+            assert "Source" in flat or "as for dq_" in flat or "Runs the dq_qgemm kernel" in flat, name
     for q in ("dq_packed_size", "dq_act_size", "dq_qgemm_rows_workspace"):
         assert "Source" in blocks[q], q
 

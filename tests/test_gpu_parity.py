@@ -171,6 +171,22 @@ def test_subblock_dots_bit_exact(dq, type_):
         assert np.array_equal(S.cpu().numpy(), dots[..., j]), f"sub-block {j}"
 
 
+@pytest.mark.parametrize("type_,M,N,K", [(oracle.Q4_K, 33, 40, 512), (oracle.Q6_K, 37, 70, 768),
+                                         (oracle.Q4_K, 160, 100, 1024), (oracle.Q6_K, 20, 48, 512),
+                                         (oracle.Q4_K, 512, 64, 512)])
+def test_subdots_hook_bit_exact(dq, type_, M, N, K):
+    # dq_debug_subdots: every per-sub-block int32 dot from the GEMM kernel's own
+    # unpack + MFMA path (scales replaced by one-hot selectors), full int8 Q6_K
+    # scales in the weights (the hook ignores them)
+    W = _weights(type_, N, K, 300 + M + N, full_scales=True)
+    x = synth.activations(np.random.default_rng(310 + M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    dots = dq.debug_subdots(type_, _act(dq, xq, xd, xb), packed, N)
+    _sync()
+    assert np.array_equal(dots.cpu().numpy(), oracle.subdots(type_, xq, W, N))
+
+
 # --------------------------------------------------------------------------- #
 # GEMM outputs within tolerance, tails and degenerate shapes                  #
 # --------------------------------------------------------------------------- #

@@ -94,3 +94,17 @@ def test_shared_record_superblock_sums_bit_exact(dq, type_, M, N, K):
     oS, oMn = oracle.superblock_sums(type_, xq, xb, W, N)
     assert np.array_equal(S.cpu().numpy(), oS)
     assert np.array_equal(Mn.cpu().numpy(), oMn)
+
+
+@pytest.mark.parametrize("type_,M,N,K", [(oracle.Q4_K, 145, 17200, 1024),
+                                         (oracle.Q6_K, 80, 17700, 1024)])
+def test_shared_record_subdots_bit_exact(dq, type_, M, N, K):
+    # every per-sub-block int32 dot through the shared-record kernel's own path
+    print(f"shared-record sub-block dots type {type_} {M}x{N}x{K}", flush=True)
+    W = _weights(type_, N, K, 13 * M + N)
+    x = synth.activations(np.random.default_rng(17 * M), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    packed = dq.repack_weights(type_, N, K, _t(W.reshape(-1)))
+    dots = dq.debug_subdots(type_, _act(dq, xq, xd, xb), packed, N)
+    torch.cuda.synchronize()
+    assert np.array_equal(dots.cpu().numpy(), oracle.subdots(type_, xq, W, N))
