@@ -920,10 +920,14 @@ hipError_t launch_ring(int mode, int64_t M, int64_t N, int nb, const uint8_t *qa
   if (mode == 2)
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 2>), grid, block, 0, stream, (int)M, N, nb,
                        qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds, sub);
-  else if (mode == 4)
-    hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 4>), grid, block, 0, stream, (int)M, N, nb,
-                       qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds, sub);
-  else
+  else if (mode == 4) {
+    if constexpr (RS::NTW % 2 == 0)
+      hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 4>), grid, block, 0, stream, (int)M, N, nb,
+                         qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds,
+                         sub);
+    else
+      return hipErrorInvalidValue;  // gate/up pairs need an even number of tiles
+  } else
     hipLaunchKernelGGL((qgemm_ring_kernel<TYPE, RS, 0>), grid, block, 0, stream, (int)M, N, nb,
                        qa, qa_bytes, packed, y, ldy, y_vec, dbg_S, dbg_Mn, device_props().xcds, sub);
   return hipGetLastError();
