@@ -177,14 +177,16 @@ int dq_swiglu_quantize_act(int64_t M, int64_t F, const float *gu, int64_t ldgu, 
  *
  * Source: Architecture page, "A forward pass", step 2 (RMSNorm, then one
  * int8 quantization reused by Q, K and V); "Source map" (RMSNorm among the
- * GPU kernels).  Per row, IEEE binary32 with no contraction: 256 partial sums
- * of squares, partial j over the 4-value groups j, j + 256, j + 512, ... in
- * increasing order (one square and one addition at a time); a halving tree,
- * at h = 128, 64, ..., 1: partial[j] += partial[j + h]; mean = partial[0] / K;
+ * GPU kernels).  Per row, IEEE binary32 with no contraction, the sum of
+ * squares ss is formed block by block (256 values): in each block, the values
+ * 4l .. 4l+3 give the lane sum s[l] = ((x0*x0 + x1*x1) + x2*x2) + x3*x3 (l =
+ * 0..63); the block sum is the pairwise tree of six levels s[i] = s[2i] +
+ * s[2i+1]; ss adds the block sums in increasing block order.  mean = ss / K;
  * rinv = 1 / sqrt(mean + eps) (both correctly rounded); y = (x * rinv) *
  * gamma.  Then y is quantized by the dq_quantize_act rule, bit-identical to
  * any binary32 implementation of these steps.  Inputs must be finite.
  *
+ *   K     : a multiple of 256, at most 262144.
  *   x     : device f32, M rows, row stride ldx >= K floats; read only.
  *   gamma : device f32, K weights; read only.
  *   eps   : finite, >= 0.

@@ -254,12 +254,15 @@ int dqo_swiglu_quantize_act(int64_t M, int64_t F, const float *gu, int64_t ldgu,
 }
 
 /* RMSNorm of one row, then the quantizer.  The sum of squares is formed in  */
-/* a fixed order: 256 partial sums, partial j taking the 4-value groups      */
-/* g = j, j + 256, j + 512, ... (values 4g .. 4g+3) in increasing order, one */
-/* square and one addition at a time; then a halving tree, at h = 128, 64,   */
-/* ..., 1: partial[j] += partial[j + h] for j < h.  With ss = partial[0]:    */
-/*   mean = ss / K;  rinv = 1 / sqrt(mean + eps)  (both correctly rounded);  */
-/*   y[k] = (x[k] * rinv) * gamma[k].                                        */
+/* a fixed order, block by block (256 values each):                          */
+/*   lane sum: for l = 0..63, s[l] = ((x0*x0 + x1*x1) + x2*x2) + x3*x3 over  */
+/*     the block's values 4l .. 4l+3, one square and one addition at a time; */
+/*   block sum: a pairwise tree over the 64 lane sums, six levels of         */
+/*     s[i] = s[2i] + s[2i+1];                                               */
+/*   ss: the block sums added in increasing block order, starting from      */
+/*     block 0's.                                                            */
+/* Then mean = ss / K;  rinv = 1 / sqrt(mean + eps)  (both correctly         */
+/* rounded);  y[k] = (x[k] * rinv) * gamma[k].                               */
 int dqo_rmsnorm_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx,
                              const float *gamma, float eps, int8_t *q, float *d,
                              int32_t *bsum) {
@@ -268,19 +271,23 @@ int dqo_rmsnorm_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx,
   if (!y) return -2;
   for (int64_t m = 0; m < M; ++m) {
     const float *xr = x + m * ldx;
-    float part[256];
-    for (int j = 0; j < 256; ++j) part[j] = 0.0f;
-    for (int64_t g = 0; 4 * g < K; ++g) {
-      const int j = (int)(g % 256);
-      for (int i = 0; i < 4; ++i) {
-        const float v = xr[4 * g + i];
-        const float sq = v * v;
-        part[j] = part[j] + sq;
+    float ss = 0.0f;
+    for (int64_t b = 0; b < K / QK; ++b) {
+      float s[64];
+      for (int l = 0; l < 64; ++l) {
+        const float *v = xr + b * QK + 4 * l;
+        float t = v[0] * v[0];
+        for (int i = 1; i < 4; ++i) {
+          const float sq = v[i] * v[i];
+          t = t + sq;
+        }
+        s[l] = t;
       }
+      for (int n = 32; n >= 1; n /= 2)
+        for (int i = 0; i < n; ++i) s[i] = s[2 * i] + s[2 * i + 1];
+      ss = b == 0 ? s[0] : ss + s[0];
     }
-    for (int h = 128; h >= 1; h /= 2)
-      for (int j = 0; j < h; ++j) part[j] = part[j] + part[j + h];
-    const float mean = part[0] / (float)K;
+    const float mean = ss / (float)K;
     const float rinv = 1.0f / sqrtf(mean + eps);
     for (int64_t k = 0; k < K; ++k) {
       const float t = xr[k] * rinv;

@@ -154,6 +154,9 @@ int dq_rmsnorm_quantize_act(int64_t M, int64_t K, const float *x, int64_t ldx,
   size_t bytes = 0;
   if (int s = dq_act_size(M, K, &bytes)) return s;
   if (ldx < K) return fail(DQ_EINVAL, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (K > (int64_t)dq::NORM_MAX_BLOCKS * dq::QK)
+    return fail(DQ_EINVAL, "K = %lld too large for the RMSNorm producer (at most %lld)",
+                (long long)K, (long long)dq::NORM_MAX_BLOCKS * dq::QK);
   if (!(eps >= 0.0f) || !isfinite(eps)) return fail(DQ_EINVAL, "eps must be finite and >= 0");
   if (M == 0) return ok();
   if (!x || !gamma || !qa) return fail(DQ_EINVAL, "NULL pointer argument");

@@ -169,6 +169,9 @@ hipError_t launch_quantize(int64_t M, int64_t K, const float *x, int64_t ldx, co
                            int64_t L, uint8_t *qa, int32_t *err, hipStream_t stream);
 hipError_t launch_swiglu_quantize(int64_t M, int64_t F, const float *gu, int64_t ldgu,
                                   uint8_t *qa, hipStream_t stream);
+// The RMSNorm producer keeps one sum of squares per 256-block of a row in
+// LDS: rows of at most NORM_MAX_BLOCKS blocks (K <= 262144).
+constexpr int NORM_MAX_BLOCKS = 1024;
 hipError_t launch_rmsnorm_quantize(int64_t M, int64_t K, const float *x, int64_t ldx,
                                    const float *gamma, float eps, uint8_t *qa,
                                    hipStream_t stream);

@@ -151,22 +151,43 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(int64_t M, int64_t
   quantize_lane(v, rec, r, lane);
 }
 
-// RMSNorm then quantize: one workgroup of 16 waves per (padded) row.  The
-// sum of squares is formed in the order the producer defines: thread j < 256
-// keeps a partial over the 4-value groups j, j + 256, ... in increasing order
-// (one square and one addition at a time), then a halving tree at h = 128,
-// 64, ..., 1: partial[j] += partial[j + h].  mean = ss / K, rinv = 1 /
-// sqrt(mean + eps), y = (x * rinv) * gamma; wave w then quantizes blocks w,
-// w + 16, ... of y (one block per wave at K = 4096).
+// RMSNorm then quantize: one workgroup of 16 waves per (padded) row, wave w
+// owning the row's 256-blocks w, w + 16, ...  The sum of squares is formed
+// in the order the producer defines: every lane adds its 4 squares in turn,
+// the wave adds its 64 lane sums as a pairwise tree (DPP moves pair lanes 2i
+// and 2i + 1, then quads, octets, rows of 16, rows 0-1 and 2-3, then the two
+// halves), each block's sum goes to LDS, and after one barrier every wave
+// adds the block sums in increasing block order.  mean = ss / K, rinv = 1 /
+// sqrt(mean + eps), y = (x * rinv) * gamma; each wave then quantizes its
+// blocks.
 //
-// Latency: a thread's groups are loaded four at a time before any is added,
-// the tree's levels h <= 32 run inside wave 0 on lane shuffles (the same
-// additions of the same operands, without a workgroup barrier each), and
-// every wave loads its first block of x and gamma at the start, while the
-// sum of squares is still being formed.
-constexpr int NORM_PARTS = 256;    // partial sums of the defined order
+// Latency: every wave loads its first block of x and gamma before anything
+// waits, so at K <= 4096 the row costs one memory round trip, one barrier
+// and no LDS shuffles.
 constexpr int NORM_THREADS = 1024;
 constexpr int NORM_WAVES = NORM_THREADS / 64;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline float dpp_or_zero(float v) {
+  // lanes of rows outside ROW_MASK read 0
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// The pairwise tree over the wave's 64 values; every level adds two values
+// the tree pairs (in either order: binary32 addition commutes).  The full
+// sum ends in lane 63 and is returned in every lane.
+__device__ inline float wave_tree_sum(float v) {
+  v = v + dpp_or_zero<DPP_QUAD_1032>(v);
+  v = v + dpp_or_zero<DPP_QUAD_2301>(v);
+  v = v + dpp_or_zero<DPP_ROW_HALF_MIRROR>(v);
+  v = v + dpp_or_zero<DPP_ROW_MIRROR>(v);
+  // rows 1 and 3 add the sum of the row before (lane 15 of it), then rows 2
+  // and 3 add rows 0 + 1 (lane 31); the other rows add 0
+  v = v + dpp_or_zero<DPP_ROW_BCAST15, 0xa>(v);
+  v = v + dpp_or_zero<DPP_ROW_BCAST31, 0xc>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 
 template <bool VEC>
 __device__ inline void load4(const float *p, float (&v)[4]) {
@@ -183,7 +204,7 @@ template <bool VEC>
 __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
     int64_t M, int64_t Mpad, int nb, const float *__restrict__ x, int64_t ldx,
     const float *__restrict__ gamma, float eps, uint8_t *__restrict__ qa) {
-  __shared__ float part[NORM_PARTS];
+  __shared__ float block_ss[NORM_MAX_BLOCKS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m = blockIdx.x;
   const int64_t mb = m / ACT_ROWS;
@@ -192,7 +213,7 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
   const bool valid = m < M;  // uniform across the workgroup
   const float *xr = x + (valid ? m : 0) * ldx;
 
-  // this wave's first block (it does not depend on the norm)
+  // this wave's first block and its weights
   float xv[4] = {0.f, 0.f, 0.f, 0.f}, gv[4] = {0.f, 0.f, 0.f, 0.f};
   if (valid && wave < nb) {
     load4<VEC>(xr + (int64_t)wave * QK + 4 * lane, xv);
@@ -201,42 +222,22 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_quantize_kernel(
 
   float rinv = 0.0f;
   if (valid) {
-    if (tid < NORM_PARTS) {
-      float acc = 0.0f;
-      for (int64_t g0 = tid; 4 * g0 < K; g0 += 4 * NORM_PARTS) {
-        float v[4][4];
+    for (int b = wave; b < nb; b += NORM_WAVES) {
+      float v[4] = {xv[0], xv[1], xv[2], xv[3]};
+      if (b != wave) load4<VEC>(xr + (int64_t)b * QK + 4 * lane, v);
+      float t = v[0] * v[0];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t g = g0 + (int64_t)u * NORM_PARTS;
-          if (4 * g < K) load4<VEC>(xr + 4 * g, v[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (4 * (g0 + (int64_t)u * NORM_PARTS) < K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float sq = v[u][i] * v[u][i];
-              acc = acc + sq;
-            }
-          }
-        }
+      for (int i = 1; i < 4; ++i) {
+        const float sq = v[i] * v[i];
+        t = t + sq;
       }
-      part[tid] = acc;
+      t = wave_tree_sum(t);
+      if (lane == 0) block_ss[b] = t;
     }
     __syncthreads();
-    if (tid < 128) part[tid] = part[tid] + part[tid + 128];
-    __syncthreads();
-    if (wave == 0) {
-      float p = part[lane] + part[lane + 64];  // h = 64: lane j < 64 holds partial[j]
-#pragma unroll
-      for (int h = 32; h >= 1; h >>= 1) {
-        const float o = __shfl_down(p, h, 64);  // partial[j + h] for lanes j < h
-        p = p + o;
-      }
-      if (lane == 0) part[0] = p;
-    }
-    __syncthreads();
-    const float mean = part[0] / (float)K;
+    float ss = block_ss[0];
+    for (int b = 1; b < nb; ++b) ss = ss + block_ss[b];
+    const float mean = ss / (float)K;
     rinv = 1.0f / __builtin_sqrtf(mean + eps);
   }
 

@@ -113,6 +113,8 @@ def test_host_checks_return_codes(lib):
     assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, 16, float("nan"), 16, None) == dq.DQ_EINVAL
     assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, None, 1e-5, 16, None) == dq.DQ_EINVAL
     assert lib.dq_rmsnorm_quantize_act(4, 512, 16, 512, 16, 1e-5, 8, None) == dq.DQ_EINVAL
+    # one sum of squares per 256-block in LDS: K at most 262144
+    assert lib.dq_rmsnorm_quantize_act(1, 262400, 16, 262400, 16, 1e-5, 16, None) == dq.DQ_EINVAL
     # empty shapes are valid no-ops
     assert lib.dq_qgemm(dq.Q4_K, 0, 32, 256, None, None, None, 32, None) == dq.DQ_OK
     # the gate/up GEMM with SiLU(gate) * up in its epilogue
