@@ -137,7 +137,9 @@ def main():
         log("bench.py measures one GPU: this build runs the hot path on a single MI355X; "
             "multi-GPU sharding is a design note only, so --gpus must be 1.")
         sys.exit(2)
-    clocks_before = host_clocks()
+    # not in counters mode: under a counter profiler a child process would
+    # initialise the GPU before its interpreter starts
+    clocks_before = None if args.counters else host_clocks()
 
     import torch
     import quantized_gemm_diffusion_amd as dq
