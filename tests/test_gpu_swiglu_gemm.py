@@ -2,16 +2,17 @@
 weights with silu(gate) * up formed in its epilogue.
 
 The epilogue's values are defined as the binary32 SwiGLU steps applied to the
-f32 values dq_qgemm computes on the same interleaved matrix, so the checks are
-bit-exact against the oracle's binary32 SwiGLU of the library's own GEMM
-output (that output itself is checked against the oracle's f64 definition by
-the GEMM parity tests, on the same kernels):
-  * every element of h against oracle.silu_mul, where the oracle's
-    per-element loop finishes in seconds, else a seeded sample of 4,096;
+f32 values dq_qgemm computes on the same interleaved matrix.  Checks:
+  * every element of h against oracle.silu_mul of the library's own GEMM
+    output, bit for bit, where the oracle's per-element loop finishes in
+    seconds, else a seeded sample of 4,096;
   * dq_quantize_act(h) against oracle.swiglu_quantize_act of the GEMM output
     rearranged to [gate | up], codes, scales and sums byte for byte (the
     codes the down projection reads, as dq_swiglu_quantize_act would make
-    them).
+    them);
+  * h against silu(g) * u of the oracle's own f64 gate and up outputs, within
+    the bound that the GEMM's tolerance implies (independent of the library's
+    GEMM output).
 Shapes: LLaDA-8B's 160 x 12288 x 4096 and the three shared-record shapes
 (on a 256-CU device; one with a last workgroup of a single tile pair), Dream-7B's
 512 x 18944 x 3584 (the canvas kernel), few rows (no narrow kernel for this
@@ -27,6 +28,7 @@ import act_layout
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+TOL = 1e-4  # the GEMM's bound: |y - y_ref| <= TOL * T
 
 
 @pytest.fixture(scope="module")
@@ -97,3 +99,44 @@ def test_swiglu_epilogue_bit_exact(dq, type_, M, F, K, pad):
         assert padding_ok
         assert np.array_equal(gq, q) and np.array_equal(gb, b)
         assert np.array_equal(gd.view(np.uint32), d.view(np.uint32))
+
+
+def _silu64(g):
+    return g / (1.0 + np.exp(-g))
+
+
+@pytest.mark.parametrize("type_,M,F,K", [(oracle.Q4_K, 160, 12288, 4096),
+                                         (oracle.Q4_K, 512, 18944, 3584),
+                                         (oracle.Q6_K, 200, 1024, 768)])
+def test_swiglu_epilogue_against_oracle_gemm(dq, type_, M, F, K):
+    """h against silu(g) * u of the oracle's f64 gate and up outputs, at 4,096
+    seeded points and the corners.  With |g' - g| <= 1e-4 Tg and |u' - u| <=
+    1e-4 Tu (the GEMM bound) and |silu'| <= 1.1 everywhere:
+      |h' - h| <= 1.1 (|u| + du) dg + |silu(g)| du,
+    plus the binary32 rounding of the epilogue's steps (1e-6 |h|)."""
+    print(f"gate/up SwiGLU GEMM against the oracle: type {type_} M {M} F {F} K {K}", flush=True)
+    rng = np.random.default_rng(3 * M + F)
+    gate = synth.weights(rng, type_, F, K)
+    up = synth.weights(rng, type_, F, K)
+    W = dq.interleave_gate_up(gate, up)
+    x = synth.activations(np.random.default_rng(5 * M + K), M, K)
+    xq, xd, xb = oracle.quantize_act(x)
+    act = dq.Act(_t(act_layout.pack(xq, xd, xb)), M, K)
+    packed = dq.repack_weights(type_, 2 * F, K, _t(W.reshape(-1)))
+    h = dq.qgemm_swiglu(type_, act, packed, F)
+    torch.cuda.synchronize()
+    h = h.cpu().numpy()
+    r2 = np.random.default_rng(17)
+    mi = np.concatenate([r2.integers(0, M, 4096), [0, 0, M - 1, M - 1]])
+    fi = np.concatenate([r2.integers(0, F, 4096), [0, F - 1, 0, F - 1]])
+    # rows of the interleaved matrix: tile i of gate at 32i .. 32i+15, of up at 32i+16 ..
+    g_row = 32 * (fi // 16) + fi % 16
+    g, Tg = oracle.qgemm_ref_points(type_, xq, xd, W, mi, g_row)
+    u, Tu = oracle.qgemm_ref_points(type_, xq, xd, W, mi, g_row + 16)
+    ref = _silu64(g) * u
+    dg, du = TOL * Tg, TOL * Tu
+    bound = 1.1 * (np.abs(u) + du) * dg + np.abs(_silu64(g)) * du + 1e-6 * np.abs(ref) + 1e-30
+    err = np.abs(h[mi, fi].astype(np.float64) - ref)
+    assert np.all(np.isfinite(h[mi, fi]))
+    assert np.all(err <= bound), f"{(err > bound).sum()} points out of bound, " \
+                                 f"worst err/bound {np.max(err / bound):.3g}"
