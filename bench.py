@@ -134,8 +134,8 @@ def host_clocks():
 def main():
     args = parse()
     if args.gpus != 1:
-        log("bench.py measures one GPU: this build runs the hot path on a single MI355X; "
-            "multi-GPU sharding is a design note only, so --gpus must be 1.")
+        log("bench.py measures one GPU: the library runs the hot path on a single MI355X and "
+            "sharding across GPUs is described, not implemented, so --gpus must be 1.")
         sys.exit(2)
     # not in counters mode: under a counter profiler a child process would
     # initialise the GPU before its interpreter starts
