@@ -117,3 +117,50 @@ def test_graph_replays_of_the_next_rows(dq):
             assert torch.equal(got, want), f"replay {i} differs from the eager result"
         dq.attention(qkv, H, Hkv, D, tab, dq.ROPE_NORM)  # the program's own eager work
         torch.cuda.synchronize()
+
+
+def test_graph_replays_of_the_step_at_llada_shapes(dq):
+    """The benchmark's layer at L = 160 (the shared-record kernel plain and with
+    the SwiGLU epilogue, the canvas kernel for down, both producers) captured
+    once; every replay equals the eager result bit for bit."""
+    print("graph replay of one LLaDA-8B layer at L = 160", flush=True)
+    L, K, F = 160, 4096, 12288
+    rng = np.random.default_rng(31)
+    x = _t(synth.activations(rng, L, K))
+    gamma = _t((1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32))
+    Wqkv = synth.q4k_weights(np.random.default_rng(32), 3 * K, K)
+    gate = synth.q4k_weights(np.random.default_rng(33), F, K)
+    up = synth.q4k_weights(np.random.default_rng(34), F, K)
+    Wd = synth.q6k_weights(np.random.default_rng(35), K, F)
+    pqkv = dq.repack_weights(dq.Q4_K, 3 * K, K, _t(Wqkv.reshape(-1)))
+    pgu = dq.repack_weights(dq.Q4_K, 2 * F, K, _t(dq.interleave_gate_up(gate, up).reshape(-1)))
+    pd = dq.repack_weights(dq.Q6_K, K, F, _t(Wd.reshape(-1)))
+    a1 = torch.empty(dq.act_size(L, K), dtype=torch.uint8, device=DEV)
+    a2 = torch.empty(dq.act_size(L, F), dtype=torch.uint8, device=DEV)
+    yqkv = torch.empty((L, 3 * K), device=DEV)
+    h = torch.empty((L, F), device=DEV)
+    yd = torch.empty((L, K), device=DEV)
+
+    def step():
+        act = dq.rmsnorm_quantize_act(x, gamma, 1e-5, out=a1)
+        dq.qgemm(dq.Q4_K, act, pqkv, 3 * K, y=yqkv)
+        dq.qgemm_swiglu(dq.Q4_K, act, pgu, F, h=h)
+        dq.qgemm(dq.Q6_K, dq.quantize_act(h, out=a2), pd, K, y=yd)
+
+    outs = (yqkv, h, yd)
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, eager):
+            assert torch.equal(got, want), f"replay {i} differs from the eager result"
+        dq.qgemm(dq.Q4_K, dq.quantize_act(x), pqkv, 3 * K)  # the program's own eager work
+        torch.cuda.synchronize()
