@@ -59,6 +59,7 @@ def test_swiglu_quantize_bit_exact(dq, M, F, pad):
 @pytest.mark.parametrize("M,K,pad,eps", [(1, 256, 0, 1e-5), (37, 512, 0, 0.0), (20, 768, 3, 1e-6),
                                          (160, 4096, 0, 1e-5), (17, 12288, 0, 1e-5),
                                          (5, 3584, 0, 1e-5),   # fewer blocks than waves
+                                         (512, 3584, 0, 1e-5),  # Dream-7B's canvas
                                          (2, 262144, 0, 1e-5)])  # the largest K: 64 blocks a wave
 def test_rmsnorm_quantize_bit_exact(dq, M, K, pad, eps):
     rng = np.random.default_rng(200 + M + pad)
