@@ -677,8 +677,9 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
 // Every wave of a workgroup owns one 16-column n-tile and a contiguous range of
 // super-blocks (its K-part), and runs all MB m-blocks of the workgroup's row
 // group against that tile: acc[MB] f32x4, one digit set and one fragment keep
-// a wave within 168 registers, so three waves share each SIMD and one wave's
-// fold and digit work issues while another's MFMAs run.  The NTW waves of a
+// a wave within 168 registers, so three waves share each SIMD where the
+// canvas kernel has two (more waves to cover the waits; matrix and vector
+// instructions of different waves overlap little on this part).  The NTW waves of a
 // K-part read the same activation records, so each record is copied into LDS
 // once for all of them: the K-part's ring holds two phases of P steps, and
 // the workgroup crosses one barrier per phase.
@@ -698,7 +699,9 @@ __global__ __launch_bounds__(64 * SH::WAVES, SH::OCC) void qgemm_kernel(int M, i
 // to within one super-block; every wave crosses the same barriers, whether
 // or not its K-part has steps left.  At the end the KS partial sums of each
 // output are added in K-part order through LDS and stored with 16-byte row
-// segments.
+// segments.  MODE: 0 = canvas GEMM, 2 = debug stores of S and Mn (or of one
+// sub-block's dots), 4 = SiLU(gate) * up of an interleaved gate/up matrix
+// (pairs of n-tiles 2i, 2i + 1 inside one workgroup: NTW even).
 template <int MB_, int NTW_, int KS_, int P_>
 struct RingShape {
   static constexpr int MB = MB_, NTW = NTW_, KS = KS_, P = P_, WAVES = NTW_ * KS_;
